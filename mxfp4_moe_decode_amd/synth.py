@@ -1,0 +1,125 @@
+"""Seeded synthetic inputs shaped like the MiniMax-M3.1 MoE layer.
+
+This module only draws random numbers; it holds none of the layer's
+arithmetic (no quantization, routing or FFN).  Both the GPU path and the CPU
+oracle take their inputs from here, so the two never share anything else.
+
+Workloads (sizes from the layer the pages describe: 128 routed experts, 4 active
+per token, plus a shared expert, article "MiniMax-M3.1 on AMD Instinct GPUs:
+Day-0 support and optimization", section "MiniMax-M3.1 at a glance"; hidden and
+intermediate sizes are not on the pages and are taken as 3072 / 1024):
+
+* ``tiny``     T=4,    H=256,  E=8,   k=2, I=128,  no shared expert, seed 0
+* ``decode1``  T=1,    H=3072, E=128, k=4, I=1024, shared expert I_s=1024
+* ``decode16`` T=16,   same layer, router weights U(-1/sqrt(H), 1/sqrt(H))
+* ``chain8``   T=4,    8 layers with distinct weights, Zipf(s=1.2) router bias,
+               residual add between layers
+* ``prefill``  T=8192, same layer as ``decode1``
+
+Draws: expert and shared weights fp32 N(0, 0.02); router weights fp32 N(0, 0.02)
+(``decode16``: uniform); activations N(0, 1) stored as bf16 (round to nearest
+even of the fp32 draw).  Zipf bias: b_e = -s * ln(rank_e) with rank a seeded
+permutation of 1..E, so the prior over experts is proportional to rank^-s.
+
+Every tensor has its own PCG64 stream, ``default_rng([seed, workload, layer,
+tag, index])``, so any single expert can be regenerated on its own.
+"""
+
+import math
+
+import numpy as np
+
+WORKLOADS = {
+    "tiny": dict(T=4, H=256, E=8, k=2, I=128, I_s=0, router="normal", layers=1,
+                 zipf=None, residual=False),
+    "decode1": dict(T=1, H=3072, E=128, k=4, I=1024, I_s=1024, router="normal", layers=1,
+                    zipf=None, residual=False),
+    "decode16": dict(T=16, H=3072, E=128, k=4, I=1024, I_s=1024, router="uniform", layers=1,
+                     zipf=None, residual=False),
+    "chain8": dict(T=4, H=3072, E=128, k=4, I=1024, I_s=1024, router="normal", layers=8,
+                   zipf=1.2, residual=True),
+    "prefill": dict(T=8192, H=3072, E=128, k=4, I=1024, I_s=1024, router="normal", layers=1,
+                    zipf=None, residual=False),
+}
+_WID = {name: i + 1 for i, name in enumerate(WORKLOADS)}
+_TAG = {"router": 1, "w13": 2, "w2": 3, "ws13": 4, "ws2": 5, "bias": 6, "x": 7}
+WEIGHT_STD = 0.02
+
+
+def workload(name, **overrides):
+    cfg = dict(WORKLOADS[name])
+    cfg.update(overrides)
+    cfg["name"] = name
+    cfg.setdefault("seed", 0)
+    return cfg
+
+
+def _rng(cfg, layer, tag, index=0):
+    return np.random.default_rng([cfg["seed"], _WID[cfg["name"]], layer, _TAG[tag], index])
+
+
+def router_weights(cfg, layer=0):
+    """fp32 [E, H]."""
+    g = _rng(cfg, layer, "router")
+    E, H = cfg["E"], cfg["H"]
+    if cfg["router"] == "uniform":
+        b = 1.0 / math.sqrt(H)
+        return g.uniform(-b, b, size=(E, H)).astype(np.float32)
+    return (g.standard_normal((E, H), dtype=np.float32) * np.float32(WEIGHT_STD)).astype(np.float32)
+
+
+def router_bias(cfg, layer=0):
+    """fp32 [E] Zipf offsets, or None."""
+    if not cfg.get("zipf"):
+        return None
+    g = _rng(cfg, layer, "bias")
+    rank = g.permutation(cfg["E"]) + 1
+    return (-cfg["zipf"] * np.log(rank.astype(np.float64))).astype(np.float32)
+
+
+def _normal(cfg, layer, tag, index, shape):
+    g = _rng(cfg, layer, tag, index)
+    return (g.standard_normal(shape, dtype=np.float32) * np.float32(WEIGHT_STD)).astype(np.float32)
+
+
+def expert_w13(cfg, layer, e):
+    """fp32 [2I, H]: gate rows 0..I-1, up rows I..2I-1."""
+    return _normal(cfg, layer, "w13", e, (2 * cfg["I"], cfg["H"]))
+
+
+def expert_w2(cfg, layer, e):
+    """fp32 [H, I]."""
+    return _normal(cfg, layer, "w2", e, (cfg["H"], cfg["I"]))
+
+
+def shared_w13(cfg, layer=0):
+    return _normal(cfg, layer, "ws13", 0, (2 * cfg["I_s"], cfg["H"]))
+
+
+def shared_w2(cfg, layer=0):
+    return _normal(cfg, layer, "ws2", 0, (cfg["H"], cfg["I_s"]))
+
+
+def f32_to_bf16_bits(a):
+    """Storage rounding of an fp32 draw to bf16 (nearest, ties to even)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def activations(cfg, layer=0, T=None, index=0):
+    """bf16 bit patterns [T, H] of N(0, 1) draws."""
+    T = cfg["T"] if T is None else T
+    g = _rng(cfg, layer, "x", index)
+    return f32_to_bf16_bits(g.standard_normal((T, cfg["H"]), dtype=np.float32))
+
+
+def device_normal_(tensor, seed, std=WEIGHT_STD):
+    """Fill a CUDA fp32 tensor with N(0, std^2) draws from torch's seeded
+    device generator (used where host generation would be too slow, e.g. the
+    many rotated layer copies a benchmark keeps resident)."""
+    import torch
+    g = torch.Generator(device=tensor.device)
+    g.manual_seed(int(seed))
+    tensor.normal_(0.0, std, generator=g)
+    return tensor

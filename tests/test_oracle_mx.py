@@ -1,0 +1,234 @@
+"""Pins of the oracle's MX formats against the OCP MX closed forms, torch's
+float8 dtypes (a library conversion written independently of the oracle),
+brute force over every bf16 pattern, and invariants of the block scale rule."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mx
+from tests.conftest import read_golden
+
+
+def _all_bf16_values():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = mx.bf16_bits_to_f64(bits)
+    return v[np.isfinite(v)]
+
+
+# --------------------------------------------------------------------------- decoders
+
+def test_e2m1_table_matches_ocp_golden():
+    for code, val in read_golden("e2m1_values.txt"):
+        got = mx.e2m1_value(int(code))
+        assert float(got) == float(val), code
+        assert math.copysign(1.0, float(got)) == math.copysign(1.0, float(val))
+
+
+def test_e4m3_specials_match_ocp_golden():
+    for code, val in read_golden("e4m3_specials.txt"):
+        got = float(mx.e4m3_value(int(code, 16)))
+        if val == "nan":
+            assert math.isnan(got)
+        else:
+            assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val))
+
+
+def test_e4m3_all_codes_match_torch_float8_e4m3fn():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).double().numpy()
+    got = mx.e4m3_value(np.arange(256))
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+    assert np.array_equal(np.signbit(ref[~nan]), np.signbit(got[~nan]))
+
+
+def test_e8m0_matches_golden_and_torch():
+    for code, lg in read_golden("e8m0_specials.txt"):
+        got = float(mx.e8m0_value(int(code)))
+        if lg == "nan":
+            assert math.isnan(got)
+        else:
+            assert got == math.ldexp(1.0, int(lg))
+    ref = torch.arange(255, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
+    assert np.array_equal(ref, mx.e8m0_value(np.arange(255)))
+
+
+# --------------------------------------------------------------------------- element rounding
+
+def test_e4m3_rounding_matches_torch_for_every_bf16_value():
+    """torch's fp32 -> float8_e4m3fn conversion rounds to nearest even and
+    returns NaN past the 448/480 midpoint; the MX conversion saturates there."""
+    v = _all_bf16_values()
+    got = mx.round_to_element(v, "fp8")
+    inr = np.abs(v) <= 464.0
+    ref = torch.from_numpy(v[inr].astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got[inr], ref)
+    out = ~inr
+    assert np.all((got[out] & 0x7F) == 0x7E)
+    assert np.array_equal(got[out] >> 7, np.signbit(v[out]).astype(np.uint8))
+
+
+def _brute_force_codes(v, fmt):
+    """Nearest element value by exhaustive comparison against every finite
+    code; equal distances go to the even magnitude code; sign copied."""
+    maxc = mx.FORMATS[fmt]["max_code"]
+    grid = np.array([float(mx.element_value(c, fmt)) for c in range(maxc + 1)])
+    mag = np.abs(v)
+    dist = np.abs(mag[:, None] - grid[None, :])
+    best = dist.min(axis=1, keepdims=True)
+    cand = dist == best
+    # among equally near codes prefer the even one (there are at most two)
+    even = cand & (np.arange(maxc + 1)[None, :] % 2 == 0)
+    code = np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1))
+    code = np.where(mag >= grid[-1], maxc, code)
+    return (code | (np.signbit(v).astype(np.int64) << mx.FORMATS[fmt]["sign_bit"])).astype(np.uint8)
+
+
+@pytest.mark.parametrize("shift", [-3, 0, 2, 7])
+def test_e2m1_rounding_brute_force_every_bf16_value(shift):
+    v = _all_bf16_values()
+    v = np.ldexp(v, shift)
+    assert np.array_equal(mx.round_to_element(v, "fp4"), _brute_force_codes(v, "fp4"))
+
+
+def test_e2m1_ties_go_to_even_codes():
+    # midpoints between neighbouring E2M1 values and the expected even code
+    cases = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6, 7.0: 7}
+    for v, c in cases.items():
+        assert int(mx.round_to_element(np.array([v]), "fp4")[0]) == c, v
+        assert int(mx.round_to_element(np.array([-v]), "fp4")[0]) == c | 8, -v
+    # sign kept for values that round to zero and for -0.0
+    assert int(mx.round_to_element(np.array([-0.1]), "fp4")[0]) == 8
+    assert int(mx.round_to_element(np.array([-0.0]), "fp4")[0]) == 8
+    assert int(mx.round_to_element(np.array([1e30]), "fp4")[0]) == 7
+
+
+def test_e4m3_fp32_midpoints_and_neighbours_match_torch():
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 0x7E, 2000)
+    lo = mx.e4m3_value(codes)
+    hi = mx.e4m3_value(codes + 1)
+    mid = (lo + hi) / 2  # exact in fp32 for E4M3 neighbours
+    for d in (0, 1, -1):
+        v = np.nextafter(mid.astype(np.float32), np.float32(np.inf) if d > 0 else np.float32(-np.inf)) if d else mid.astype(np.float32)
+        ref = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(mx.round_to_element(v.astype(np.float64), "fp8"), ref)
+
+
+# --------------------------------------------------------------------------- block scale
+
+@pytest.mark.parametrize("fmt,lo,hi", [("fp4", 4.0, 8.0), ("fp8", 256.0, 512.0)])
+def test_scaled_block_max_in_top_binade(fmt, lo, hi):
+    """floor(log2 amax) - emax puts amax / X in [2^emax, 2^(emax+1))."""
+    rng = np.random.default_rng(1)
+    amax = np.ldexp(rng.uniform(1, 2, 5000), rng.integers(-100, 100, 5000))
+    e = mx.shared_exponent(amax, fmt)
+    s = np.ldexp(amax, -e)
+    assert np.all((s >= lo) & (s < hi))
+
+
+def test_scale_clamps_and_zero_block():
+    assert int(mx.shared_exponent(0.0, "fp4")) == -127
+    assert int(mx.shared_exponent(2.0 ** -140, "fp4")) == -127
+    assert int(mx.shared_exponent(2.0 ** 127, "fp4")) == 125
+    codes, scales = mx.mx_quantize(np.zeros((1, 32)), "fp4")
+    assert scales[0, 0] == 0 and np.all(codes == 0)
+
+
+def test_quantize_error_within_half_quantum():
+    """|dequant - v| <= half the element spacing at |v| (or the saturation gap)."""
+    rng = np.random.default_rng(2)
+    for fmt, mbits, emin in (("fp4", 1, 0), ("fp8", 3, -6)):
+        v = rng.standard_normal((64, 256)).astype(np.float32).astype(np.float64)
+        c, s = mx.mx_quantize(v, fmt)
+        dq = mx.mx_dequantize(c, s, fmt)
+        X = np.repeat(mx.e8m0_value(s), 32, axis=1)
+        y = np.abs(v) / X
+        p = np.floor(np.log2(np.maximum(y, 2.0 ** -30)))
+        half = 0.5 * np.ldexp(1.0, (np.maximum(p, emin) - mbits).astype(int)) * X
+        maxv = float(mx.element_value(mx.FORMATS[fmt]["max_code"], fmt))
+        sat = y > maxv
+        assert np.all(np.abs(dq - v)[~sat] <= half[~sat])
+        assert np.all(np.abs(dq[sat]) == maxv * X[sat])
+
+
+def test_quantize_requantize_is_identity():
+    rng = np.random.default_rng(3)
+    for fmt in ("fp4", "fp8"):
+        v = rng.standard_normal((16, 128)).astype(np.float32).astype(np.float64)
+        c, s = mx.mx_quantize(v, fmt)
+        c2, s2 = mx.mx_quantize(mx.mx_dequantize(c, s, fmt), fmt)
+        # the block max may drop a binade when it saturated; codes then shift, so
+        # compare values instead of codes
+        assert np.array_equal(mx.mx_dequantize(c2, s2, fmt), mx.mx_dequantize(c, s, fmt))
+
+
+# --------------------------------------------------------------------------- lossless BF16 widening
+
+def test_e4m3_times_power_of_two_is_exact_in_bf16():
+    """vLLM PR "[ROCm] MiniMax-M3: allow the AMD monokernel decode on
+    MiniMax-M3.1", section "Purpose": E4M3 times a power-of-two scale is exact
+    in BF16.  Checked for every finite code and scales 2^-100..2^100."""
+    vals = mx.e4m3_value(np.arange(256))
+    vals = vals[np.isfinite(vals)]
+    for k in range(-100, 101, 7):
+        y = np.ldexp(vals, k)
+        back = mx.bf16_bits_to_f64(mx.round_to_bf16_bits(y))
+        assert np.array_equal(back, y)
+    vals4 = mx.e2m1_value(np.arange(16))
+    y = np.ldexp(vals4, 5)
+    assert np.array_equal(mx.bf16_bits_to_f64(mx.round_to_bf16_bits(y)), y)
+
+
+# --------------------------------------------------------------------------- bf16 rounding / packing
+
+def test_round_to_bf16_matches_torch_on_fp32_inputs():
+    rng = np.random.default_rng(4)
+    v = np.concatenate([rng.standard_normal(20000), np.ldexp(rng.standard_normal(2000), -130)]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mx.round_to_bf16_bits(v.astype(np.float64)), ref)
+
+
+def test_round_to_bf16_single_rounding_from_fp64():
+    # 1 + 2^-8 + 2^-30 lies just above the bf16 midpoint 1 + 2^-8; a detour
+    # through fp32 would land on the midpoint and round to even (1.0)
+    y = np.array([1.0 + 2.0 ** -8 + 2.0 ** -30])
+    assert mx.bf16_bits_to_f64(mx.round_to_bf16_bits(y))[0] == 1.0 + 2.0 ** -7
+
+
+def test_fp4_nibble_order():
+    assert mx.pack_fp4(np.array([[0x1, 0xF]]))[0, 0] == 0xF1
+    c = np.random.default_rng(0).integers(0, 16, (3, 64)).astype(np.uint8)
+    assert np.array_equal(mx.unpack_fp4(mx.pack_fp4(c)), c)
+
+
+# --------------------------------------------------------------------------- tiled layout
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
+def test_tiled_layout_is_a_bijection_with_hand_checked_entries(fmt):
+    N, K = 32, 640  # K/128 = 5 tiles -> scale groups padded to 8
+    rng = np.random.default_rng(7)
+    maxc = 16 if fmt == "fp4" else 256
+    codes = rng.integers(0, maxc, (N, K)).astype(np.uint8)
+    scales = rng.integers(100, 150, (N, K // 32)).astype(np.uint8)
+    tc, ts = mx.tile_weight(codes, scales, fmt)
+    TB = 1024 if fmt == "fp4" else 2048
+    assert tc.size == N // 16 * (K // 128) * TB
+    assert ts.size == N // 16 * 2 * 256
+    if fmt == "fp4":
+        # row 17 (strip 1, lane 1 + 16*q), column 300 = tile 2, q = 1, j = 6 (even -> low nibble)
+        byte = tc[(1 * 5 + 2) * 1024 + 16 * (1 + 16 * 1) + 6]
+        assert byte & 0xF == codes[17, 300] and byte >> 4 == codes[17, 301]
+        assert np.array_equal(np.sort(mx.unpack_fp4(tc)), np.sort(codes.reshape(-1)))
+    else:
+        # row 3, column 128*4 + 64 + 16*2 + 5 = 613: tile 4, c = 1, q = 2, j = 5
+        assert tc[(0 * 5 + 4) * 2048 + 1024 + 16 * (3 + 16 * 2) + 5] == codes[3, 613]
+        assert np.array_equal(np.sort(tc), np.sort(codes.reshape(-1)))
+    # scale of row 20, block 4*(4*1 + 0) + 3 = 19: strip 1, group 1, lane 4 + 16*3, byte 0
+    assert ts[((1 * 2 + 1) * 64 + 4 + 48) * 4 + 0] == scales[20, 19]
+    # padding (K-tiles 5..7) holds 127
+    assert ts[((0 * 2 + 1) * 64 + 0) * 4 + 1] == 127
