@@ -1,0 +1,218 @@
+/*
+ * mxmoe.h — C ABI of libmxmoe.so, a fused MXFP4 Mixture-of-Experts layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (article "MiniMax-M3.1 on AMD Instinct GPUs: Day-0 support and
+ * optimization", section "MiniMax-M3.1 at a glance"; model card
+ * "amd/MiniMax-M3.1-Flash-Quark-MXFP4", section "Model Overview"):
+ *
+ *   logits[t,e] = sum_h x[t,h] * Wr[e,h] (+ bias[e])     fp32 router ("high precision")
+ *   ids[t,:]    = top-k experts by logit (k of E; 4 of 128 in the model)
+ *   w[t,j]      = softmax over the k chosen logits
+ *   xq          = MXFP4(x[t])                             dynamic activation quantization
+ *   g, u        = xq . W13[e] gate rows, up rows           MXFP4 x MXFP4, fp32 accumulate
+ *   a           = MXFP4(silu(g) * u)
+ *   d[t,j]      = a . W2[e] rows
+ *   s[t]        = the same FFN in MXFP8 (shared expert, every token passes through it)
+ *   y[t]        = bf16( sum_j w[t,j] * d[t,j] + s[t] (+ residual[t]) )
+ *
+ * Element and scale formats are those of the OCP Microscaling Formats (MX) v1.0
+ * specification: E2M1 (FP4) and E4M3 (FP8, max 448, no Inf) elements, blocks
+ * of 32 consecutive elements along the reduction axis sharing one E8M0 scale
+ * 2^(code-127).  Conversion: block exponent floor(log2(max|v|)) - emax_elem
+ * (2 for E2M1, 8 for E4M3) clamped to [-127, 127] (-127 for an all-zero
+ * block), elements rounded to nearest with ties to the even code, saturated
+ * to the largest finite magnitude, sign kept (also when rounding to zero).
+ *
+ * Conventions for every call:
+ *  - All data pointers are device memory owned by the caller.  The library
+ *    never allocates, frees, synchronizes or reads device data on the host
+ *    (except moe_decode_status, a diagnostic); every compute call only
+ *    enqueues work on `stream` and is safe to capture into a HIP graph.
+ *  - Arguments are validated before anything is enqueued.  A call that
+ *    returns an error has enqueued nothing.  Kernel launch failures return
+ *    MOE_ERR_HIP.
+ *  - bf16 tensors are passed as uint16_t bit patterns, row-major.
+ *  - Calls on one stream are ordered; calls that share a workspace must not
+ *    run concurrently on different streams.
+ */
+#ifndef MXMOE_H
+#define MXMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = -1,   /* null pointer, bad size, misaligned pointer */
+  MOE_ERR_UNSUPPORTED = -2,        /* valid request this entry point does not serve (e.g. decode T > 16) */
+  MOE_ERR_WORKSPACE_TOO_SMALL = -3,
+  MOE_ERR_HIP = -4,                /* a HIP runtime call or kernel launch failed */
+  MOE_ERR_TIMEOUT = -5             /* reported by moe_decode_status: a device-side wait gave up */
+} moe_status;
+
+enum { MX_FMT_FP4 = 0, MX_FMT_FP8 = 1 };
+enum { MX_LAYOUT_ROWMAJOR = 0, MX_LAYOUT_TILED = 1 };
+
+/*
+ * Tiled MX weight layout (MX_LAYOUT_TILED), the layout every weight pointer in
+ * moe_layer_t uses.  A matrix W[N][K] (N % 16 == 0, K % 128 == 0, quantized
+ * along K) is cut into tiles of 16 rows x 128 columns.  Tile (nt, kt) holds TB
+ * bytes (1024 for FP4, 2048 for FP8) at byte offset (nt*(K/128) + kt)*TB.
+ * Inside a tile, with l = 0..63, r = 16*nt + l%16, q = l/16, j = 0..15:
+ *   FP4: byte 16*l + j            = W[r][128*kt + 32*q + 2*j] (low nibble),
+ *                                   W[r][128*kt + 32*q + 2*j + 1] (high nibble)
+ *   FP8: byte 1024*c + 16*l + j   = W[r][128*kt + 64*c + 16*q + j], c = 0, 1
+ * Scales: KG = ceil(K/512) groups of four K-tiles per 16-row strip;
+ *   byte ((nt*KG + g)*64 + l)*4 + i = E8M0 scale of W[r][32*(4*(4*g+i) + q) ...],
+ *   127 where 4*g + i >= K/128.
+ * Each tile is exactly one operand of the gfx950 scaled matrix instruction
+ * (16x16x128), so a wavefront streams weights as whole 1 KiB rows of HBM.
+ *
+ * Row-major MX layout (MX_LAYOUT_ROWMAJOR): codes [N][K/2] for FP4 (element 2i
+ * in the low nibble of byte i) or [N][K] for FP8; scales [N][K/32].
+ */
+size_t mx_codes_bytes(int rows, int cols, int fmt, int layout);
+size_t mx_scales_bytes(int rows, int cols, int layout);
+
+/*
+ * Static MX quantization of fp32 weights (the model card's "Routed-expert
+ * weight quantization: OCP MXFP4, Static"; the shared expert is MXFP8, article
+ * section "MiniMax-M3.1 at a glance").  Run once at load time.
+ *   w      [rows][cols] fp32, row-major, 16-byte aligned
+ *   fmt    MX_FMT_FP4 or MX_FMT_FP8; layout MX_LAYOUT_ROWMAJOR or MX_LAYOUT_TILED
+ *   codes  mx_codes_bytes(rows, cols, fmt, layout) bytes, 16-byte aligned
+ *   scales mx_scales_bytes(rows, cols, layout) bytes, 4-byte aligned
+ * Requires cols % 32 == 0 (row-major) or rows % 16 == 0 and cols % 128 == 0 (tiled).
+ */
+moe_status mx_quantize_weights(const float* w, int rows, int cols, int fmt, int layout,
+                               uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+/*
+ * Dynamic MXFP4 quantization of bf16 activations (model card "Model
+ * Overview": "Routed-expert activation quantization: OCP MXFP4, Dynamic").
+ *   x      [rows][cols] bf16, 16-byte aligned, cols % 32 == 0
+ *   codes  [rows][cols/2] packed E2M1 (element 2i in the low nibble of byte i)
+ *   scales [rows][cols/32] E8M0
+ * Bit-exact: the conversion is integer arithmetic on the bf16 patterns.
+ */
+moe_status mxfp4_quant_act(const uint16_t* x, int rows, int cols, uint8_t* codes,
+                           uint8_t* scales, hipStream_t stream);
+
+/*
+ * One MoE layer's weights (device pointers, caller-owned, tiled layout).
+ * Routed expert e's matrices start at e * mx_codes_bytes(rows, cols, FP4, TILED)
+ * bytes from w13 / w2 (scales likewise with mx_scales_bytes).
+ */
+typedef struct {
+  int32_t hidden;        /* H: multiple of 128 */
+  int32_t inter;         /* I: routed expert intermediate size, multiple of 128 */
+  int32_t num_experts;   /* E: 1..256 */
+  int32_t top_k;         /* k: 1..min(E, 8) */
+  int32_t shared_inter;  /* I_s: shared expert intermediate size, multiple of 128, or 0 for none */
+  const float* router_w;      /* [E][H] fp32 row-major */
+  const float* router_bias;   /* [E] fp32 added to the logits, or NULL */
+  const uint8_t* w13;         /* E x tiled FP4 [2I][H]: rows 0..I-1 gate, I..2I-1 up */
+  const uint8_t* w13_scale;
+  const uint8_t* w2;          /* E x tiled FP4 [H][I] */
+  const uint8_t* w2_scale;
+  const uint8_t* ws13;        /* tiled FP8 [2I_s][H] (gate rows first), NULL if I_s == 0 */
+  const uint8_t* ws13_scale;
+  const uint8_t* ws2;         /* tiled FP8 [H][I_s], NULL if I_s == 0 */
+  const uint8_t* ws2_scale;
+} moe_layer_t;
+
+/*
+ * Router and top-k (article "MiniMax-M3.1 at a glance": 4 of 128 routed
+ * experts per token; routers kept in high precision).
+ *   x        [T][H] bf16
+ *   logits   [T][E] fp32 output, or NULL
+ *   topk_ids [T][k] int32: the k largest logits in descending order; equal
+ *            logits go to the lower expert index
+ *   topk_w   [T][k] fp32: softmax over the k chosen logits
+ * Logit arithmetic (fixed, independent of T): lane l = 0..63 accumulates with
+ * fp32 FMA, in order, the products x[t][h]*Wr[e][h] for h = 256*i + 4*l + c
+ * (i ascending, c = 0..3); the 64 partial sums are added by a butterfly over
+ * lane distances 32, 16, 8, 4, 2, 1; then bias[e] is added.  The fused decode
+ * call uses the same arithmetic, so both produce identical logits.
+ */
+moe_status moe_router_topk(const moe_layer_t* layer, const uint16_t* x, int T, float* logits,
+                           int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+/*
+ * Token sort by expert: a stable counting sort of the slots s = t*k + j by
+ * topk_ids[t][j], each expert's segment padded to a multiple of block_m.
+ *   sorted_slots   moe_align_sort_capacity(T, k, E, block_m) int32: slots grouped
+ *                  by expert (experts ascending, slots ascending inside), each
+ *                  segment padded with T*k; entries past num_padded are T*k
+ *   block_expert   capacity / block_m int32: expert owning each block of block_m
+ *                  entries; -1 past the last block
+ *   expert_offsets [E+1] int32: exclusive scan of the unpadded counts
+ *   num_padded     [1] int32: total padded length
+ *   ws             moe_align_sort_workspace_bytes(T, k, E) bytes of scratch
+ */
+size_t moe_align_sort_capacity(int T, int k, int E, int block_m);
+size_t moe_align_sort_workspace_bytes(int T, int k, int E);
+moe_status moe_align_sort(const int32_t* topk_ids, int T, int k, int E, int block_m,
+                          int32_t* sorted_slots, int32_t* block_expert, int32_t* expert_offsets,
+                          int32_t* num_padded, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Workspace for the fused calls.  path 0: fused_moe_mxfp4_decode (T <= 16),
+ * path 1: fused_moe_mxfp4_grouped (any T).  Returns 0 for invalid arguments.
+ * A decode workspace must be zero-filled once (moe_workspace_init) before its
+ * first use; every decode call leaves it zero-filled again on exit.
+ */
+size_t moe_workspace_bytes(const moe_layer_t* layer, int T, int path);
+moe_status moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The whole layer for 1..16 rows in ONE kernel launch ("mono decode": one
+ * fused kernel launch per MoE layer for a pure decode of at most 16 tokens,
+ * article section "Serving with vLLM / What we Optimized"; the monokernel's
+ * "rows (1..16)", vLLM PR #64273 section "Test Result").
+ *   x         [T][H] bf16, T in 1..16 (MOE_ERR_UNSUPPORTED otherwise)
+ *   residual  [T][H] bf16 added before the single bf16 rounding, or NULL
+ *   y         [T][H] bf16 output; may alias residual, must not alias x
+ *   ws        moe_workspace_bytes(layer, T, 0) bytes, zero-filled before first use
+ *   topk_ids_out [T][k], topk_w_out [T][k]: routing result, or NULL
+ * Output row t depends only on x[t] (and residual[t]): results are bit-identical
+ * for any T and any row order.  The launch is a persistent grid sized to the
+ * device's co-resident capacity; its device-side waits are bounded, and a wait
+ * that gives up marks the workspace (see moe_decode_status) instead of hanging.
+ */
+moe_status fused_moe_mxfp4_decode(const moe_layer_t* layer, const uint16_t* x, int T,
+                                  const uint16_t* residual, uint16_t* y, void* ws, size_t ws_bytes,
+                                  int32_t* topk_ids_out, float* topk_w_out, hipStream_t stream);
+
+/*
+ * The layer for any number of rows (prefill and steps wider than 16 rows,
+ * which the pages keep on the standard path: article section "Performance,
+ * mono decode on vs off").  Several launches: router + top-k, token sort,
+ * activation quantization, grouped gate/up and down GEMMs on scaled FP4
+ * matrix instructions, the MXFP8 shared expert, and the combine.
+ *   x, residual, y as for the decode call; T >= 1
+ *   ws  moe_workspace_bytes(layer, T, 1) bytes (no initialization needed)
+ */
+moe_status fused_moe_mxfp4_grouped(const moe_layer_t* layer, const uint16_t* x, int T,
+                                   const uint16_t* residual, uint16_t* y, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/*
+ * Diagnostic (synchronizes the device): MOE_OK if no fused decode call on this
+ * workspace has given up a device-side wait, MOE_ERR_TIMEOUT otherwise.
+ */
+moe_status moe_decode_status(const void* ws, size_t ws_bytes);
+
+const char* moe_status_string(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXMOE_H */

@@ -1,0 +1,296 @@
+"""Thin Python binding of libmxmoe.so (ctypes).  Argument marshalling only:
+torch provides device memory and the current stream; every computation runs in
+the library's HIP kernels.  Importing works without a GPU; calling a compute
+function needs the built library and a GPU, and fails loudly otherwise."""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxmoe.so")
+
+MX_FMT = {"fp4": 0, "fp8": 1}
+MX_LAYOUT = {"rowmajor": 0, "tiled": 1}
+
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARGUMENT", -2: "MOE_ERR_UNSUPPORTED",
+          -3: "MOE_ERR_WORKSPACE_TOO_SMALL", -4: "MOE_ERR_HIP", -5: "MOE_ERR_TIMEOUT"}
+
+EXPORTS = [
+    "mx_codes_bytes", "mx_scales_bytes", "mx_quantize_weights", "mxfp4_quant_act",
+    "moe_router_topk", "moe_align_sort_capacity", "moe_align_sort_workspace_bytes", "moe_align_sort",
+    "moe_workspace_bytes", "moe_workspace_init", "fused_moe_mxfp4_decode", "fused_moe_mxfp4_grouped",
+    "moe_decode_status", "moe_status_string",
+]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({_lib_or_none_string(status)})")
+
+
+class MoeLayerC(ctypes.Structure):
+    """moe_layer_t of mxmoe.h."""
+    _fields_ = [
+        ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+        ("top_k", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
+        ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
+        ("w13", ctypes.c_void_p), ("w13_scale", ctypes.c_void_p),
+        ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
+        ("ws13", ctypes.c_void_p), ("ws13_scale", ctypes.c_void_p),
+        ("ws2", ctypes.c_void_p), ("ws2_scale", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load():
+    """Load the built library (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m mxfp4_moe_decode_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, Z, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_int
+    LP = ctypes.POINTER(MoeLayerC)
+    sig = {
+        "mx_codes_bytes": (Z, [I, I, I, I]),
+        "mx_scales_bytes": (Z, [I, I, I]),
+        "mx_quantize_weights": (S, [P, I, I, I, I, P, P, P]),
+        "mxfp4_quant_act": (S, [P, I, I, P, P, P]),
+        "moe_router_topk": (S, [LP, P, I, P, P, P, P]),
+        "moe_align_sort_capacity": (Z, [I, I, I, I]),
+        "moe_align_sort_workspace_bytes": (Z, [I, I, I]),
+        "moe_align_sort": (S, [P, I, I, I, I, P, P, P, P, P, Z, P]),
+        "moe_workspace_bytes": (Z, [LP, I, I]),
+        "moe_workspace_init": (S, [P, Z, P]),
+        "fused_moe_mxfp4_decode": (S, [LP, P, I, P, P, P, Z, P, P, P]),
+        "fused_moe_mxfp4_grouped": (S, [LP, P, I, P, P, P, Z, P]),
+        "moe_decode_status": (S, [P, Z]),
+        "moe_status_string": (ctypes.c_char_p, [S]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _lib_or_none_string(status):
+    try:
+        return load().moe_status_string(status).decode()
+    except Exception:
+        return "?"
+
+
+def _check(fn, status):
+    if status != 0:
+        raise MoeError(fn, status)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous CUDA tensors")
+
+
+# --------------------------------------------------------------------------- quantization
+
+def mx_codes_bytes(rows, cols, fmt="fp4", layout="tiled"):
+    return load().mx_codes_bytes(rows, cols, MX_FMT[fmt], MX_LAYOUT[layout])
+
+
+def mx_scales_bytes(rows, cols, layout="tiled"):
+    return load().mx_scales_bytes(rows, cols, MX_LAYOUT[layout])
+
+
+def mx_quantize_weights(w, fmt="fp4", layout="tiled", codes=None, scales=None):
+    """Static MX quantization of an fp32 [rows, cols] CUDA tensor.  Returns
+    (codes, scales) uint8 tensors (flat for the tiled layout)."""
+    _need_cuda(w)
+    if w.dtype != torch.float32 or w.dim() != 2:
+        raise ValueError("w must be a 2-D float32 tensor")
+    rows, cols = w.shape
+    nc, ns = mx_codes_bytes(rows, cols, fmt, layout), mx_scales_bytes(rows, cols, layout)
+    if nc == 0 or ns == 0:
+        raise ValueError(f"unsupported shape {tuple(w.shape)} for layout {layout}")
+    if codes is None:
+        codes = torch.empty(nc, dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(ns, dtype=torch.uint8, device=w.device)
+    _check("mx_quantize_weights", load().mx_quantize_weights(
+        _ptr(w), rows, cols, MX_FMT[fmt], MX_LAYOUT[layout], _ptr(codes), _ptr(scales), _stream()))
+    if layout == "rowmajor":
+        codes = codes.view(rows, cols // 2 if fmt == "fp4" else cols)
+        scales = scales.view(rows, cols // 32)
+    return codes, scales
+
+
+def mxfp4_quant_act(x):
+    """Dynamic MXFP4 quantization of bf16 [rows, cols]: (codes [rows, cols/2],
+    scales [rows, cols/32]) uint8."""
+    _need_cuda(x)
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    rows, cols = x.shape
+    codes = torch.empty(rows, cols // 2, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(rows, cols // 32, dtype=torch.uint8, device=x.device)
+    _check("mxfp4_quant_act", load().mxfp4_quant_act(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales
+
+
+# --------------------------------------------------------------------------- layer weights
+
+class MoELayer:
+    """Device weights of one layer in the library's tiled MX layout."""
+
+    def __init__(self, hidden, inter, num_experts, top_k, shared_inter, router_w, router_bias,
+                 w13, w13_scale, w2, w2_scale, ws13=None, ws13_scale=None, ws2=None, ws2_scale=None):
+        self.hidden, self.inter, self.num_experts, self.top_k, self.shared_inter = (
+            hidden, inter, num_experts, top_k, shared_inter)
+        self.router_w, self.router_bias = router_w, router_bias
+        self.w13, self.w13_scale, self.w2, self.w2_scale = w13, w13_scale, w2, w2_scale
+        self.ws13, self.ws13_scale, self.ws2, self.ws2_scale = ws13, ws13_scale, ws2, ws2_scale
+        self._c = MoeLayerC(hidden, inter, num_experts, top_k, shared_inter,
+                            router_w.data_ptr(), router_bias.data_ptr() if router_bias is not None else None,
+                            w13.data_ptr(), w13_scale.data_ptr(), w2.data_ptr(), w2_scale.data_ptr(),
+                            ws13.data_ptr() if ws13 is not None else None,
+                            ws13_scale.data_ptr() if ws13_scale is not None else None,
+                            ws2.data_ptr() if ws2 is not None else None,
+                            ws2_scale.data_ptr() if ws2_scale is not None else None)
+
+    @property
+    def c(self):
+        return ctypes.byref(self._c)
+
+    @classmethod
+    def from_fp32(cls, hidden, inter, num_experts, top_k, shared_inter, router_w, router_bias,
+                  expert_w13, expert_w2, shared_w13=None, shared_w2=None, device="cuda"):
+        """Quantize fp32 weights on the device.  ``expert_w13(e)`` /
+        ``expert_w2(e)`` return the fp32 [2I, H] / [H, I] matrices of expert e
+        (host arrays or device tensors); ``router_w`` [E, H]; ``router_bias``
+        [E] or None; shared weights [2I_s, H] / [H, I_s] or None."""
+        H, I, E, Is = hidden, inter, num_experts, shared_inter
+        dev = torch.device(device)
+
+        def dev_f32(a):
+            return torch.as_tensor(a, dtype=torch.float32).to(dev).contiguous()
+
+        c13, s13 = mx_codes_bytes(2 * I, H, "fp4"), mx_scales_bytes(2 * I, H)
+        c2, s2 = mx_codes_bytes(H, I, "fp4"), mx_scales_bytes(H, I)
+        w13 = torch.empty(E * c13, dtype=torch.uint8, device=dev)
+        w13s = torch.empty(E * s13, dtype=torch.uint8, device=dev)
+        w2 = torch.empty(E * c2, dtype=torch.uint8, device=dev)
+        w2s = torch.empty(E * s2, dtype=torch.uint8, device=dev)
+        for e in range(E):
+            mx_quantize_weights(dev_f32(expert_w13(e)), "fp4", "tiled",
+                                w13[e * c13:(e + 1) * c13], w13s[e * s13:(e + 1) * s13])
+            mx_quantize_weights(dev_f32(expert_w2(e)), "fp4", "tiled",
+                                w2[e * c2:(e + 1) * c2], w2s[e * s2:(e + 1) * s2])
+        sh = {}
+        if Is > 0:
+            sh["ws13"], sh["ws13_scale"] = mx_quantize_weights(dev_f32(shared_w13), "fp8", "tiled")
+            sh["ws2"], sh["ws2_scale"] = mx_quantize_weights(dev_f32(shared_w2), "fp8", "tiled")
+        rb = None if router_bias is None else dev_f32(router_bias)
+        return cls(H, I, E, top_k, Is, dev_f32(router_w), rb, w13, w13s, w2, w2s, **sh)
+
+
+# --------------------------------------------------------------------------- router / sort
+
+def moe_router_topk(layer, x, want_logits=False):
+    _need_cuda(x)
+    T = x.shape[0]
+    ids = torch.empty(T, layer.top_k, dtype=torch.int32, device=x.device)
+    w = torch.empty(T, layer.top_k, dtype=torch.float32, device=x.device)
+    logits = torch.empty(T, layer.num_experts, dtype=torch.float32, device=x.device) if want_logits else None
+    _check("moe_router_topk", load().moe_router_topk(layer.c, _ptr(x), T, _ptr(logits), _ptr(ids), _ptr(w), _stream()))
+    return (ids, w, logits) if want_logits else (ids, w)
+
+
+def moe_align_sort(topk_ids, num_experts, block_m):
+    _need_cuda(topk_ids)
+    T, k = topk_ids.shape
+    lib = load()
+    cap = lib.moe_align_sort_capacity(T, k, num_experts, block_m)
+    wsb = lib.moe_align_sort_workspace_bytes(T, k, num_experts)
+    if cap == 0 or wsb == 0:
+        raise ValueError("invalid align_sort arguments")
+    dev = topk_ids.device
+    sorted_slots = torch.empty(cap, dtype=torch.int32, device=dev)
+    block_expert = torch.empty(cap // block_m, dtype=torch.int32, device=dev)
+    offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+    num_padded = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    _check("moe_align_sort", lib.moe_align_sort(
+        _ptr(topk_ids), T, k, num_experts, block_m, _ptr(sorted_slots), _ptr(block_expert),
+        _ptr(offsets), _ptr(num_padded), _ptr(ws), wsb, _stream()))
+    return sorted_slots, block_expert, offsets, num_padded
+
+
+# --------------------------------------------------------------------------- fused layer
+
+def moe_workspace_bytes(layer, T, path):
+    return load().moe_workspace_bytes(layer.c, T, path)
+
+
+def decode_workspace(layer, device="cuda"):
+    """A zero-initialized workspace for fused_moe_mxfp4_decode (any T <= 16)."""
+    n = moe_workspace_bytes(layer, 16, 0)
+    if n == 0:
+        raise ValueError("invalid layer")
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    _check("moe_workspace_init", load().moe_workspace_init(_ptr(ws), n, _stream()))
+    return ws
+
+
+def fused_moe_mxfp4_decode(layer, x, residual=None, out=None, workspace=None, return_routing=False):
+    _need_cuda(x, residual, out, workspace)
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = decode_workspace(layer, x.device)
+    ids = w = None
+    if return_routing:
+        ids = torch.empty(T, layer.top_k, dtype=torch.int32, device=x.device)
+        w = torch.empty(T, layer.top_k, dtype=torch.float32, device=x.device)
+    _check("fused_moe_mxfp4_decode", load().fused_moe_mxfp4_decode(
+        layer.c, _ptr(x), T, _ptr(residual), _ptr(out), _ptr(workspace), workspace.numel(),
+        _ptr(ids), _ptr(w), _stream()))
+    return (out, ids, w) if return_routing else out
+
+
+def grouped_workspace(layer, T, device="cuda"):
+    n = moe_workspace_bytes(layer, T, 1)
+    if n == 0:
+        raise MoeError("moe_workspace_bytes", -2)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def fused_moe_mxfp4_grouped(layer, x, residual=None, out=None, workspace=None):
+    _need_cuda(x, residual, out, workspace)
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = grouped_workspace(layer, T, x.device)
+    _check("fused_moe_mxfp4_grouped", load().fused_moe_mxfp4_grouped(
+        layer.c, _ptr(x), T, _ptr(residual), _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def moe_decode_status(workspace):
+    return load().moe_decode_status(_ptr(workspace), workspace.numel())

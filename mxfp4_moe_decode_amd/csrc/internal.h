@@ -1,0 +1,57 @@
+// Internal declarations shared by the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mxmoe.h"
+
+namespace mxmoe {
+
+// Tiled layout sizes (see mxmoe.h).
+inline size_t tiled_codes_bytes(int rows, int cols, int fmt) {
+  return (size_t)(rows / 16) * (size_t)(cols / 128) * (fmt == MX_FMT_FP4 ? 1024u : 2048u);
+}
+inline int tiled_scale_groups(int cols) { return (cols / 128 + 3) / 4; }
+inline size_t tiled_scales_bytes(int rows, int cols) {
+  return (size_t)(rows / 16) * (size_t)tiled_scale_groups(cols) * 256u;
+}
+
+__host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ------------------------------------------------------------------ quantization
+hipError_t launch_quant_weights(const float* w, int rows, int cols, int fmt, int layout,
+                                uint8_t* codes, uint8_t* scales, hipStream_t stream);
+hipError_t launch_quant_act_fp4(const uint16_t* x, int rows, int cols, uint8_t* codes,
+                                uint8_t* scales, hipStream_t stream);
+hipError_t launch_fill_u32(void* p, size_t words, uint32_t value, hipStream_t stream);
+
+// ------------------------------------------------------------------ router
+hipError_t launch_router_topk(const moe_layer_t& L, const uint16_t* x, int T, float* logits,
+                              int32_t* ids, float* w, hipStream_t stream);
+
+// ------------------------------------------------------------------ align / sort
+constexpr int kSortChunk = 1024;
+size_t align_sort_ws_bytes(int T, int k, int E);
+hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int block_m,
+                             int32_t* sorted_slots, int32_t* block_expert, int32_t* expert_offsets,
+                             int32_t* num_padded, void* ws, hipStream_t stream);
+
+// ------------------------------------------------------------------ fused decode
+constexpr int kDecodeMaxT = 16;
+size_t decode_ws_bytes(const moe_layer_t& L);
+hipError_t launch_decode(const moe_layer_t& L, const uint16_t* x, int T, const uint16_t* residual,
+                         uint16_t* y, void* ws, int32_t* ids_out, float* w_out,
+                         hipStream_t stream);
+// Offset of the status word inside a decode workspace.
+constexpr size_t kDecodeStatusOffset = 0;
+// Bytes of the counter region at the start of a decode workspace (zero at rest).
+size_t decode_sync_bytes(const moe_layer_t& L);
+
+// ------------------------------------------------------------------ grouped path
+size_t grouped_ws_bytes(const moe_layer_t& L, int T);
+hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const uint16_t* residual,
+                          uint16_t* y, void* ws, hipStream_t stream);
+
+}  // namespace mxmoe

@@ -1,0 +1,231 @@
+// Device helpers shared by the gfx950 kernels: MX element conversion in
+// integer arithmetic, scaled FP4/FP8 matrix-core wrappers, the router's
+// fixed-order dot product and wavefront reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxmoe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// MX element formats (OCP Microscaling Formats v1.0).  MB: mantissa bits,
+// EMIN: exponent of the smallest normal, EMAX: exponent of the largest power
+// of two (emax_elem of the scale rule), MAXC: largest finite magnitude code,
+// SIGN: sign bit position.
+// ---------------------------------------------------------------------------
+struct FP4 { static constexpr int MB = 1, EMIN = 0, EMAX = 2, MAXC = 0x7, SIGN = 3; };
+struct FP8 { static constexpr int MB = 3, EMIN = -6, EMAX = 8, MAXC = 0x7E, SIGN = 7; };
+
+// Block exponent floor(log2(amax)) - emax_elem, clamped below at -127, from
+// the fp32 bit pattern of the block's largest magnitude (sign cleared).  Zero
+// and subnormal maxima give -127.  fp32 inputs never reach the upper clamp.
+template <class F>
+__device__ __forceinline__ int block_exponent(uint32_t amax_bits) {
+  int e = (int)(amax_bits >> 23) - 127 - F::EMAX;
+  return e < -127 ? -127 : e;
+}
+
+// Element code of v * 2^-e, v given as an fp32 bit pattern: round to nearest,
+// ties to the even code, saturate to MAXC, sign bit copied.  Integer-only, so
+// the result does not depend on the floating-point or denormal mode.
+//   |v| = M * 2^(Ev-150) (M the 24-bit significand), q = |v| * 2^-e,
+//   p = floor(log2 q); the element grid spacing is 2^qe with
+//   qe = max(p, EMIN) - MB; n = RNE(q / 2^qe);
+//   code = (max(p - EMIN, 0) << MB) + n  (a carry into the next binade is
+//   absorbed by the same formula).  The right shift s below is always >= 1
+//   for e >= -127.
+template <class F>
+__device__ __forceinline__ uint32_t quant_elem(uint32_t bits, int e) {
+  const uint32_t sign = bits >> 31;
+  const uint32_t a = bits & 0x7fffffffu;
+  const int E = (int)(a >> 23);
+  uint32_t M = a & 0x7fffffu;
+  int Ev = 1;
+  if (E) { M |= 0x800000u; Ev = E; }
+  uint32_t code = 0;
+  if (M) {
+    const int msb = 31 - __clz(M);
+    const int p = msb + Ev - 150 - e;
+    const int pe = p > F::EMIN ? p : F::EMIN;
+    const int s = 150 + e + (pe - F::MB) - Ev;
+    uint32_t n = 0;
+    if (s < 32) {
+      n = M >> s;
+      const uint32_t rem = M & ((1u << s) - 1u);
+      const uint32_t half = 1u << (s - 1);
+      n += (rem > half) || (rem == half && (n & 1u));
+    }
+    const int base = p > F::EMIN ? p - F::EMIN : 0;
+    code = ((uint32_t)base << F::MB) + n;
+    if (code > (uint32_t)F::MAXC) code = F::MAXC;
+  }
+  return code | (sign << F::SIGN);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// fp32 -> bf16 round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Quantize 32 consecutive values (fp32 bit patterns) of one MX block held by
+// one lane.  FP4: 16 packed bytes (element 2i in the low nibble of byte i);
+// FP8: 32 bytes.  Returns the E8M0 scale code.
+template <class F>
+__device__ __forceinline__ uint32_t quant_block32(const uint32_t* bits, uint32_t* out_words) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = max(amax, bits[i] & 0x7fffffffu);
+  const int e = block_exponent<F>(amax);
+  if constexpr (F::MB == 1) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) word |= quant_elem<F>(bits[8 * w + i], e) << (4 * i);
+      out_words[w] = word;
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) word |= quant_elem<F>(bits[4 * w + i], e) << (8 * i);
+      out_words[w] = word;
+    }
+  }
+  return (uint32_t)(e + 127);
+}
+
+// ---------------------------------------------------------------------------
+// Scaled matrix instructions, 16x16x128 (gfx950).  Operand layout, verified on
+// the device: lane l supplies row l%16 of its operand.  FP4: 16 bytes holding
+// K = 32*(l/16) .. +32 (element 2i in the low nibble of byte i).  FP8: bytes
+// 0..15 hold K = 16*(l/16) .. +16, bytes 16..31 hold K = 64 + 16*(l/16) .. +16.
+// Scale operands: lane l gives the E8M0 of (row l%16, K block l/16) in the low
+// byte.  Result: lane l, element i = C[4*(l/16) + i][l%16] with C = A * B^T.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ v4f mfma_fp4(v4i a, v4i b, v4f c, uint32_t sa, uint32_t sb) {
+  v8i A = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  v8i B = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
+__device__ __forceinline__ v4f mfma_fp8(v4i a0, v4i a1, v4i b0, v4i b1, v4f c, uint32_t sa,
+                                        uint32_t sb) {
+  v8i A = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+  v8i B = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 0, 0, 0, (int)sa, 0, (int)sb);
+}
+
+// Streaming 16-byte load of weights (read once per call).
+__device__ __forceinline__ v4i load_stream16(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+}
+
+// ---------------------------------------------------------------------------
+// Router dot product, the fixed order every router path uses: lane l
+// accumulates with fp32 FMA the products for h = 256*i + 4*l + c (i ascending,
+// c = 0..3), then wave_sum_butterfly adds the 64 partial sums.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float router_lane_partial(const uint16_t* xrow, const float* wrow, int H,
+                                                     int lane) {
+  float p = 0.f;
+  for (int h = 4 * lane; h < H; h += 256) {
+    const float4 w = *reinterpret_cast<const float4*>(wrow + h);
+    const uint2 xv = *reinterpret_cast<const uint2*>(xrow + h);
+    p = fmaf(bf16_to_f32(xv.x & 0xffffu), w.x, p);
+    p = fmaf(bf16_to_f32(xv.x >> 16), w.y, p);
+    p = fmaf(bf16_to_f32(xv.y & 0xffffu), w.z, p);
+    p = fmaf(bf16_to_f32(xv.y >> 16), w.w, p);
+  }
+  return p;
+}
+
+// Butterfly sum over the 64 lanes; every lane ends with the same value
+// (fp32 addition is commutative, so partners compute identical sums).
+__device__ __forceinline__ float wave_sum_butterfly(float p) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) p += __shfl_xor(p, off);
+  return p;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v, int width) {
+  for (int off = width / 2; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off));
+  return v;
+}
+
+// Top-k key: order-preserving fp32 bits (with -0 folded onto +0) above the
+// complemented expert index, so the largest key is the largest logit and,
+// among equal logits, the lowest expert index.
+__device__ __forceinline__ uint64_t topk_key(float logit, int e) {
+  uint32_t b = __float_as_uint(logit + 0.0f);
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)b << 32) | (uint32_t)(0xffffu - (uint32_t)e);
+}
+
+__device__ __forceinline__ float topk_key_logit(uint64_t key) {
+  uint32_t b = (uint32_t)(key >> 32);
+  b = (b & 0x80000000u) ? (b & 0x7fffffffu) : ~b;
+  return __uint_as_float(b);
+}
+
+__device__ __forceinline__ int topk_key_expert(uint64_t key) {
+  return (int)(0xffffu - (uint32_t)(key & 0xffffu));
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, off);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), off);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Top-k of one row of E <= 256 logits by one wavefront.  Lane 0 writes
+// ids[0..k) in descending logit order and w[0..k) = softmax over the chosen
+// logits in fp32: z_j = exp(l_j - l_0), w_j = z_j / sum_j z_j with the sum
+// taken in j order.  ids / w may be LDS or global memory.
+__device__ __forceinline__ void wave_topk(const float* logits_row, int E, int k, int lane,
+                                          int32_t* ids, float* w) {
+  uint64_t key[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int e = lane + 64 * r;
+    key[r] = e < E ? topk_key(logits_row[e], e) : 0ull;
+  }
+  for (int j = 0; j < k; ++j) {
+    uint64_t m = key[0];
+#pragma unroll
+    for (int r = 1; r < 4; ++r) m = key[r] > m ? key[r] : m;
+    const uint64_t best = wave_max_u64(m);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (key[r] == best) key[r] = 0ull;
+    if (lane == 0) {
+      ids[j] = topk_key_expert(best);
+      w[j] = topk_key_logit(best);  // the logit for now
+    }
+  }
+  if (lane == 0) {
+    const float l0 = w[0];
+    float sum = 0.f;
+    for (int j = 0; j < k; ++j) sum += expf(w[j] - l0);
+    for (int j = 0; j < k; ++j) w[j] = expf(w[j] - l0) / sum;
+  }
+}
+
+}  // namespace mxmoe

@@ -1,0 +1,152 @@
+// MX quantization kernels: static weight quantization (fp32 -> MXFP4 / MXFP8,
+// row-major or tiled) and dynamic MXFP4 activation quantization (bf16 -> MXFP4).
+// One thread per 32-element block; the conversion is the integer routine in
+// mx_device.h, so results are bit-exact.
+#include "internal.h"
+#include "mx_device.h"
+
+namespace mxmoe {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Destination of the packed codes of block (r, b) of a [rows][cols] matrix.
+// Row-major: FP4 bytes [r][16b .. 16b+16), FP8 bytes [r][32b .. 32b+32).
+// Tiled (see mxmoe.h): FP4: one 16-byte piece; FP8: two 16-byte pieces.
+template <class F, bool Tiled>
+__device__ __forceinline__ void store_block(uint8_t* codes, uint8_t* scales, int r, int b, int cols,
+                                            const uint32_t* words, uint32_t scale) {
+  const int KT = cols / 128;
+  if constexpr (!Tiled) {
+    if constexpr (F::MB == 1) {
+      *reinterpret_cast<uint4*>(codes + (size_t)r * (cols / 2) + 16 * b) =
+          make_uint4(words[0], words[1], words[2], words[3]);
+    } else {
+      uint4* dst = reinterpret_cast<uint4*>(codes + (size_t)r * cols + 32 * b);
+      dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
+      dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
+    }
+    scales[(size_t)r * (cols / 32) + b] = (uint8_t)scale;
+  } else {
+    const int nt = r / 16, kt = b / 4, q = b % 4;
+    const int lane = (r % 16) + 16 * q;
+    if constexpr (F::MB == 1) {
+      uint8_t* tile = codes + ((size_t)nt * KT + kt) * 1024;
+      *reinterpret_cast<uint4*>(tile + 16 * lane) = make_uint4(words[0], words[1], words[2], words[3]);
+    } else {
+      // K offsets 32q .. 32q+32 inside the tile: the first 16 go to (c, q') =
+      // ((32q)/64, (32q%64)/16), the next 16 to the following q'.
+      uint8_t* tile = codes + ((size_t)nt * KT + kt) * 2048;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k0 = 32 * q + 16 * h;
+        const int c = k0 / 64, qq = (k0 % 64) / 16;
+        const int ll = (r % 16) + 16 * qq;
+        *reinterpret_cast<uint4*>(tile + 1024 * c + 16 * ll) =
+            make_uint4(words[4 * h], words[4 * h + 1], words[4 * h + 2], words[4 * h + 3]);
+      }
+    }
+    const int KG = (KT + 3) / 4;
+    const int g = kt / 4, i = kt % 4;
+    scales[(((size_t)nt * KG + g) * 64 + lane) * 4 + i] = (uint8_t)scale;
+  }
+}
+
+template <class F, bool Tiled>
+__global__ void __launch_bounds__(kThreads) quant_weights_kernel(const float* __restrict__ w,
+                                                                 int rows, int cols,
+                                                                 uint8_t* __restrict__ codes,
+                                                                 uint8_t* __restrict__ scales) {
+  const int nb = cols / 32;
+  const size_t blk = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (blk >= (size_t)rows * nb) return;
+  const int r = (int)(blk / nb), b = (int)(blk % nb);
+  const uint4* src = reinterpret_cast<const uint4*>(w + (size_t)r * cols + 32 * b);
+  uint32_t bits[32];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint4 v = src[i];
+    bits[4 * i] = v.x;
+    bits[4 * i + 1] = v.y;
+    bits[4 * i + 2] = v.z;
+    bits[4 * i + 3] = v.w;
+  }
+  uint32_t words[8];
+  const uint32_t s = quant_block32<F>(bits, words);
+  store_block<F, Tiled>(codes, scales, r, b, cols, words, s);
+}
+
+__global__ void __launch_bounds__(kThreads) quant_act_fp4_kernel(const uint16_t* __restrict__ x,
+                                                                 int rows, int cols,
+                                                                 uint8_t* __restrict__ codes,
+                                                                 uint8_t* __restrict__ scales) {
+  const int nb = cols / 32;
+  const size_t blk = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (blk >= (size_t)rows * nb) return;
+  const int r = (int)(blk / nb), b = (int)(blk % nb);
+  const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)r * cols + 32 * b);
+  uint32_t bits[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = src[i];
+    const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bits[8 * i + 2 * j] = p[j] << 16;
+      bits[8 * i + 2 * j + 1] = p[j] & 0xffff0000u;
+    }
+  }
+  uint32_t words[4];
+  const uint32_t s = quant_block32<FP4>(bits, words);
+  *reinterpret_cast<uint4*>(codes + (size_t)r * (cols / 2) + 16 * b) =
+      make_uint4(words[0], words[1], words[2], words[3]);
+  scales[(size_t)r * nb + b] = (uint8_t)s;
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+}  // namespace
+
+hipError_t launch_fill_u32(void* p, size_t words, uint32_t value, hipStream_t stream) {
+  if (words == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((words + 255) / 256);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(grid), dim3(256), 0, stream, (uint32_t*)p, words, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_weights(const float* w, int rows, int cols, int fmt, int layout,
+                                uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  const size_t nblk = (size_t)rows * (cols / 32);
+  const unsigned grid = (unsigned)((nblk + kThreads - 1) / kThreads);
+  if (layout == MX_LAYOUT_TILED) {
+    // scale bytes of K-tiles past the end of a group hold 127
+    const size_t sb = tiled_scales_bytes(rows, cols);
+    hipError_t err = launch_fill_u32(scales, sb / 4, 0x7f7f7f7fu, stream);
+    if (err != hipSuccess) return err;
+  }
+  if (fmt == MX_FMT_FP4) {
+    if (layout == MX_LAYOUT_TILED)
+      hipLaunchKernelGGL((quant_weights_kernel<FP4, true>), dim3(grid), dim3(kThreads), 0, stream, w, rows, cols, codes, scales);
+    else
+      hipLaunchKernelGGL((quant_weights_kernel<FP4, false>), dim3(grid), dim3(kThreads), 0, stream, w, rows, cols, codes, scales);
+  } else {
+    if (layout == MX_LAYOUT_TILED)
+      hipLaunchKernelGGL((quant_weights_kernel<FP8, true>), dim3(grid), dim3(kThreads), 0, stream, w, rows, cols, codes, scales);
+    else
+      hipLaunchKernelGGL((quant_weights_kernel<FP8, false>), dim3(grid), dim3(kThreads), 0, stream, w, rows, cols, codes, scales);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act_fp4(const uint16_t* x, int rows, int cols, uint8_t* codes,
+                                uint8_t* scales, hipStream_t stream) {
+  const size_t nblk = (size_t)rows * (cols / 32);
+  const unsigned grid = (unsigned)((nblk + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(quant_act_fp4_kernel, dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace mxmoe

@@ -1,0 +1,68 @@
+// Router logits and top-k for any number of rows (used on its own and by the
+// grouped path).  A workgroup takes a group of rows, keeps them in LDS, computes
+// the E logits of each row with the fixed-order dot product of mx_device.h and
+// then one wavefront per row selects the top k.
+#include "internal.h"
+#include "mx_device.h"
+
+namespace mxmoe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+__global__ void __launch_bounds__(kThreads) router_topk_kernel(
+    const uint16_t* __restrict__ x, int T, int H, int E, int k, int rows_per_wg,
+    const float* __restrict__ wr, const float* __restrict__ bias, float* __restrict__ logits_out,
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                               // [rows][H]
+  float* ls = reinterpret_cast<float*>(smem + align_up((size_t)rows_per_wg * H * 2, 16));  // [rows][E]
+  const int t0 = blockIdx.x * rows_per_wg;
+  const int nrows = min(rows_per_wg, T - t0);
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+
+  // stage the rows (16-byte copies; H % 128 == 0)
+  const int vec_per_row = H / 8;
+  for (int i = threadIdx.x; i < nrows * vec_per_row; i += kThreads) {
+    const int r = i / vec_per_row, c = i % vec_per_row;
+    reinterpret_cast<uint4*>(xs + (size_t)r * H)[c] =
+        reinterpret_cast<const uint4*>(x + (size_t)(t0 + r) * H)[c];
+  }
+  __syncthreads();
+
+  for (int e = wave; e < E; e += kWaves) {
+    const float* wrow = wr + (size_t)e * H;
+    const float b = bias ? bias[e] : 0.f;
+    for (int r = 0; r < nrows; ++r) {
+      float p = router_lane_partial(xs + (size_t)r * H, wrow, H, lane);
+      p = wave_sum_butterfly(p);
+      if (bias) p = p + b;
+      if (lane == 0) ls[r * E + e] = p;
+    }
+  }
+  __syncthreads();
+
+  if (logits_out) {
+    for (int i = threadIdx.x; i < nrows * E; i += kThreads)
+      logits_out[(size_t)t0 * E + i] = ls[i];
+  }
+  for (int r = wave; r < nrows; r += kWaves)
+    wave_topk(ls + r * E, E, k, lane, ids_out + (size_t)(t0 + r) * k, w_out + (size_t)(t0 + r) * k);
+}
+
+}  // namespace
+
+hipError_t launch_router_topk(const moe_layer_t& L, const uint16_t* x, int T, float* logits,
+                              int32_t* ids, float* w, hipStream_t stream) {
+  const int H = L.hidden, E = L.num_experts;
+  int rows = 32768 / H;
+  rows = rows < 1 ? 1 : (rows > 8 ? 8 : rows);
+  const size_t lds = align_up((size_t)rows * H * 2, 16) + (size_t)rows * E * 4;
+  const unsigned grid = (unsigned)((T + rows - 1) / rows);
+  hipLaunchKernelGGL(router_topk_kernel, dim3(grid), dim3(kThreads), lds, stream, x, T, H, E,
+                     L.top_k, rows, L.router_w, L.router_bias, logits, ids, w);
+  return hipGetLastError();
+}
+
+}  // namespace mxmoe

@@ -21,8 +21,10 @@ Draws: expert and shared weights fp32 N(0, 0.02); router weights fp32 N(0, 0.02)
 even of the fp32 draw).  Zipf bias: b_e = -s * ln(rank_e) with rank a seeded
 permutation of 1..E, so the prior over experts is proportional to rank^-s.
 
-Every tensor has its own PCG64 stream, ``default_rng([seed, workload, layer,
-tag, index])``, so any single expert can be regenerated on its own.
+Every tensor has its own stream, so any single expert can be regenerated on
+its own: on the host a PCG64 ``default_rng([seed, workload, layer, tag,
+index])``; for full-size expert and shared weights, torch's device Philox
+generator seeded from the same key (``device_*`` functions).
 """
 
 import math
@@ -114,12 +116,39 @@ def activations(cfg, layer=0, T=None, index=0):
     return f32_to_bf16_bits(g.standard_normal((T, cfg["H"]), dtype=np.float32))
 
 
-def device_normal_(tensor, seed, std=WEIGHT_STD):
-    """Fill a CUDA fp32 tensor with N(0, std^2) draws from torch's seeded
-    device generator (used where host generation would be too slow, e.g. the
-    many rotated layer copies a benchmark keeps resident)."""
+def _device_seed(cfg, layer, tag, index):
+    """64-bit seed for torch's device generator, mixed from the same key as
+    the host streams."""
+    h = 1469598103934665603
+    for v in (cfg["seed"], _WID[cfg["name"]], layer, _TAG[tag], index):
+        h = ((h ^ (int(v) & 0xFFFFFFFFFFFFFFFF)) * 1099511628211) & 0xFFFFFFFFFFFFFFFF
+    return h & 0x7FFFFFFFFFFFFFFF
+
+
+def _device_normal(cfg, layer, tag, index, shape, device):
     import torch
-    g = torch.Generator(device=tensor.device)
-    g.manual_seed(int(seed))
-    tensor.normal_(0.0, std, generator=g)
-    return tensor
+    g = torch.Generator(device=device)
+    g.manual_seed(_device_seed(cfg, layer, tag, index))
+    t = torch.empty(shape, dtype=torch.float32, device=device)
+    return t.normal_(0.0, WEIGHT_STD, generator=g)
+
+
+def device_expert_w13(cfg, layer, e, device="cuda"):
+    """fp32 [2I, H] N(0, 0.02) drawn on the device (torch's seeded Philox
+    generator): the full-size layers have 128 experts of 9.4M weights each,
+    too many to draw on the host for every test and benchmark run.  The oracle
+    reads the very same values back with ``.cpu()``."""
+    return _device_normal(cfg, layer, "w13", e, (2 * cfg["I"], cfg["H"]), device)
+
+
+def device_expert_w2(cfg, layer, e, device="cuda"):
+    """fp32 [H, I], as ``device_expert_w13``."""
+    return _device_normal(cfg, layer, "w2", e, (cfg["H"], cfg["I"]), device)
+
+
+def device_shared_w13(cfg, layer=0, device="cuda"):
+    return _device_normal(cfg, layer, "ws13", 0, (2 * cfg["I_s"], cfg["H"]), device)
+
+
+def device_shared_w2(cfg, layer=0, device="cuda"):
+    return _device_normal(cfg, layer, "ws2", 0, (cfg["H"], cfg["I_s"]), device)
