@@ -1,0 +1,252 @@
+"""Benchmark of the fused MXFP4 MoE decode layer on one MI355X.
+
+One step = one call of fused_moe_mxfp4_decode (router, top-k, MXFP4 routed
+experts, MXFP8 shared expert and combine in one launch) on the 1-row decode
+workload: T=1, H=3072, 128 experts top-4, I=1024, shared expert I_s=1024.
+Weights rotate over --rotate distinct layer instances (full expert sets, each
+653 MB) and every step reads a different input row, so the routed weights a
+step touches are not served from the 256 MB last-level cache.  The 16-row
+workload is measured the same way and reported beside it.
+
+Prints one JSON line.  `value` is the mean device time of one launch (HIP
+events recorded around every launch on the stream it runs on); `ms_per_step`
+is wall-clock time per step over the timed region.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def layer_bytes(H, I, E, Is, D, T, residual=False):
+    """Algorithmic HBM bytes of one layer call: router weights, D routed
+    experts (W13 + W2 codes and scales), the shared expert, x, y (+ residual)."""
+    routed = 3 * I * H * 17 // 32
+    shared = 3 * Is * H * 33 // 32
+    return E * H * 4 + D * routed + shared + (3 if residual else 2) * T * H * 2
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in ("decode.hip", "mx_device.h"):
+        with open(os.path.join(ROOT, "mxfp4_moe_decode_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    entry = rec.get(workload)
+    if not entry or entry.get("kernel_hash") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def build_layers(binding, synth, name, count):
+    import torch
+    cfg = synth.workload(name)
+    layers = []
+    for li in range(count):
+        layers.append(binding.MoELayer.from_fp32(
+            cfg["H"], cfg["I"], cfg["E"], cfg["k"], cfg["I_s"], synth.router_weights(cfg, li),
+            synth.router_bias(cfg, li), lambda e, li=li: synth.device_expert_w13(cfg, li, e),
+            lambda e, li=li: synth.device_expert_w2(cfg, li, e),
+            synth.device_shared_w13(cfg, li), synth.device_shared_w2(cfg, li)))
+    torch.cuda.synchronize()
+    return cfg, layers
+
+
+def time_decode(binding, synth, name, rotate, steps, warmup, pool=64):
+    import torch
+    cfg, layers = build_layers(binding, synth, name, rotate)
+    T = cfg["T"]
+    xs = [torch.from_numpy(synth.activations(cfg, T=T, index=j).view(np.int16)).cuda().view(torch.bfloat16)
+          for j in range(pool)]
+    ws = binding.decode_workspace(layers[0])
+    ys = [torch.empty_like(xs[0]) for _ in range(4)]
+    ids = torch.empty(steps, T, cfg["k"], dtype=torch.int32, device="cuda")
+    w = torch.empty(steps, T, cfg["k"], dtype=torch.float32, device="cuda")
+    lib = binding.load()
+    stream = torch.cuda.current_stream()
+    sp = binding.ctypes.c_void_p(stream.cuda_stream)
+
+    def launch(i, rec_ids=None, rec_w=None):
+        L = layers[i % rotate]
+        st = lib.fused_moe_mxfp4_decode(L.c, binding._ptr(xs[i % pool]), T, None, binding._ptr(ys[i % 4]),
+                                        binding._ptr(ws), ws.numel(), binding._ptr(rec_ids),
+                                        binding._ptr(rec_w), sp)
+        if st != 0:
+            raise binding.MoeError("fused_moe_mxfp4_decode", st)
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev0[i].record(stream)
+        launch(warmup + i, ids[i], w[i])
+        ev1[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dur_ms = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)])
+    if binding.moe_decode_status(ws) != 0:
+        raise RuntimeError("a device-side wait timed out during the benchmark")
+    ids_np = ids.cpu().numpy()
+    D = np.array([len(np.unique(ids_np[i])) for i in range(steps)])
+    nbytes = np.array([layer_bytes(cfg["H"], cfg["I"], cfg["E"], cfg["I_s"], d, T) for d in D])
+    us = dur_ms * 1e3
+    gbs = nbytes / (us * 1e-6) / 1e9
+    del layers
+    torch.cuda.empty_cache()
+    return {
+        "cfg": cfg, "us_mean": float(us.mean()), "us_median": float(np.median(us)),
+        "us_p10": float(np.percentile(us, 10)), "us_p90": float(np.percentile(us, 90)),
+        "wall_ms_per_step": wall / steps * 1e3, "bytes_mean": float(nbytes.mean()),
+        "gbs": float(nbytes.mean() / (us.mean() * 1e-6) / 1e9), "gbs_median": float(np.median(gbs)),
+        "distinct_experts_mean": float(D.mean()),
+    }
+
+
+def cpu_baseline(synth, seconds=15.0):
+    """The oracle, as it stands, on a bounded sample of the 1-row workload."""
+    import torch
+    from oracle import moe, mx
+    from threadpoolctl import threadpool_info
+
+    cfg = synth.workload("decode1")
+    layer = 0
+    x_all = [synth.activations(cfg, T=1, index=j) for j in range(64)]
+    wr = synth.router_weights(cfg, layer)
+    # quantize (outside the timed region) the experts the sample rows use
+    cache13, cache2 = {}, {}
+
+    def q13(e):
+        if e not in cache13:
+            cache13[e] = mx.mx_quantize(synth.device_expert_w13(cfg, layer, e).cpu().numpy().astype(np.float64), "fp4")
+        return cache13[e]
+
+    def q2(e):
+        if e not in cache2:
+            cache2[e] = mx.mx_quantize(synth.device_expert_w2(cfg, layer, e).cpu().numpy().astype(np.float64), "fp4")
+        return cache2[e]
+
+    class P:
+        def __init__(self, f, i):
+            self.f, self.i = f, i
+
+        def __getitem__(self, e):
+            return self.f(int(e))[self.i]
+
+    sc13, ss13 = mx.mx_quantize(synth.device_shared_w13(cfg, layer).cpu().numpy().astype(np.float64), "fp8")
+    sc2, ss2 = mx.mx_quantize(synth.device_shared_w2(cfg, layer).cpu().numpy().astype(np.float64), "fp8")
+    L = moe.Layer(cfg["H"], cfg["I"], cfg["E"], cfg["k"], cfg["I_s"], wr, None,
+                  P(q13, 0), P(q13, 1), P(q2, 0), P(q2, 1), sc13, ss13, sc2, ss2)
+    n_rows = 0
+    # warm the expert cache for the rows the sample will use
+    for x in x_all[:8]:
+        ids, _ = moe.select_topk(moe.router_logits(mx.bf16_bits_to_f64(x), wr), cfg["k"])
+        for e in ids.reshape(-1):
+            q13(int(e)), q2(int(e))
+    t0 = time.perf_counter()
+    while True:
+        moe.moe_layer(x_all[n_rows % 8], L)
+        n_rows += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": el / n_rows * 1e6, "unit": "us", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_rows} calls of the fp64 oracle layer on the 1-row workload "
+                      f"(T=1, H=3072, 128 experts top-4, I=1024, MXFP8 shared I_s=1024), "
+                      f"8 distinct input rows, weights pre-quantized"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate", type=int, default=16, help="distinct layer instances cycled through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-16", action="store_true", help="skip the 16-row measurement")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer is built and measured on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mxfp4_moe_decode_amd import binding, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.load()
+    r1 = time_decode(binding, synth, "decode1", args.rotate, args.steps, args.warmup)
+    print(f"[bench] 1 row: {r1['us_mean']:.2f} us mean, {r1['us_median']:.2f} us median, "
+          f"{r1['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    r16 = None
+    if not args.no_16:
+        r16 = time_decode(binding, synth, "decode16", max(4, args.rotate // 2), args.steps, args.warmup)
+        print(f"[bench] 16 rows: {r16['us_mean']:.2f} us mean, {r16['gbs']:.0f} GB/s, "
+              f"D={r16['distinct_experts_mean']:.1f}", file=sys.stderr, flush=True)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(synth, args.cpu_seconds)
+
+    traffic = load_traffic("decode1")
+    out = {
+        "metric": "fused MXFP4 MoE layer us at 1/16 rows; achieved HBM GB/s and % roofline",
+        "value": round(r1["us_mean"], 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r1["wall_ms_per_step"], 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4 (E2M1 x E8M0 routed, E4M3 x E8M0 shared, fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": "decode1: 1 bf16 row, hidden 3072, 128 MXFP4 experts top-4, "
+                               "intermediate 1024, MXFP8 shared expert 1024, one launch per layer",
+                   "rows": 1, "hidden": 3072, "experts": 128, "top_k": 4, "inter": 1024,
+                   "shared_inter": 1024, "rotated_layer_instances": args.rotate},
+        "us_median": round(r1["us_median"], 3),
+        "us_p10": round(r1["us_p10"], 3),
+        "us_p90": round(r1["us_p90"], 3),
+        "roofline": {"bound": "hbm", "achieved": round(r1["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(r1["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": int(r1["bytes_mean"])},
+    }
+    if r16:
+        out["rows16"] = {"us_mean": round(r16["us_mean"], 3), "us_median": round(r16["us_median"], 3),
+                         "gbs": round(r16["gbs"], 1), "frac": round(r16["gbs"] / HBM_PEAK_GBS, 4),
+                         "distinct_experts_mean": round(r16["distinct_experts_mean"], 2),
+                         "algorithmic_bytes_per_launch": int(r16["bytes_mean"]),
+                         "ms_per_step": round(r16["wall_ms_per_step"], 5)}
+    out["cpu_baseline"] = cpu
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

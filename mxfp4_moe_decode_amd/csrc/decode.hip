@@ -72,6 +72,7 @@ struct DecodeArgs {
 };
 
 struct Smem {
+  float logits[kDecodeMaxT * 256];
   int32_t ids[kMaxSlots];
   float w[kMaxSlots];
   uint8_t elist[kMaxSlots];
@@ -82,10 +83,40 @@ struct Smem {
 };
 
 // ------------------------------------------------------------------ synchronisation
+// Data handed from one workgroup to another (logits, quantized x, partial
+// sums, intermediate codes) is written and read with relaxed agent-scope
+// atomic accesses, which gfx950 issues with the sc1 bit: they are served at
+// the device's coherence point, past the per-XCD L2 caches, so no L2
+// write-back or invalidate is needed.  A producer waits for its stores to be
+// acknowledged (vmcnt 0) before it bumps a counter; a consumer polls the
+// counter and issues its data loads only after the poll has returned.
+template <class T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ v4i ld_dev16(const uint8_t* p) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t a = ld_dev(q), b = ld_dev(q + 1);
+  return v4i{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)(uint32_t)b, (int)(uint32_t)(b >> 32)};
+}
+__device__ __forceinline__ void st_dev16(uint8_t* p, uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  st_dev(q, (uint64_t)w0 | ((uint64_t)w1 << 32));
+  st_dev(q + 1, (uint64_t)w2 | ((uint64_t)w3 << 32));
+}
+// Wait until every vector memory access of this wavefront is acknowledged.
+__device__ __forceinline__ void drain_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Keeps the compiler from moving memory accesses across this point.
+__device__ __forceinline__ void compiler_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
+
 __device__ __forceinline__ void wait_count(uint32_t* ctr, uint32_t target, uint32_t* status) {
   const uint64_t t0 = wall_clock64();
-  while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
-    if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
+  while (ld_dev(ctr) < target) {
+    if (ld_dev(status)) return;
     if (wall_clock64() - t0 > kSpinTicks) {
       __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
@@ -95,24 +126,26 @@ __device__ __forceinline__ void wait_count(uint32_t* ctr, uint32_t target, uint3
 }
 
 __device__ __forceinline__ void wave_wait(uint32_t* ctr, uint32_t target, uint32_t* status, int lane) {
+  compiler_fence();
   if (lane == 0) wait_count(ctr, target, status);
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  compiler_fence();
 }
 
 __device__ __forceinline__ void wave_release_add(uint32_t* ctr, int lane) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  compiler_fence();
+  drain_stores();
   if (lane == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // True in every lane of the wavefront whose arrival completes the count.
 __device__ __forceinline__ bool wave_arrive_last(uint32_t* ctr, uint32_t target, int lane) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  compiler_fence();
+  drain_stores();
   uint32_t old = 0;
-  if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = (uint32_t)__shfl((int)old, 0);
-  if (old + 1 != target) return false;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return true;
+  compiler_fence();
+  return old + 1 == target;
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return (g / (1.f + expf(-g))) * u; }
@@ -135,15 +168,14 @@ __device__ void unit_xq(const DecodeArgs& A, int t, int lane) {
     }
     uint32_t words[8];
     uint32_t s = quant_block32<FP4>(bits, words);
-    *reinterpret_cast<uint4*>(A.xq4 + (size_t)t * (A.H / 2) + 16 * b) =
-        make_uint4(words[0], words[1], words[2], words[3]);
-    A.xs4[t * nb + b] = (uint8_t)s;
+    st_dev16(A.xq4 + (size_t)t * (A.H / 2) + 16 * b, words[0], words[1], words[2], words[3]);
+    st_dev(&A.xs4[t * nb + b], (uint8_t)s);
     if (A.Is) {
       s = quant_block32<FP8>(bits, words);
-      uint4* dst = reinterpret_cast<uint4*>(A.xq8 + (size_t)t * A.H + 32 * b);
-      dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
-      dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
-      A.xs8[t * nb + b] = (uint8_t)s;
+      uint8_t* dst = A.xq8 + (size_t)t * A.H + 32 * b;
+      st_dev16(dst, words[0], words[1], words[2], words[3]);
+      st_dev16(dst + 16, words[4], words[5], words[6], words[7]);
+      st_dev(&A.xs8[t * nb + b], (uint8_t)s);
     }
   }
   wave_release_add(&A.sync[S_XQ], lane);
@@ -153,7 +185,7 @@ __device__ void unit_router(const DecodeArgs& A, int e, int t, int lane) {
   float p = router_lane_partial(A.x + (size_t)t * A.H, A.router_w + (size_t)e * A.H, A.H, lane);
   p = wave_sum_butterfly(p);
   if (A.router_bias) p = p + A.router_bias[e];
-  if (lane == 0) A.logits[t * A.E + e] = p;
+  if (lane == 0) st_dev(&A.logits[t * A.E + e], p);
   wave_release_add(&A.sync[S_ROUTER], lane);
 }
 
@@ -166,19 +198,19 @@ __device__ void finalize_shared(const DecodeArgs& A, int nb, int lane) {
     float g = 0.f, u = 0.f;
     if (act) {
       const float* gp = A.sgu_part + (size_t)m * A.KS1 * (2 * Is) + 32 * nb + col;
-      g = gp[0];
-      u = gp[Is];
+      g = ld_dev(gp);
+      u = ld_dev(gp + Is);
       for (int kc = 1; kc < A.KS1; ++kc) {
-        g = g + gp[(size_t)kc * 2 * Is];
-        u = u + gp[(size_t)kc * 2 * Is + Is];
+        g = g + ld_dev(gp + (size_t)kc * 2 * Is);
+        u = u + ld_dev(gp + (size_t)kc * 2 * Is + Is);
       }
     }
     const uint32_t ab = __float_as_uint(silu_mul(g, u));
     const int e = block_exponent<FP8>(wave_max_u32(ab & 0x7fffffffu, 32));
     const uint32_t code = quant_elem<FP8>(ab, e);
     if (act) {
-      A.a8[(size_t)m * Is + 32 * nb + col] = (uint8_t)code;
-      if (col == 0) A.as8[m * (Is / 32) + nb] = (uint8_t)(e + 127);
+      st_dev(&A.a8[(size_t)m * Is + 32 * nb + col], (uint8_t)code);
+      if (col == 0) st_dev(&A.as8[m * (Is / 32) + nb], (uint8_t)(e + 127));
     }
   }
 }
@@ -207,21 +239,21 @@ __device__ void unit_shared_gu(const DecodeArgs& A, int st, int kc, int lane) {
       uint32_t sa = 127;
       if (m < A.T) {
         const uint8_t* ap = A.xq8 + (size_t)m * A.H + kt * 128 + 16 * q;
-        a0 = *reinterpret_cast<const v4i*>(ap);
-        a1 = *reinterpret_cast<const v4i*>(ap + 64);
-        sa = A.xs8[m * (A.H / 32) + 4 * kt + q];
+        a0 = ld_dev16(ap);
+        a1 = ld_dev16(ap + 64);
+        sa = ld_dev(&A.xs8[m * (A.H / 32) + 4 * kt + q]);
       }
       acc = mfma_fp8(a0, a1, B0[i], B1[i], acc, sa, (sb >> (8 * ((kt0 + i) & 3))) & 0xffu);
     }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int mm = 4 * q + r;
-    if (mm < A.T) A.sgu_part[((size_t)mm * A.KS1 + kc) * (2 * Is) + 16 * st + (lane & 15)] = acc[r];
+    if (mm < A.T) st_dev(&A.sgu_part[((size_t)mm * A.KS1 + kc) * (2 * Is) + 16 * st + (lane & 15)], acc[r]);
   }
   const int nb = ((16 * st) % Is) / 32;
   if (wave_arrive_last(&A.sgu_cnt[nb], 4 * A.KS1, lane)) {
     finalize_shared(A, nb, lane);
-    if (lane == 0) A.sgu_cnt[nb] = 0;
+    if (lane == 0) st_dev(&A.sgu_cnt[nb], 0u);
     wave_release_add(&A.sync[S_SA], lane);
   }
 }
@@ -264,19 +296,20 @@ __device__ void finalize_routed(const DecodeArgs& A, const Smem& sm, int dd, int
     float g = 0.f, u = 0.f;
     if (act) {
       const float* gp = A.gu_part + (size_t)slot * A.KS1 * (2 * I) + 32 * nb + col;
-      g = gp[0];
-      u = gp[I];
+      g = ld_dev(gp);
+      u = ld_dev(gp + I);
       for (int kc = 1; kc < A.KS1; ++kc) {
-        g = g + gp[(size_t)kc * 2 * I];
-        u = u + gp[(size_t)kc * 2 * I + I];
+        g = g + ld_dev(gp + (size_t)kc * 2 * I);
+        u = u + ld_dev(gp + (size_t)kc * 2 * I + I);
       }
     }
     const uint32_t ab = __float_as_uint(silu_mul(g, u));
     const int e = block_exponent<FP4>(wave_max_u32(ab & 0x7fffffffu, 32));
     const uint32_t code = quant_elem<FP4>(ab, e);
     const uint32_t hi = (uint32_t)__shfl_down((int)code, 1);
-    if (act && !(col & 1)) A.a4[(size_t)slot * (I / 2) + 16 * nb + col / 2] = (uint8_t)((code & 0xfu) | ((hi & 0xfu) << 4));
-    if (act && col == 0) A.as4[slot * (I / 32) + nb] = (uint8_t)(e + 127);
+    if (act && !(col & 1))
+      st_dev(&A.a4[(size_t)slot * (I / 2) + 16 * nb + col / 2], (uint8_t)((code & 0xfu) | ((hi & 0xfu) << 4)));
+    if (act && col == 0) st_dev(&A.as4[slot * (I / 32) + nb], (uint8_t)(e + 127));
   }
 }
 
@@ -302,8 +335,8 @@ __device__ void unit_routed_gu(const DecodeArgs& A, const Smem& sm, int dd, int 
       v4i a = {0, 0, 0, 0};
       uint32_t sa = 127;
       if (tok >= 0) {
-        a = *reinterpret_cast<const v4i*>(A.xq4 + (size_t)tok * (A.H / 2) + kt * 64 + 16 * q);
-        sa = A.xs4[tok * (A.H / 32) + 4 * kt + q];
+        a = ld_dev16(A.xq4 + (size_t)tok * (A.H / 2) + kt * 64 + 16 * q);
+        sa = ld_dev(&A.xs4[tok * (A.H / 32) + 4 * kt + q]);
       }
       acc = mfma_fp4(a, B[i], acc, sa, (sb >> (8 * ((kt0 + i) & 3))) & 0xffu);
     }
@@ -311,13 +344,13 @@ __device__ void unit_routed_gu(const DecodeArgs& A, const Smem& sm, int dd, int 
   for (int r = 0; r < 4; ++r) {
     const int mm = 4 * q + r;
     if (mm < n)
-      A.gu_part[((size_t)sm.tl[dd][mm] * A.KS1 + kc) * (2 * I) + 16 * st + (lane & 15)] = acc[r];
+      st_dev(&A.gu_part[((size_t)sm.tl[dd][mm] * A.KS1 + kc) * (2 * I) + 16 * st + (lane & 15)], acc[r]);
   }
   const int nb = ((16 * st) % I) / 32;
   uint32_t* cnt = &A.gu_cnt[e * (I / 32) + nb];
   if (wave_arrive_last(cnt, 4 * A.KS1, lane)) {
     finalize_routed(A, sm, dd, nb, lane);
-    if (lane == 0) *cnt = 0;
+    if (lane == 0) st_dev(cnt, 0u);
     wave_release_add(&A.a_ready[e], lane);
   }
 }
@@ -328,10 +361,10 @@ __device__ void combine(const DecodeArgs& A, const Smem& sm, int hs, int lane) {
   for (int idx = lane; idx < A.T * 16; idx += kWave) {
     const int t = idx >> 4, h = 16 * hs + (idx & 15);
     float acc = 0.f;
-    for (int j = 0; j < k; ++j) acc = fmaf(sm.w[t * k + j], A.d_part[(size_t)(t * k + j) * H + h], acc);
+    for (int j = 0; j < k; ++j) acc = fmaf(sm.w[t * k + j], ld_dev(&A.d_part[(size_t)(t * k + j) * H + h]), acc);
     if (A.Is) {
-      float s = A.s_part[(size_t)t * H + h];
-      for (int kh = 1; kh < A.SDS; ++kh) s = s + A.s_part[((size_t)kh * kDecodeMaxT + t) * H + h];
+      float s = ld_dev(&A.s_part[(size_t)t * H + h]);
+      for (int kh = 1; kh < A.SDS; ++kh) s = s + ld_dev(&A.s_part[((size_t)kh * kDecodeMaxT + t) * H + h]);
       acc = acc + s;
     }
     if (A.residual) acc = acc + bf16_to_f32(A.residual[(size_t)t * H + h]);
@@ -343,7 +376,7 @@ __device__ void arrive_output(const DecodeArgs& A, const Smem& sm, int hs, int l
   uint32_t* cnt = &A.comb_cnt[hs];
   if (wave_arrive_last(cnt, (uint32_t)(A.SDS + sm.D), lane)) {
     combine(A, sm, hs, lane);
-    if (lane == 0) *cnt = 0;
+    if (lane == 0) st_dev(cnt, 0u);
   }
 }
 
@@ -371,16 +404,16 @@ __device__ void unit_shared_down(const DecodeArgs& A, const Smem& sm, int hs, in
       uint32_t sa = 127;
       if (m < A.T) {
         const uint8_t* ap = A.a8 + (size_t)m * Is + kt * 128 + 16 * q;
-        a0 = *reinterpret_cast<const v4i*>(ap);
-        a1 = *reinterpret_cast<const v4i*>(ap + 64);
-        sa = A.as8[m * (Is / 32) + 4 * kt + q];
+        a0 = ld_dev16(ap);
+        a1 = ld_dev16(ap + 64);
+        sa = ld_dev(&A.as8[m * (Is / 32) + 4 * kt + q]);
       }
       acc = mfma_fp8(a0, a1, B0[i], B1[i], acc, sa, (sb >> (8 * ((kt0 + i) & 3))) & 0xffu);
     }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int mm = 4 * q + r;
-    if (mm < A.T) A.s_part[((size_t)kh * kDecodeMaxT + mm) * A.H + 16 * hs + (lane & 15)] = acc[r];
+    if (mm < A.T) st_dev(&A.s_part[((size_t)kh * kDecodeMaxT + mm) * A.H + 16 * hs + (lane & 15)], acc[r]);
   }
   arrive_output(A, sm, hs, lane);
 }
@@ -408,8 +441,8 @@ __device__ void unit_routed_down(const DecodeArgs& A, const Smem& sm, int dd, in
         v4i a = {0, 0, 0, 0};
         uint32_t sa = 127;
         if (slot >= 0) {
-          a = *reinterpret_cast<const v4i*>(A.a4 + (size_t)slot * (I / 2) + kt * 64 + 16 * q);
-          sa = A.as4[slot * (I / 32) + 4 * kt + q];
+          a = ld_dev16(A.a4 + (size_t)slot * (I / 2) + kt * 64 + 16 * q);
+          sa = ld_dev(&A.as4[slot * (I / 32) + 4 * kt + q]);
         }
         const uint32_t sbw = i < 4 ? sb0 : sb1;
         acc = mfma_fp4(a, B[i], acc, sa, (sbw >> (8 * (i & 3))) & 0xffu);
@@ -418,7 +451,7 @@ __device__ void unit_routed_down(const DecodeArgs& A, const Smem& sm, int dd, in
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int mm = 4 * q + r;
-    if (mm < n) A.d_part[(size_t)sm.tl[dd][mm] * A.H + 16 * hs + (lane & 15)] = acc[r];
+    if (mm < n) st_dev(&A.d_part[(size_t)sm.tl[dd][mm] * A.H + 16 * hs + (lane & 15)], acc[r]);
   }
   arrive_output(A, sm, hs, lane);
 }
@@ -452,9 +485,11 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DecodeArgs A) {
     wait_count(&A.sync[S_XQ], (uint32_t)T, A.sync);
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  compiler_fence();
+  for (int i = threadIdx.x; i < T * E; i += kThreads) sm.logits[i] = ld_dev(&A.logits[i]);
+  __syncthreads();
   for (int t = wave; t < T; t += kWavesPerWG)
-    wave_topk(A.logits + t * E, E, A.k, lane, sm.ids + t * A.k, sm.w + t * A.k);
+    wave_topk(sm.logits + t * E, E, A.k, lane, sm.ids + t * A.k, sm.w + t * A.k);
   __syncthreads();
   build_expert_list(A, sm, lane, wave);
   __syncthreads();
@@ -486,15 +521,17 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DecodeArgs A) {
   // exit: the last workgroup resets the launch-wide counters
   __syncthreads();
   if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const uint32_t old = __hip_atomic_fetch_add(&A.sync[S_DONE], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    compiler_fence();
+    drain_stores();
+    const uint32_t old = __hip_atomic_fetch_add(&A.sync[S_DONE], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    compiler_fence();
     if (old + 1 == (uint32_t)A.G) {
-      A.sync[S_ROUTER] = 0;
-      A.sync[S_XQ] = 0;
-      A.sync[S_SA] = 0;
-      for (int e = 0; e < E; ++e) A.a_ready[e] = 0;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      A.sync[S_DONE] = 0;
+      st_dev(&A.sync[S_ROUTER], 0u);
+      st_dev(&A.sync[S_XQ], 0u);
+      st_dev(&A.sync[S_SA], 0u);
+      for (int e = 0; e < E; ++e) st_dev(&A.a_ready[e], 0u);
+      drain_stores();
+      st_dev(&A.sync[S_DONE], 0u);
     }
   }
 }

@@ -10,9 +10,15 @@ Comparison rules (written here once, used by every parity test):
 * top-k ids: bit-exact for every row whose top-k is decided by more than twice
   that bound; a row with a closer call must hold a valid top-k of the GPU's own
   logits (several answers are correct there);
-* layer output: per row max|y - y_ref| / max|y_ref| <= 2e-2 (the stated
-  tolerance), and, stricter, at least 99% of elements within one bf16 ulp of
-  the oracle's correctly rounded bf16 value.
+* layer output: per row max|y - y_ref| / max|y_ref| <= 2e-2, the stated
+  tolerance, on every layer.  Stricter, for layers of routed experts alone:
+  99.9% of elements within one bf16 ulp of the oracle's correctly rounded
+  value, since their MXFP4 partial sums are exact in fp32 and only the final
+  rounding differs.  With the MXFP8 shared expert no element-share check is
+  made: its fp32 sums round, and where one lands within that rounding of an
+  E4M3 boundary of the re-quantized intermediate the code differs by one step
+  and the whole shared-output row moves by a few 1e-3 of its scale (within the
+  2e-2 tolerance); the share is printed as a diagnostic.
 """
 
 import numpy as np
@@ -120,9 +126,9 @@ def check_topk(ids_gpu, l_gpu, l_ref, bound, k):
     return exact
 
 
-def check_layer_output(y_bits, ref, tol=2e-2, ulp_frac=0.99):
+def check_layer_output(y_bits, ref, tol=2e-2, ulp_frac=None):
     """``ref`` is the oracle's output dict.  Returns (max row error, fraction
-    of elements within one bf16 ulp)."""
+    of elements within one bf16 ulp); ``ulp_frac`` enforces a minimum share."""
     y = mx.bf16_bits_to_f64(np.asarray(y_bits).astype(np.uint16))
     yr = ref["y"]
     row_err = np.abs(y - yr).max(axis=1) / np.maximum(np.abs(yr).max(axis=1), 1e-30)
@@ -130,6 +136,7 @@ def check_layer_output(y_bits, ref, tol=2e-2, ulp_frac=0.99):
     yb = mx.bf16_bits_to_f64(ref["y_bits"])
     _, ex = np.frexp(np.maximum(np.abs(yb), 2.0 ** -126))
     ulp = np.ldexp(1.0, ex.astype(np.int64) - 8)
-    within = np.mean(np.abs(y - yb) <= ulp)
-    assert within >= ulp_frac, f"only {within:.4f} of elements within one bf16 ulp"
-    return float(row_err.max()), float(within)
+    within = float(np.mean(np.abs(y - yb) <= ulp))
+    if ulp_frac is not None:
+        assert within >= ulp_frac, f"only {within:.4f} of elements within one bf16 ulp"
+    return float(row_err.max()), within
