@@ -209,6 +209,20 @@ moe_status fused_moe_mxfp4_grouped(const moe_layer_t* layer, const uint16_t* x, 
  */
 moe_status moe_decode_status(const void* ws, size_t ws_bytes);
 
+/*
+ * Diagnostic (synchronizes the device): phase timestamps of the last fused
+ * decode call on this workspace, in ticks of the device's 100 MHz constant
+ * clock.  Workgroup g fills words [8g, 8g+8): launch start, phase 1 done
+ * (x quantization, router, shared gate/up), routing known, phase 2 done
+ * (routed gate/up), phase 3 done (down projections and combine), end of its
+ * last phase-1 unit (0 if it had none), all logits seen, quantized x seen.
+ * Copies at most n_words words to host memory and returns
+ * the number of workgroups of that call (0 if none ran yet), or a negative
+ * moe_status.
+ */
+int moe_decode_trace(const moe_layer_t* layer, const void* ws, size_t ws_bytes, uint64_t* host,
+                     size_t n_words);
+
 const char* moe_status_string(moe_status status);
 
 #ifdef __cplusplus

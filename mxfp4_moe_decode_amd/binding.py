@@ -9,7 +9,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmxmoe.so")
+# MXMOE_LIB selects another build of the library (e.g. for A/B measurements);
+# by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("MXMOE_LIB") or os.path.join(_HERE, "libmxmoe.so")
 
 MX_FMT = {"fp4": 0, "fp8": 1}
 MX_LAYOUT = {"rowmajor": 0, "tiled": 1}
@@ -21,7 +23,7 @@ EXPORTS = [
     "mx_codes_bytes", "mx_scales_bytes", "mx_quantize_weights", "mxfp4_quant_act",
     "moe_router_topk", "moe_align_sort_capacity", "moe_align_sort_workspace_bytes", "moe_align_sort",
     "moe_workspace_bytes", "moe_workspace_init", "fused_moe_mxfp4_decode", "fused_moe_mxfp4_grouped",
-    "moe_decode_status", "moe_status_string",
+    "moe_decode_status", "moe_decode_trace", "moe_status_string",
 ]
 
 
@@ -71,6 +73,7 @@ def load():
         "fused_moe_mxfp4_decode": (S, [LP, P, I, P, P, P, Z, P, P, P]),
         "fused_moe_mxfp4_grouped": (S, [LP, P, I, P, P, P, Z, P]),
         "moe_decode_status": (S, [P, Z]),
+        "moe_decode_trace": (I, [LP, P, Z, P, Z]),
         "moe_status_string": (ctypes.c_char_p, [S]),
     }
     for name, (res, args) in sig.items():
@@ -294,3 +297,15 @@ def fused_moe_mxfp4_grouped(layer, x, residual=None, out=None, workspace=None):
 
 def moe_decode_status(workspace):
     return load().moe_decode_status(_ptr(workspace), workspace.numel())
+
+
+def moe_decode_trace(layer, workspace):
+    """Per-workgroup phase timestamps (device clock ticks) of the last decode
+    call on ``workspace``: an int64 array [grid, 8] (see mxmoe.h)."""
+    import numpy as np
+    buf = np.zeros(2048 * 8, dtype=np.uint64)
+    g = load().moe_decode_trace(layer.c, _ptr(workspace), workspace.numel(),
+                                buf.ctypes.data_as(ctypes.c_void_p), buf.size)
+    if g < 0:
+        raise MoeError("moe_decode_trace", g)
+    return buf[: g * 8].reshape(g, 8).astype(np.int64)

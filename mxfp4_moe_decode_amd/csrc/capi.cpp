@@ -158,6 +158,22 @@ moe_status moe_decode_status(const void* ws, size_t ws_bytes) {
   return status ? MOE_ERR_TIMEOUT : MOE_OK;
 }
 
+int moe_decode_trace(const moe_layer_t* layer, const void* ws, size_t ws_bytes, uint64_t* host,
+                     size_t n_words) {
+  if (check_layer(layer) != MOE_OK || !ws || !host) return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < decode_ws_bytes(*layer)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  uint32_t grid = 0;
+  if (hipMemcpy(&grid, static_cast<const char*>(ws) + kDecodeGridOffset, 4, hipMemcpyDeviceToHost) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  size_t n = (size_t)grid * kTraceWords;
+  if (n > n_words) n = n_words;
+  if (n && hipMemcpy(host, static_cast<const char*>(ws) + decode_trace_offset(*layer), n * 8,
+                     hipMemcpyDeviceToHost) != hipSuccess)
+    return MOE_ERR_HIP;
+  return (int)grid;
+}
+
 const char* moe_status_string(moe_status status) {
   switch (status) {
     case MOE_OK: return "ok";

@@ -40,6 +40,8 @@ hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int block_
 
 // ------------------------------------------------------------------ fused decode
 constexpr int kDecodeMaxT = 16;
+constexpr int kDecodeMaxGrid = 2048;
+constexpr int kTraceWords = 8;
 size_t decode_ws_bytes(const moe_layer_t& L);
 hipError_t launch_decode(const moe_layer_t& L, const uint16_t* x, int T, const uint16_t* residual,
                          uint16_t* y, void* ws, int32_t* ids_out, float* w_out,
@@ -48,6 +50,8 @@ hipError_t launch_decode(const moe_layer_t& L, const uint16_t* x, int T, const u
 constexpr size_t kDecodeStatusOffset = 0;
 // Bytes of the counter region at the start of a decode workspace (zero at rest).
 size_t decode_sync_bytes(const moe_layer_t& L);
+size_t decode_trace_offset(const moe_layer_t& L);
+constexpr size_t kDecodeGridOffset = 4 * 256;  // word holding the grid size of the last call
 
 // ------------------------------------------------------------------ grouped path
 size_t grouped_ws_bytes(const moe_layer_t& L, int T);

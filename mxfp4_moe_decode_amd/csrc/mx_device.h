@@ -141,13 +141,27 @@ __device__ __forceinline__ v4i load_stream16(const uint8_t* p) {
 __device__ __forceinline__ float router_lane_partial(const uint16_t* xrow, const float* wrow, int H,
                                                      int lane) {
   float p = 0.f;
-  for (int h = 4 * lane; h < H; h += 256) {
-    const float4 w = *reinterpret_cast<const float4*>(wrow + h);
-    const uint2 xv = *reinterpret_cast<const uint2*>(xrow + h);
-    p = fmaf(bf16_to_f32(xv.x & 0xffffu), w.x, p);
-    p = fmaf(bf16_to_f32(xv.x >> 16), w.y, p);
-    p = fmaf(bf16_to_f32(xv.y & 0xffffu), w.z, p);
-    p = fmaf(bf16_to_f32(xv.y >> 16), w.w, p);
+  // batches of 16 strides: all loads of a batch are issued before its FMAs
+  for (int h0 = 4 * lane; h0 < H; h0 += 16 * 256) {
+    float4 w[16];
+    uint2 xv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int h = h0 + 256 * j;
+      if (h < H) {
+        w[j] = *reinterpret_cast<const float4*>(wrow + h);
+        xv[j] = *reinterpret_cast<const uint2*>(xrow + h);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (h0 + 256 * j < H) {
+        p = fmaf(bf16_to_f32(xv[j].x & 0xffffu), w[j].x, p);
+        p = fmaf(bf16_to_f32(xv[j].x >> 16), w[j].y, p);
+        p = fmaf(bf16_to_f32(xv[j].y & 0xffffu), w[j].z, p);
+        p = fmaf(bf16_to_f32(xv[j].y >> 16), w[j].w, p);
+      }
+    }
   }
   return p;
 }
@@ -184,47 +198,66 @@ __device__ __forceinline__ int topk_key_expert(uint64_t key) {
   return (int)(0xffffu - (uint32_t)(key & 0xffffu));
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, off);
-    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), off);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+// Weights of a chosen top-k: z_j = exp(l_j - l_0), w_j = z_j / sum_j z_j in
+// fp32 with the sum taken in j order (l_0 is the largest logit).  In place:
+// w[] holds the chosen logits on entry.
+__device__ __forceinline__ void topk_weights_inplace(float* w, int k) {
+  const float l0 = w[0];
+  float sum = 0.f;
+  for (int j = 0; j < k; ++j) sum += expf(w[j] - l0);
+  for (int j = 0; j < k; ++j) w[j] = expf(w[j] - l0) / sum;
 }
 
-// Top-k of one row of E <= 256 logits by one wavefront.  Lane 0 writes
-// ids[0..k) in descending logit order and w[0..k) = softmax over the chosen
-// logits in fp32: z_j = exp(l_j - l_0), w_j = z_j / sum_j z_j with the sum
-// taken in j order.  ids / w may be LDS or global memory.
-__device__ __forceinline__ void wave_topk(const float* logits_row, int E, int k, int lane,
-                                          int32_t* ids, float* w) {
-  uint64_t key[4];
+constexpr int kTopkMax = 8;
+
+// Inserts key x into the descending list L[0..k) (k <= kTopkMax), dropping
+// the smallest.
+__device__ __forceinline__ void topk_insert(uint64_t (&L)[kTopkMax], uint64_t x, int k) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int e = lane + 64 * r;
-    key[r] = e < E ? topk_key(logits_row[e], e) : 0ull;
-  }
-  for (int j = 0; j < k; ++j) {
-    uint64_t m = key[0];
-#pragma unroll
-    for (int r = 1; r < 4; ++r) m = key[r] > m ? key[r] : m;
-    const uint64_t best = wave_max_u64(m);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (key[r] == best) key[r] = 0ull;
-    if (lane == 0) {
-      ids[j] = topk_key_expert(best);
-      w[j] = topk_key_logit(best);  // the logit for now
+  for (int j = 0; j < kTopkMax; ++j)
+    if (j < k && x > L[j]) {
+      const uint64_t t = L[j];
+      L[j] = x;
+      x = t;
     }
+}
+
+// Top-k of rows of E logits, G = 16 lanes per row: lane `sub` of a row scans
+// experts sub, sub+16, ... keeping its own top k, then the 16 lists are merged
+// by exchanges over lane distances 8, 4, 2, 1.  The top k of a set under the
+// key order is unique, so every lane ends with the same list.  Lane sub == 0
+// writes ids[0..k) (descending logit, ties to the lower expert) and w[0..k).
+// All 64 lanes of the wavefront must call it (rows past the end pass row = 0).
+__device__ __forceinline__ void rows_topk16(const float* logits_row, bool active, int E, int k, int sub,
+                                            int32_t* ids, float* w) {
+  uint64_t L[kTopkMax];
+#pragma unroll
+  for (int j = 0; j < kTopkMax; ++j) L[j] = 0ull;
+  if (active)
+    for (int e = sub; e < E; e += 16) topk_insert(L, topk_key(logits_row[e], e), k);
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) {
+    uint64_t P[kTopkMax];
+#pragma unroll
+    for (int j = 0; j < kTopkMax; ++j) {
+      if (j < k) {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)L[j], off);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(L[j] >> 32), off);
+        P[j] = ((uint64_t)hi << 32) | lo;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kTopkMax; ++j)
+      if (j < k) topk_insert(L, P[j], k);
   }
-  if (lane == 0) {
-    const float l0 = w[0];
-    float sum = 0.f;
-    for (int j = 0; j < k; ++j) sum += expf(w[j] - l0);
-    for (int j = 0; j < k; ++j) w[j] = expf(w[j] - l0) / sum;
+  if (active && sub == 0) {
+#pragma unroll
+    for (int j = 0; j < kTopkMax; ++j)
+      if (j < k) {
+        ids[j] = topk_key_expert(L[j]);
+        w[j] = topk_key_logit(L[j]);
+      }
+    topk_weights_inplace(w, k);
   }
 }
 

@@ -47,8 +47,13 @@ __global__ void __launch_bounds__(kThreads) router_topk_kernel(
     for (int i = threadIdx.x; i < nrows * E; i += kThreads)
       logits_out[(size_t)t0 * E + i] = ls[i];
   }
-  for (int r = wave; r < nrows; r += kWaves)
-    wave_topk(ls + r * E, E, k, lane, ids_out + (size_t)(t0 + r) * k, w_out + (size_t)(t0 + r) * k);
+  for (int r0 = 0; r0 < nrows; r0 += kThreads / 16) {
+    const int r = r0 + (int)threadIdx.x / 16;
+    const bool act = r < nrows;
+    const int rr = act ? r : 0;
+    rows_topk16(ls + rr * E, act, E, k, threadIdx.x & 15, ids_out + (size_t)(t0 + rr) * k,
+                w_out + (size_t)(t0 + rr) * k);
+  }
 }
 
 }  // namespace

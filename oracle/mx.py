@@ -97,6 +97,8 @@ def round_to_element(v, fmt):
     by the block scale).  Ties go to the even code; magnitudes beyond the
     largest finite value saturate to it; the sign bit is copied from v."""
     v = np.asarray(v, dtype=np.float64)
+    shape = v.shape
+    v = v.reshape(-1)
     grid = _magnitude_grid(fmt)
     max_code = FORMATS[fmt]["max_code"]
     mag = np.abs(v)
@@ -104,14 +106,14 @@ def round_to_element(v, fmt):
     i = np.searchsorted(grid, mag, side="right")
     lo = np.clip(i - 1, 0, max_code)
     hi = np.clip(i, 0, max_code)
-    d_lo = mag - grid[lo]
-    d_hi = grid[hi] - mag
+    d_lo = mag - np.take(grid, lo)
+    d_hi = np.take(grid, hi) - mag
     code = np.where(d_lo < d_hi, lo, hi)
     tie = d_lo == d_hi
     code = np.where(tie, np.where(lo % 2 == 0, lo, hi), code)
     code = np.where(mag >= grid[max_code], max_code, code)
     sign = np.signbit(v).astype(np.int64) << FORMATS[fmt]["sign_bit"]
-    return (code | sign).astype(np.uint8)
+    return (code | sign).astype(np.uint8).reshape(shape)
 
 
 def shared_exponent(amax, fmt):
