@@ -190,6 +190,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-16", action="store_true", help="skip the 16-row measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the measurement, run 5 plain elementwise copies (torch.neg, fp32) of this "
+                         "many MiB: a kernel of known traffic that calibrates the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -211,6 +214,15 @@ def main():
         r16 = time_decode(binding, synth, "decode16", max(4, args.rotate // 2), args.steps, args.warmup)
         print(f"[bench] 16 rows: {r16['us_mean']:.2f} us mean, {r16['gbs']:.0f} GB/s, "
               f"D={r16['distinct_experts_mean']:.1f}", file=sys.stderr, flush=True)
+    if args.copy_mib:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: 5 x torch.neg over {args.copy_mib} MiB fp32 "
+              f"(each reads and writes {args.copy_mib << 20} bytes)", file=sys.stderr, flush=True)
+        del src, dst
     cpu = None if args.no_cpu_baseline else cpu_baseline(synth, args.cpu_seconds)
 
     traffic = load_traffic("decode1")

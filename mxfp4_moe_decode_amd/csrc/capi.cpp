@@ -71,7 +71,7 @@ moe_status mxfp4_quant_act(const uint16_t* x, int rows, int cols, uint8_t* codes
   if (!x || !codes || !scales) return MOE_ERR_INVALID_ARGUMENT;
   if (rows <= 0 || cols <= 0 || cols % 32) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(codes, 16)) return MOE_ERR_INVALID_ARGUMENT;
-  return from_hip(launch_quant_act_fp4(x, rows, cols, codes, scales, stream));
+  return from_hip(launch_quant_act(x, rows, cols, MX_FMT_FP4, codes, scales, stream));
 }
 
 moe_status moe_router_topk(const moe_layer_t* layer, const uint16_t* x, int T, float* logits,

@@ -1,14 +1,486 @@
-// Grouped (prefill) path.  Not built yet: reports no workspace, so the entry
-// point returns MOE_ERR_UNSUPPORTED.
+// The MoE layer for any number of rows as a short sequence of launches on one
+// stream (the path the article "MiniMax-M3.1 on AMD Instinct GPUs: Day-0 support
+// and optimization" takes beyond the fused decode sizes, section "Serving with
+// vLLM / What we Optimized"):
+//
+//   1. router logits and top-k per row;
+//   2. align-sort of the T*k (row, choice) slots by expert, each expert's
+//      segment padded to kBM rows;
+//   3. MXFP4 (and, with a shared expert, MXFP8) quantization of x;
+//   4. routed gate/up: one grouped scaled-FP4 GEMM over the kBM-row blocks,
+//      epilogue SwiGLU and MXFP4 re-quantization of the intermediate;
+//   5. shared gate/up: dense scaled-FP8 GEMM, epilogue SwiGLU and MXFP8
+//      re-quantization;
+//   6. routed down: grouped scaled-FP4 GEMM, fp32 result per slot;
+//   7. shared down: dense scaled-FP8 GEMM whose epilogue is the combine
+//      (without a shared expert a separate combine kernel runs instead).
+//
+// Arithmetic is that of the fused decode kernel, step for step: the same
+// 16x16x128 scaled matrix instructions in K-chunks of CT tiles whose sums are
+// added in chunk order, the same SwiGLU / re-quantization and the same combine
+// order.  For the same rows and routing both paths give identical bits.
+//
+// GEMM tiling.  A workgroup of four wavefronts (2 x 2) owns a tile of rows x
+// columns; each wavefront holds MF row fragments of 16 and four column strips
+// of 16 (gate/up: two gate strips and the two matching up strips of one
+// 32-column intermediate block, so SwiGLU and the block re-quantization stay
+// inside the wavefront).  Weight tiles stream from the tiled MX layout straight
+// into the matrix-instruction operands; activation rows are read in place
+// (gathered through the sorted slots for the routed gate/up).  Operands of the
+// next K-tile are loaded while the current one is multiplied.  Workgroups are
+// numbered so that each XCD receives a contiguous run of tiles: the tiles of
+// one expert's blocks then share that XCD's L2.
 #include "internal.h"
+#include "mx_device.h"
 
 namespace mxmoe {
+namespace {
 
-size_t grouped_ws_bytes(const moe_layer_t&, int) { return 0; }
+constexpr int kThreads = 256;
+constexpr int kBM = 128;  // rows of a routed block (the align-sort block size)
+constexpr int kNF = 4;    // column strips per wavefront
 
-hipError_t launch_grouped(const moe_layer_t&, const uint16_t*, int, const uint16_t*, uint16_t*, void*,
-                          hipStream_t) {
-  return hipErrorNotSupported;
+enum Mode { GU_ROUTED = 0, GU_SHARED = 1, DOWN_ROUTED = 2, DOWN_SHARED = 3 };
+
+struct GemmArgs {
+  int T, k, H;
+  int MB, NT;               // row blocks and column tiles of the launch
+  int KT, CT, KG;           // K-tiles of 128, tiles per chunk, scale groups of 4 tiles
+  const uint8_t* a;         // activation codes, row-major
+  const uint8_t* as;        // activation scales, row-major [rows, K/32]
+  size_t a_stride, as_stride;
+  const uint8_t* b;         // weight codes, tiled layout
+  const uint8_t* bs;        // weight scales, tiled layout
+  size_t b_estride, bs_estride;  // per expert
+  const int32_t* sorted_slots;
+  const int32_t* block_expert;
+  const int32_t* num_padded;
+  int inter;                // gate/up: intermediate size
+  uint8_t* oc;              // gate/up: intermediate codes
+  uint8_t* os;              // gate/up: intermediate scales
+  float* d_part;            // routed down output [T*k, H]
+  const float* topk_w;      // shared down: routing weights [T, k]
+  const uint16_t* residual; // shared down: optional residual [T, H]
+  uint16_t* y;              // shared down: output [T, H]
+};
+
+template <class F>
+struct Frag {
+  static constexpr int R = F::MB == 1 ? 1 : 2;    // 16-byte register quads per operand row
+  static constexpr int MF = F::MB == 1 ? 4 : 2;   // row fragments per wavefront
+  static constexpr int BM = 2 * 16 * MF;          // rows per workgroup
+  static constexpr int TB = 1024 * R;             // bytes of one weight tile
+};
+
+__device__ __forceinline__ uint32_t row_move32(uint32_t v) {  // neighbour swap inside a quad
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint32_t row16_max32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xf, 0xf, false));
+  return v;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return (g / (1.f + expf(-g))) * u; }
+
+template <class F>
+struct Stage {
+  v4i a[Frag<F>::MF][Frag<F>::R];
+  v4i b[kNF][Frag<F>::R];
+  uint32_t sa[Frag<F>::MF];
+  uint32_t sw[kNF];
+};
+
+template <class F>
+__device__ __forceinline__ void load_stage(const GemmArgs& g, int kt, const int (&arow)[Frag<F>::MF],
+                                           const uint8_t* const (&bp)[kNF], const uint8_t* const (&sp)[kNF],
+                                           int q, Stage<F>& s) {
+  constexpr int MF = Frag<F>::MF, R = Frag<F>::R, TB = Frag<F>::TB;
+#pragma unroll
+  for (int i = 0; i < MF; ++i) {
+    if (arow[i] >= 0) {
+      const uint8_t* ap = g.a + (size_t)arow[i] * g.a_stride + (size_t)kt * 64 * R + 16 * q;
+#pragma unroll
+      for (int r = 0; r < R; ++r) s.a[i][r] = *reinterpret_cast<const v4i*>(ap + 64 * r);
+      const uint32_t w4 = *reinterpret_cast<const uint32_t*>(g.as + (size_t)arow[i] * g.as_stride + 4 * kt);
+      s.sa[i] = (w4 >> (8 * q)) & 0xffu;
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) s.a[i][r] = v4i{0, 0, 0, 0};
+      s.sa[i] = 127u;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kNF; ++j) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) s.b[j][r] = *reinterpret_cast<const v4i*>(bp[j] + (size_t)kt * TB + 1024 * r);
+    s.sw[j] = *reinterpret_cast<const uint32_t*>(sp[j] + (size_t)(kt >> 2) * 256);
+  }
+}
+
+template <class F>
+__device__ __forceinline__ void mma_stage(const Stage<F>& s, int kt, v4f (&acc)[Frag<F>::MF][kNF]) {
+  constexpr int MF = Frag<F>::MF;
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int j = 0; j < kNF; ++j) {
+      const uint32_t sb = (s.sw[j] >> (8 * (kt & 3))) & 0xffu;
+      if constexpr (F::MB == 1)
+        acc[i][j] = mfma_fp4(s.a[i][0], s.b[j][0], acc[i][j], s.sa[i], sb);
+      else
+        acc[i][j] = mfma_fp8(s.a[i][0], s.a[i][1], s.b[j][0], s.b[j][1], acc[i][j], s.sa[i], sb);
+    }
+}
+
+template <class F>
+__device__ __forceinline__ void end_chunk(int kt, int CT, v4f (&acc)[Frag<F>::MF][kNF],
+                                          v4f (&sum)[Frag<F>::MF][kNF]) {
+  if ((kt + 1) % CT) return;
+#pragma unroll
+  for (int i = 0; i < Frag<F>::MF; ++i)
+#pragma unroll
+    for (int j = 0; j < kNF; ++j) {
+      sum[i][j] = kt + 1 == CT ? acc[i][j] : sum[i][j] + acc[i][j];
+      acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+template <class F, int MODE>
+__global__ void __launch_bounds__(kThreads) grouped_gemm_kernel(GemmArgs g) {
+  using Fr = Frag<F>;
+  constexpr int MF = Fr::MF, BM = Fr::BM, TB = Fr::TB;
+  constexpr bool kRouted = MODE == GU_ROUTED || MODE == DOWN_ROUTED;
+  constexpr bool kGateUp = MODE == GU_ROUTED || MODE == GU_SHARED;
+  __shared__ int32_t slots[BM];
+
+  // XCD-aware order: consecutive workgroup ids go to different XCDs, so XCD x
+  // is given the contiguous run of tiles x*G/8 .. (x+1)*G/8 (G % 8 == 0).
+  const int G = gridDim.x, L = blockIdx.x;
+  const int tile = (L & 7) * (G >> 3) + (L >> 3);
+  const int mb = tile / g.NT, nt = tile % g.NT;
+  if (mb >= g.MB) return;
+  int e = 0;
+  if constexpr (kRouted) {
+    if (mb * BM >= *g.num_padded) return;
+    e = g.block_expert[mb];
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+  const int m = lane & 15, q = lane >> 4;
+  const int S = g.T * g.k;
+  if (threadIdx.x < BM) {
+    const int r = mb * BM + (int)threadIdx.x;
+    slots[threadIdx.x] = kRouted ? g.sorted_slots[r] : (r < g.T ? r : S);
+  }
+  __syncthreads();
+
+  // A rows of this lane's fragments (-1: padding, multiplied as zeros)
+  int arow[MF];
+#pragma unroll
+  for (int i = 0; i < MF; ++i) {
+    const int rl = wm * 16 * MF + 16 * i + m;
+    const int slot = slots[rl];
+    if constexpr (MODE == GU_ROUTED)
+      arow[i] = slot < S ? slot / g.k : -1;
+    else if constexpr (MODE == DOWN_ROUTED)
+      arow[i] = slot < S ? mb * BM + rl : -1;
+    else
+      arow[i] = slot < S ? mb * BM + rl : -1;  // shared: slot == row for real rows
+  }
+  // weight strips of this wavefront
+  int strip[kNF];
+  if constexpr (kGateUp) {
+    const int nb = 2 * nt + wn;
+    strip[0] = 2 * nb;
+    strip[1] = 2 * nb + 1;
+    strip[2] = g.inter / 16 + 2 * nb;
+    strip[3] = g.inter / 16 + 2 * nb + 1;
+  } else {
+#pragma unroll
+    for (int j = 0; j < kNF; ++j) strip[j] = 8 * nt + 4 * wn + j;
+  }
+  const uint8_t* bp[kNF];
+  const uint8_t* sp[kNF];
+#pragma unroll
+  for (int j = 0; j < kNF; ++j) {
+    bp[j] = g.b + (size_t)e * g.b_estride + (size_t)strip[j] * g.KT * TB + lane * 16;
+    sp[j] = g.bs + (size_t)e * g.bs_estride + ((size_t)strip[j] * g.KG * 64 + lane) * 4;
+  }
+
+  v4f acc[MF][kNF], sum[MF][kNF];
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int j = 0; j < kNF; ++j) acc[i][j] = sum[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  Stage<F> s0, s1;
+  const int KT = g.KT, CT = g.CT;
+  load_stage<F>(g, 0, arow, bp, sp, q, s0);
+  for (int kt = 0; kt < KT; kt += 2) {
+    if (kt + 1 < KT) load_stage<F>(g, kt + 1, arow, bp, sp, q, s1);
+    mma_stage<F>(s0, kt, acc);
+    end_chunk<F>(kt, CT, acc, sum);
+    if (kt + 1 < KT) {
+      if (kt + 2 < KT) load_stage<F>(g, kt + 2, arow, bp, sp, q, s0);
+      mma_stage<F>(s1, kt + 1, acc);
+      end_chunk<F>(kt + 1, CT, acc, sum);
+    }
+  }
+
+  // ---------------------------------------------------------------- epilogues
+  if constexpr (kGateUp) {
+    // SwiGLU on the 32 columns of block nb, then MX re-quantization of each
+    // row's block.  sum[i][0], sum[i][1]: gate columns m and 16 + m; sum[i][2],
+    // sum[i][3]: the matching up columns.  Output row of the intermediate: the
+    // sorted position (routed) or the row (shared).
+    const int nb = 2 * nt + wn;
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rl = wm * 16 * MF + 16 * i + 4 * q + r;
+        const bool valid = slots[rl] < S;
+        const int orow = mb * BM + rl;
+        const uint32_t a0 = __float_as_uint(silu_mul(sum[i][0][r], sum[i][2][r]));
+        const uint32_t a1 = __float_as_uint(silu_mul(sum[i][1][r], sum[i][3][r]));
+        const uint32_t am = row16_max32(max(a0 & 0x7fffffffu, a1 & 0x7fffffffu));
+        const int ex = block_exponent<F>(am);
+        const uint32_t c0 = quant_elem<F>(a0, ex), c1 = quant_elem<F>(a1, ex);
+        if constexpr (F::MB == 1) {
+          const uint32_t n0 = row_move32(c0), n1 = row_move32(c1);
+          if (valid && !(m & 1)) {
+            uint8_t* op = g.oc + (size_t)orow * (g.inter / 2) + 16 * nb + m / 2;
+            op[0] = (uint8_t)((c0 & 0xfu) | ((n0 & 0xfu) << 4));
+            op[8] = (uint8_t)((c1 & 0xfu) | ((n1 & 0xfu) << 4));
+          }
+        } else {
+          if (valid) {
+            uint8_t* op = g.oc + (size_t)orow * g.inter + 32 * nb + m;
+            op[0] = (uint8_t)c0;
+            op[16] = (uint8_t)c1;
+          }
+        }
+        if (valid && m == 0) g.os[(size_t)orow * (g.inter / 32) + nb] = (uint8_t)(ex + 127);
+      }
+  } else if constexpr (MODE == DOWN_ROUTED) {
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int slot = slots[wm * 16 * MF + 16 * i + 4 * q + r];
+        if (slot < S) {
+#pragma unroll
+          for (int j = 0; j < kNF; ++j) g.d_part[(size_t)slot * g.H + 16 * strip[j] + m] = sum[i][j][r];
+        }
+      }
+  } else {
+    // combine: y = bf16( sum_j w_j d_j (j in order) + s + residual )
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = mb * BM + wm * 16 * MF + 16 * i + 4 * q + r;
+        if (t < g.T) {
+#pragma unroll
+          for (int j = 0; j < kNF; ++j) {
+            const int h = 16 * strip[j] + m;
+            float c = 0.f;
+            for (int jj = 0; jj < g.k; ++jj)
+              c = fmaf(g.topk_w[t * g.k + jj], g.d_part[(size_t)(t * g.k + jj) * g.H + h], c);
+            c = c + sum[i][j][r];
+            if (g.residual) c = c + bf16_to_f32(g.residual[(size_t)t * g.H + h]);
+            g.y[(size_t)t * g.H + h] = f32_to_bf16(c);
+          }
+        }
+      }
+  }
+}
+
+// Combine without a shared expert: y = bf16( sum_j w_j d_j + residual ).
+__global__ void __launch_bounds__(kThreads) combine_kernel(int T, int k, int H, const float* __restrict__ topk_w,
+                                                           const float* __restrict__ d_part,
+                                                           const uint16_t* residual, uint16_t* y) {
+  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= (size_t)T * H) return;
+  const int t = (int)(idx / H), h = (int)(idx % H);
+  float c = 0.f;
+  for (int j = 0; j < k; ++j) c = fmaf(topk_w[t * k + j], d_part[(size_t)(t * k + j) * H + h], c);
+  if (residual) c = c + bf16_to_f32(residual[idx]);
+  y[idx] = f32_to_bf16(c);
+}
+
+int pick_chunk(int tiles) { return tiles % 4 == 0 ? 4 : (tiles % 2 == 0 ? 2 : 1); }
+
+struct GCarve {
+  size_t ids, w, sort_ws, sorted, bexp, eoff, npad, xq4, xs4, xq8, xs8, a4, as4, a8, as8, d_part, total;
+  size_t cap, nblk;
+};
+
+GCarve gcarve(const moe_layer_t& L, int T) {
+  const size_t H = L.hidden, I = L.inter, E = L.num_experts, k = L.top_k, Is = L.shared_inter;
+  const size_t S = (size_t)T * k;
+  GCarve c{};
+  c.cap = S + (S < E ? S : E) * (kBM - 1);
+  c.nblk = (c.cap + kBM - 1) / kBM;
+  const size_t rows = c.nblk * kBM;  // every sorted position a block can touch
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, 256); return at; };
+  c.ids = take(S * 4);
+  c.w = take(S * 4);
+  c.sort_ws = take(align_sort_ws_bytes(T, (int)k, (int)E));
+  c.sorted = take(rows * 4);
+  c.bexp = take(c.nblk * 4);
+  c.eoff = take((E + 1) * 4);
+  c.npad = take(4);
+  c.xq4 = take((size_t)T * H / 2);
+  c.xs4 = take((size_t)T * H / 32);
+  c.xq8 = Is ? take((size_t)T * H) : 0;
+  c.xs8 = Is ? take((size_t)T * H / 32) : 0;
+  c.a4 = take(rows * I / 2);
+  c.as4 = take(rows * I / 32);
+  c.a8 = Is ? take((size_t)T * Is) : 0;
+  c.as8 = Is ? take((size_t)T * Is / 32) : 0;
+  c.d_part = take(S * H * 4);
+  c.total = o;
+  return c;
+}
+
+unsigned grid8(int tiles) { return (unsigned)((tiles + 7) / 8 * 8); }
+
+template <class F, int MODE>
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
+  hipLaunchKernelGGL((grouped_gemm_kernel<F, MODE>), dim3(grid8(g.MB * g.NT)), dim3(kThreads), 0, stream, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t grouped_ws_bytes(const moe_layer_t& L, int T) { return gcarve(L, T).total; }
+
+hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const uint16_t* residual,
+                          uint16_t* y, void* ws, hipStream_t stream) {
+  const GCarve c = gcarve(L, T);
+  char* base = reinterpret_cast<char*>(ws);
+  auto at = [&](size_t off) { return base + off; };
+  const int H = L.hidden, I = L.inter, E = L.num_experts, k = L.top_k, Is = L.shared_inter;
+  int32_t* ids = reinterpret_cast<int32_t*>(at(c.ids));
+  float* w = reinterpret_cast<float*>(at(c.w));
+  int32_t* sorted = reinterpret_cast<int32_t*>(at(c.sorted));
+  int32_t* bexp = reinterpret_cast<int32_t*>(at(c.bexp));
+  int32_t* npad = reinterpret_cast<int32_t*>(at(c.npad));
+  uint8_t* xq4 = reinterpret_cast<uint8_t*>(at(c.xq4));
+  uint8_t* xs4 = reinterpret_cast<uint8_t*>(at(c.xs4));
+  uint8_t* a4 = reinterpret_cast<uint8_t*>(at(c.a4));
+  uint8_t* as4 = reinterpret_cast<uint8_t*>(at(c.as4));
+  float* d_part = reinterpret_cast<float*>(at(c.d_part));
+  hipError_t err;
+  if ((err = launch_router_topk(L, x, T, nullptr, ids, w, stream)) != hipSuccess) return err;
+  if ((err = launch_align_sort(ids, T, k, E, kBM, sorted, bexp, reinterpret_cast<int32_t*>(at(c.eoff)), npad,
+                               at(c.sort_ws), stream)) != hipSuccess)
+    return err;
+  if ((err = launch_quant_act(x, T, H, MX_FMT_FP4, xq4, xs4, stream)) != hipSuccess) return err;
+
+  GemmArgs g{};
+  g.T = T;
+  g.k = k;
+  g.H = H;
+  g.sorted_slots = sorted;
+  g.block_expert = bexp;
+  g.num_padded = npad;
+  // routed gate/up: A = MXFP4 x gathered by slot, B = W13[e]
+  {
+    GemmArgs r = g;
+    r.MB = (int)c.nblk;
+    r.NT = I / 64;
+    r.KT = H / 128;
+    r.CT = pick_chunk(r.KT);
+    r.KG = (r.KT + 3) / 4;
+    r.a = xq4;
+    r.as = xs4;
+    r.a_stride = H / 2;
+    r.as_stride = H / 32;
+    r.b = L.w13;
+    r.bs = L.w13_scale;
+    r.b_estride = tiled_codes_bytes(2 * I, H, MX_FMT_FP4);
+    r.bs_estride = tiled_scales_bytes(2 * I, H);
+    r.inter = I;
+    r.oc = a4;
+    r.os = as4;
+    if ((err = launch_gemm<FP4, GU_ROUTED>(r, stream)) != hipSuccess) return err;
+  }
+  // routed down: A = intermediate in sorted order, B = W2[e], out d_part[slot]
+  {
+    GemmArgs r = g;
+    r.MB = (int)c.nblk;
+    r.NT = H / 128;
+    r.KT = I / 128;
+    r.CT = pick_chunk(r.KT);
+    r.KG = (r.KT + 3) / 4;
+    r.a = a4;
+    r.as = as4;
+    r.a_stride = I / 2;
+    r.as_stride = I / 32;
+    r.b = L.w2;
+    r.bs = L.w2_scale;
+    r.b_estride = tiled_codes_bytes(H, I, MX_FMT_FP4);
+    r.bs_estride = tiled_scales_bytes(H, I);
+    r.d_part = d_part;
+    if ((err = launch_gemm<FP4, DOWN_ROUTED>(r, stream)) != hipSuccess) return err;
+  }
+  if (Is == 0) {
+    const size_t n = (size_t)T * H;
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
+                       T, k, H, w, d_part, residual, y);
+    return hipGetLastError();
+  }
+  uint8_t* xq8 = reinterpret_cast<uint8_t*>(at(c.xq8));
+  uint8_t* xs8 = reinterpret_cast<uint8_t*>(at(c.xs8));
+  uint8_t* a8 = reinterpret_cast<uint8_t*>(at(c.a8));
+  uint8_t* as8 = reinterpret_cast<uint8_t*>(at(c.as8));
+  if ((err = launch_quant_act(x, T, H, MX_FMT_FP8, xq8, xs8, stream)) != hipSuccess) return err;
+  constexpr int BM8 = Frag<FP8>::BM;
+  // shared gate/up: A = MXFP8 x, B = Ws13
+  {
+    GemmArgs r = g;
+    r.MB = (T + BM8 - 1) / BM8;
+    r.NT = Is / 64;
+    r.KT = H / 128;
+    r.CT = pick_chunk(r.KT);
+    r.KG = (r.KT + 3) / 4;
+    r.a = xq8;
+    r.as = xs8;
+    r.a_stride = H;
+    r.as_stride = H / 32;
+    r.b = L.ws13;
+    r.bs = L.ws13_scale;
+    r.inter = Is;
+    r.oc = a8;
+    r.os = as8;
+    if ((err = launch_gemm<FP8, GU_SHARED>(r, stream)) != hipSuccess) return err;
+  }
+  // shared down + combine
+  {
+    GemmArgs r = g;
+    r.MB = (T + BM8 - 1) / BM8;
+    r.NT = H / 128;
+    r.KT = Is / 128;
+    r.CT = pick_chunk(r.KT);
+    r.KG = (r.KT + 3) / 4;
+    r.a = a8;
+    r.as = as8;
+    r.a_stride = Is;
+    r.as_stride = Is / 32;
+    r.b = L.ws2;
+    r.bs = L.ws2_scale;
+    r.d_part = d_part;
+    r.topk_w = w;
+    r.residual = residual;
+    r.y = y;
+    if ((err = launch_gemm<FP8, DOWN_SHARED>(r, stream)) != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace mxmoe

@@ -23,8 +23,10 @@ __host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a -
 // ------------------------------------------------------------------ quantization
 hipError_t launch_quant_weights(const float* w, int rows, int cols, int fmt, int layout,
                                 uint8_t* codes, uint8_t* scales, hipStream_t stream);
-hipError_t launch_quant_act_fp4(const uint16_t* x, int rows, int cols, uint8_t* codes,
-                                uint8_t* scales, hipStream_t stream);
+// Row-major activation quantization: codes [rows, cols/2] (FP4) or [rows, cols]
+// (FP8), scales [rows, cols/32].
+hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int fmt, uint8_t* codes,
+                            uint8_t* scales, hipStream_t stream);
 hipError_t launch_fill_u32(void* p, size_t words, uint32_t value, hipStream_t stream);
 
 // ------------------------------------------------------------------ router

@@ -210,55 +210,56 @@ __device__ __forceinline__ void topk_weights_inplace(float* w, int k) {
 
 constexpr int kTopkMax = 8;
 
-// Inserts key x into the descending list L[0..k) (k <= kTopkMax), dropping
-// the smallest.
-__device__ __forceinline__ void topk_insert(uint64_t (&L)[kTopkMax], uint64_t x, int k) {
-#pragma unroll
-  for (int j = 0; j < kTopkMax; ++j)
-    if (j < k && x > L[j]) {
-      const uint64_t t = L[j];
-      L[j] = x;
-      x = t;
-    }
+// Moves a 64-bit value between the lanes of a 16-lane row with one data-parallel
+// permutation (CTRL: quad_perm or row mirror patterns, which stay inside the row).
+template <int CTRL>
+__device__ __forceinline__ uint64_t row_move64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// Top-k of rows of E logits, G = 16 lanes per row: lane `sub` of a row scans
-// experts sub, sub+16, ... keeping its own top k, then the 16 lists are merged
-// by exchanges over lane distances 8, 4, 2, 1.  The top k of a set under the
-// key order is unique, so every lane ends with the same list.  Lane sub == 0
-// writes ids[0..k) (descending logit, ties to the lower expert) and w[0..k).
-// All 64 lanes of the wavefront must call it (rows past the end pass row = 0).
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Maximum over the 16 lanes of a row: swap neighbours, swap pairs, mirror
+// each half row, mirror the row.  Every lane ends with the maximum.
+__device__ __forceinline__ uint64_t row16_max64(uint64_t v) {
+  v = max_u64(v, row_move64<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max_u64(v, row_move64<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max_u64(v, row_move64<0x141>(v));  // row_half_mirror
+  v = max_u64(v, row_move64<0x140>(v));  // row_mirror
+  return v;
+}
+
+// Top k of one row of E <= 256 logits on the 16 lanes of a row: lane `sub`
+// holds the keys of experts sub, sub+16, ...; k rounds each take the row-wide
+// largest key and retire it.  Keys are unique (they carry the expert index), so
+// the result is the top k under the key order.  Lane sub == 0 of an active row
+// writes ids[0..k) (descending logit, ties to the lower expert) and w[0..k)
+// (it reads w back to form the weights).  All 64 lanes of the wavefront must
+// call it, rows past the end with active = false; k is uniform.
 __device__ __forceinline__ void rows_topk16(const float* logits_row, bool active, int E, int k, int sub,
                                             int32_t* ids, float* w) {
-  uint64_t L[kTopkMax];
+  uint64_t key[16];
 #pragma unroll
-  for (int j = 0; j < kTopkMax; ++j) L[j] = 0ull;
-  if (active)
-    for (int e = sub; e < E; e += 16) topk_insert(L, topk_key(logits_row[e], e), k);
+  for (int r = 0; r < 16; ++r) {
+    const int e = sub + 16 * r;
+    key[r] = (active && e < E) ? topk_key(logits_row[e], e) : 0ull;  // 0 is below every real key
+  }
+#pragma unroll 1
+  for (int j = 0; j < k; ++j) {
+    uint64_t m = key[0];
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) {
-    uint64_t P[kTopkMax];
+    for (int r = 1; r < 16; ++r) m = max_u64(m, key[r]);
+    m = row16_max64(m);
 #pragma unroll
-    for (int j = 0; j < kTopkMax; ++j) {
-      if (j < k) {
-        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)L[j], off);
-        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(L[j] >> 32), off);
-        P[j] = ((uint64_t)hi << 32) | lo;
-      }
+    for (int r = 0; r < 16; ++r) key[r] = key[r] == m ? 0ull : key[r];
+    if (active && sub == 0) {
+      ids[j] = topk_key_expert(m);
+      w[j] = topk_key_logit(m);
     }
-#pragma unroll
-    for (int j = 0; j < kTopkMax; ++j)
-      if (j < k) topk_insert(L, P[j], k);
   }
-  if (active && sub == 0) {
-#pragma unroll
-    for (int j = 0; j < kTopkMax; ++j)
-      if (j < k) {
-        ids[j] = topk_key_expert(L[j]);
-        w[j] = topk_key_logit(L[j]);
-      }
-    topk_weights_inplace(w, k);
-  }
+  if (active && sub == 0) topk_weights_inplace(w, k);
 }
 
 }  // namespace mxmoe

@@ -76,10 +76,10 @@ __global__ void __launch_bounds__(kThreads) quant_weights_kernel(const float* __
   store_block<F, Tiled>(codes, scales, r, b, cols, words, s);
 }
 
-__global__ void __launch_bounds__(kThreads) quant_act_fp4_kernel(const uint16_t* __restrict__ x,
-                                                                 int rows, int cols,
-                                                                 uint8_t* __restrict__ codes,
-                                                                 uint8_t* __restrict__ scales) {
+template <class F>
+__global__ void __launch_bounds__(kThreads) quant_act_kernel(const uint16_t* __restrict__ x, int rows,
+                                                             int cols, uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales) {
   const int nb = cols / 32;
   const size_t blk = (size_t)blockIdx.x * kThreads + threadIdx.x;
   if (blk >= (size_t)rows * nb) return;
@@ -96,10 +96,12 @@ __global__ void __launch_bounds__(kThreads) quant_act_fp4_kernel(const uint16_t*
       bits[8 * i + 2 * j + 1] = p[j] & 0xffff0000u;
     }
   }
-  uint32_t words[4];
-  const uint32_t s = quant_block32<FP4>(bits, words);
-  *reinterpret_cast<uint4*>(codes + (size_t)r * (cols / 2) + 16 * b) =
-      make_uint4(words[0], words[1], words[2], words[3]);
+  constexpr int kWords = F::MB == 1 ? 4 : 8;  // 16 or 32 code bytes per block
+  uint32_t words[kWords];
+  const uint32_t s = quant_block32<F>(bits, words);
+  uint4* dst = reinterpret_cast<uint4*>(codes + ((size_t)r * nb + b) * (4 * kWords));
+#pragma unroll
+  for (int w = 0; w < kWords; w += 4) dst[w / 4] = make_uint4(words[w], words[w + 1], words[w + 2], words[w + 3]);
   scales[(size_t)r * nb + b] = (uint8_t)s;
 }
 
@@ -141,11 +143,14 @@ hipError_t launch_quant_weights(const float* w, int rows, int cols, int fmt, int
   return hipGetLastError();
 }
 
-hipError_t launch_quant_act_fp4(const uint16_t* x, int rows, int cols, uint8_t* codes,
-                                uint8_t* scales, hipStream_t stream) {
+hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int fmt, uint8_t* codes,
+                            uint8_t* scales, hipStream_t stream) {
   const size_t nblk = (size_t)rows * (cols / 32);
   const unsigned grid = (unsigned)((nblk + kThreads - 1) / kThreads);
-  hipLaunchKernelGGL(quant_act_fp4_kernel, dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, codes, scales);
+  if (fmt == MX_FMT_FP4)
+    hipLaunchKernelGGL(quant_act_kernel<FP4>, dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, codes, scales);
+  else
+    hipLaunchKernelGGL(quant_act_kernel<FP8>, dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, codes, scales);
   return hipGetLastError();
 }
 

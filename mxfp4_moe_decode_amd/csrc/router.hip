@@ -1,7 +1,7 @@
 // Router logits and top-k for any number of rows (used on its own and by the
 // grouped path).  A workgroup takes a group of rows, keeps them in LDS, computes
 // the E logits of each row with the fixed-order dot product of mx_device.h and
-// then one wavefront per row selects the top k.
+// then 16 lanes per row select the top k.
 #include "internal.h"
 #include "mx_device.h"
 
