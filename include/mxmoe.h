@@ -181,8 +181,15 @@ moe_status moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
  *   y         [T][H] bf16 output; may alias residual, must not alias x
  *   ws        moe_workspace_bytes(layer, T, 0) bytes, zero-filled before first use
  *   topk_ids_out [T][k], topk_w_out [T][k]: routing result, or NULL
+ * Arithmetic: every dot product is cut into NC K-chunks of 128-wide tiles (NC =
+ * 4, else 2, else 1: the largest that divides K/128); a chunk is one chain of
+ * scaled 16x16x128 matrix instructions from zero in tile order and the chunk
+ * sums are added in chunk order in fp32; SwiGLU, re-quantization and the
+ * combine order are those of the oracle.  fused_moe_mxfp4_grouped uses the same
+ * arithmetic, so both give identical bits for the same rows.
  * Output row t depends only on x[t] (and residual[t]): results are bit-identical
- * for any T and any row order.  The launch is a persistent grid sized to the
+ * for any T and any row order.  Shapes with (H/128)/NC > 8 give
+ * MOE_ERR_UNSUPPORTED (the grouped call handles them).  The launch is a persistent grid sized to the
  * device's co-resident capacity; its device-side waits are bounded, and a wait
  * that gives up marks the workspace (see moe_decode_status) instead of hanging.
  */
@@ -212,10 +219,13 @@ moe_status moe_decode_status(const void* ws, size_t ws_bytes);
 /*
  * Diagnostic (synchronizes the device): phase timestamps of the last fused
  * decode call on this workspace, in ticks of the device's 100 MHz constant
- * clock.  Workgroup g fills words [8g, 8g+8): launch start, phase 1 done
- * (x quantization, router, shared gate/up), routing known, phase 2 done
- * (routed gate/up), phase 3 done (down projections and combine), end of its
- * last phase-1 unit (0 if it had none), all logits seen, quantized x seen.
+ * clock.  Workgroup g fills words [16g, 16g+16): launch start, its x-quant /
+ * router / shared gate/up units done, all logits seen, routing known and x
+ * staged, its routed gate/up units done (0 if it had none), its down units and
+ * combines done, end of its first such unit (0 if it had none), logits in LDS,
+ * top-k done, expert list done, then for its first routed gate/up unit: matrix
+ * products done, results stored, next tiles in place, released; then its first
+ * down unit's intermediate staged (0 where it had no such unit).
  * Copies at most n_words words to host memory and returns
  * the number of workgroups of that call (0 if none ran yet), or a negative
  * moe_status.

@@ -301,11 +301,11 @@ def moe_decode_status(workspace):
 
 def moe_decode_trace(layer, workspace):
     """Per-workgroup phase timestamps (device clock ticks) of the last decode
-    call on ``workspace``: an int64 array [grid, 8] (see mxmoe.h)."""
+    call on ``workspace``: an int64 array [grid, 16] (see mxmoe.h)."""
     import numpy as np
-    buf = np.zeros(2048 * 8, dtype=np.uint64)
+    buf = np.zeros(2048 * 16, dtype=np.uint64)
     g = load().moe_decode_trace(layer.c, _ptr(workspace), workspace.numel(),
                                 buf.ctypes.data_as(ctypes.c_void_p), buf.size)
     if g < 0:
         raise MoeError("moe_decode_trace", g)
-    return buf[: g * 8].reshape(g, 8).astype(np.int64)
+    return buf[: g * 16].reshape(g, 16).astype(np.int64)

@@ -126,7 +126,7 @@ moe_status fused_moe_mxfp4_decode(const moe_layer_t* layer, const uint16_t* x, i
   const moe_status st = check_layer(layer);
   if (st != MOE_OK) return st;
   if (!x || !y || !ws || T <= 0) return MOE_ERR_INVALID_ARGUMENT;
-  if (T > kDecodeMaxT) return MOE_ERR_UNSUPPORTED;
+  if (T > kDecodeMaxT || !decode_supported(*layer)) return MOE_ERR_UNSUPPORTED;
   if (static_cast<const void*>(y) == static_cast<const void*>(x)) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(y, 4) || !aligned(residual, 4) || !aligned(ws, 256))
     return MOE_ERR_INVALID_ARGUMENT;

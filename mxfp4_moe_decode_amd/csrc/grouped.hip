@@ -311,7 +311,8 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(int T, int k, int H, 
   y[idx] = f32_to_bf16(c);
 }
 
-int pick_chunk(int tiles) { return tiles % 4 == 0 ? 4 : (tiles % 2 == 0 ? 2 : 1); }
+// Tiles per K-chunk: the dot product is cut into 4 (else 2, else 1) chunks.
+int pick_chunk(int tiles) { return tiles / (tiles % 4 == 0 ? 4 : (tiles % 2 == 0 ? 2 : 1)); }
 
 struct GCarve {
   size_t ids, w, sort_ws, sorted, bexp, eoff, npad, xq4, xs4, xq8, xs8, a4, as4, a8, as8, d_part, total;

@@ -43,8 +43,11 @@ hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int block_
 // ------------------------------------------------------------------ fused decode
 constexpr int kDecodeMaxT = 16;
 constexpr int kDecodeMaxGrid = 2048;
-constexpr int kTraceWords = 8;
+constexpr int kTraceWords = 16;
 size_t decode_ws_bytes(const moe_layer_t& L);
+// Shapes the fused decode kernel handles (a gate/up K-chunk fits its register
+// buffers, its LDS fits a workgroup).
+bool decode_supported(const moe_layer_t& L);
 hipError_t launch_decode(const moe_layer_t& L, const uint16_t* x, int T, const uint16_t* residual,
                          uint16_t* y, void* ws, int32_t* ids_out, float* w_out,
                          hipStream_t stream);

@@ -128,9 +128,17 @@ __device__ __forceinline__ v4f mfma_fp8(v4i a0, v4i a1, v4i b0, v4i b1, v4f c, u
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 0, 0, 0, (int)sa, 0, (int)sb);
 }
 
-// Streaming 16-byte load of weights (read once per call).
+// Streaming loads of weights read once per call (non-temporal: on gfx950 a
+// cold burst of these completes about twice as fast as plain loads).
 __device__ __forceinline__ v4i load_stream16(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+}
+__device__ __forceinline__ uint32_t load_stream4(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+__device__ __forceinline__ float4 load_stream_f4(const float* p) {
+  const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -229,6 +237,50 @@ __device__ __forceinline__ uint64_t row16_max64(uint64_t v) {
   v = max_u64(v, row_move64<0x141>(v));  // row_half_mirror
   v = max_u64(v, row_move64<0x140>(v));  // row_mirror
   return v;
+}
+
+// Maximum over the whole wavefront, returned uniform: row maxima, then
+// lane 15 of rows 0 and 2 folded into rows 1 and 3, then lane 31 into rows 2
+// and 3; lane 63 ends with the maximum.
+__device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
+  v = row16_max64(v);
+  {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v, 0x142, 0xA, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), 0x142, 0xA, 0xF, false);
+    v = max_u64(v, ((uint64_t)hi << 32) | lo);
+  }
+  {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v, 0x143, 0xC, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), 0x143, 0xC, 0xF, false);
+    v = max_u64(v, ((uint64_t)hi << 32) | lo);
+  }
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Top k of one row of E <= 256 logits on a whole wavefront (lane l holds the
+// keys of experts l, l+64, ...); same result and outputs as rows_topk16 (lane
+// 0 writes).  Every lane of the wavefront must call it; k is uniform.
+__device__ __forceinline__ void row_topk64(const float* logits_row, bool active, int E, int k, int lane,
+                                           int32_t* ids, float* w) {
+  uint64_t key[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int e = lane + 64 * r;
+    key[r] = (active && e < E) ? topk_key(logits_row[e], e) : 0ull;
+  }
+#pragma unroll 1
+  for (int j = 0; j < k; ++j) {
+    const uint64_t m = wave_max64(max_u64(max_u64(key[0], key[1]), max_u64(key[2], key[3])));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) key[r] = key[r] == m ? 0ull : key[r];
+    if (active && lane == 0) {
+      ids[j] = topk_key_expert(m);
+      w[j] = topk_key_logit(m);
+    }
+  }
+  if (active && lane == 0) topk_weights_inplace(w, k);
 }
 
 // Top k of one row of E <= 256 logits on the 16 lanes of a row: lane `sub`
