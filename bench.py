@@ -27,6 +27,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 matrix peak (published)
 
 
 def layer_bytes(H, I, E, Is, D, T, residual=False):
@@ -109,6 +110,15 @@ def time_decode(binding, synth, name, rotate, steps, warmup, pool=64):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     dur_ms = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)])
+    # the same launches back to back (queue kept full): one event pair around all
+    b0 = torch.cuda.Event(enable_timing=True)
+    b1 = torch.cuda.Event(enable_timing=True)
+    b0.record(stream)
+    for i in range(steps):
+        launch(warmup + steps + i)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    b2b_us = b0.elapsed_time(b1) * 1e3 / steps
     if binding.moe_decode_status(ws) != 0:
         raise RuntimeError("a device-side wait timed out during the benchmark")
     ids_np = ids.cpu().numpy()
@@ -123,8 +133,44 @@ def time_decode(binding, synth, name, rotate, steps, warmup, pool=64):
         "us_p10": float(np.percentile(us, 10)), "us_p90": float(np.percentile(us, 90)),
         "wall_ms_per_step": wall / steps * 1e3, "bytes_mean": float(nbytes.mean()),
         "gbs": float(nbytes.mean() / (us.mean() * 1e-6) / 1e9), "gbs_median": float(np.median(gbs)),
-        "distinct_experts_mean": float(D.mean()),
+        "distinct_experts_mean": float(D.mean()), "us_back_to_back": float(b2b_us),
     }
+
+
+def prefill_flops(T, H, I, E, k, Is):
+    """Algorithmic FLOPs of the 8192-row layer: routed gate/up + down (MXFP4),
+    shared gate/up + down (MXFP8), router (fp32)."""
+    routed = 2 * T * k * 3 * I * H
+    shared = 2 * T * 3 * Is * H
+    router = 2 * T * E * H
+    return routed, shared, router
+
+
+def time_grouped(binding, synth, steps=10, warmup=3):
+    """Whole-layer time of the grouped path on the 8192-row prefill workload."""
+    import torch
+    cfg, layers = build_layers(binding, synth, "prefill", 1)
+    L = layers[0]
+    x = torch.from_numpy(synth.activations(cfg).view(np.int16)).cuda().view(torch.bfloat16)
+    y = torch.empty_like(x)
+    ws = binding.grouped_workspace(L, cfg["T"])
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        binding.fused_moe_mxfp4_grouped(L, x, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        binding.fused_moe_mxfp4_grouped(L, x, out=y, workspace=ws)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+    routed, shared, router = prefill_flops(cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["k"], cfg["I_s"])
+    del layers, L, ws
+    torch.cuda.empty_cache()
+    return {"us_mean": float(us.mean()), "us_median": float(np.median(us)),
+            "tflops_all": (routed + shared + router) / (us.mean() * 1e-6) / 1e12,
+            "gflop_routed": routed / 1e9, "gflop_shared": shared / 1e9, "gflop_router": router / 1e9}
 
 
 def cpu_baseline(synth, seconds=15.0):
@@ -189,6 +235,7 @@ def main():
     ap.add_argument("--rotate", type=int, default=16, help="distinct layer instances cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-16", action="store_true", help="skip the 16-row measurement")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 8192-row grouped measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the measurement, run 5 plain elementwise copies (torch.neg, fp32) of this "
@@ -214,6 +261,11 @@ def main():
         r16 = time_decode(binding, synth, "decode16", max(4, args.rotate // 2), args.steps, args.warmup)
         print(f"[bench] 16 rows: {r16['us_mean']:.2f} us mean, {r16['gbs']:.0f} GB/s, "
               f"D={r16['distinct_experts_mean']:.1f}", file=sys.stderr, flush=True)
+    rp = None
+    if not args.no_prefill:
+        rp = time_grouped(binding, synth)
+        print(f"[bench] prefill 8192 rows (grouped path): {rp['us_mean']:.1f} us per layer, "
+              f"{rp['tflops_all']:.1f} TFLOP/s over all layer FLOPs", file=sys.stderr, flush=True)
     if args.copy_mib:
         src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -246,6 +298,7 @@ def main():
         "us_median": round(r1["us_median"], 3),
         "us_p10": round(r1["us_p10"], 3),
         "us_p90": round(r1["us_p90"], 3),
+        "us_back_to_back": round(r1["us_back_to_back"], 3),
         "roofline": {"bound": "hbm", "achieved": round(r1["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(r1["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": int(r1["bytes_mean"])},
@@ -254,8 +307,19 @@ def main():
         out["rows16"] = {"us_mean": round(r16["us_mean"], 3), "us_median": round(r16["us_median"], 3),
                          "gbs": round(r16["gbs"], 1), "frac": round(r16["gbs"] / HBM_PEAK_GBS, 4),
                          "distinct_experts_mean": round(r16["distinct_experts_mean"], 2),
+                         "us_back_to_back": round(r16["us_back_to_back"], 3),
                          "algorithmic_bytes_per_launch": int(r16["bytes_mean"]),
                          "ms_per_step": round(r16["wall_ms_per_step"], 5)}
+    if rp:
+        out["prefill8192"] = {
+            "workload": "8192 bf16 rows through the same layer on the grouped path (router, sort, MX quant, "
+                        "grouped FP4 GEMMs, MXFP8 shared expert, combine)",
+            "us_mean": round(rp["us_mean"], 2), "us_median": round(rp["us_median"], 2),
+            "gflop": {"routed_fp4": round(rp["gflop_routed"], 1), "shared_fp8": round(rp["gflop_shared"], 1),
+                      "router_fp32": round(rp["gflop_router"], 2)},
+            "tflops_all_flops": round(rp["tflops_all"], 1),
+            "fp4_peak_tflops": FP4_PEAK_TFLOPS,
+            "frac_of_fp4_peak_whole_layer": round(rp["tflops_all"] / FP4_PEAK_TFLOPS, 4)}
     out["cpu_baseline"] = cpu
     print(json.dumps(out))
 
