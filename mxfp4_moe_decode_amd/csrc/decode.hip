@@ -23,9 +23,10 @@
 //            group combines it.
 //
 // Phases B and C give each workgroup a contiguous run of units and are one
-// software pipeline: the weight tiles of the unit after next are requested
-// before the current unit's results are released, and a release waits only
-// for memory operations issued before those requests.  A unit only waits for
+// software pipeline over two register buffers: while a unit computes from one,
+// the next unit's tiles land in the other; after its stores a unit requests
+// the tiles of the unit after next into its own buffer, and its release waits
+// only for memory operations issued before that request.  A unit only waits for
 // units of an earlier phase, so with every workgroup resident the smallest
 // unfinished unit can always progress.
 //
@@ -57,8 +58,8 @@ constexpr uint64_t kSpinTicks = 100000000ull;  // ~1 s of the 100 MHz constant c
 constexpr int kLine = 64;  // words
 __device__ __forceinline__ uint32_t* ctr(uint32_t* base, int i) { return base + (size_t)i * kLine; }
 // Lines of the sync block: status, done, x-quant, shared-intermediate ready,
-// grid size of the last call, router.
-enum { S_STATUS = 0, S_DONE = 1, S_XQ = 2, S_SA = 3, S_GRID = 4, S_ROUTER = 5, kSyncLines = 6 };
+// grid size of the last call, call epoch.
+enum { S_STATUS = 0, S_DONE = 1, S_XQ = 2, S_SA = 3, S_GRID = 4, S_EPOCH = 5, kSyncLines = 6 };
 
 // Timestamps each workgroup records (100 MHz device clock).
 enum {
@@ -80,10 +81,11 @@ struct DecodeArgs {
   uint16_t* y;
   int32_t* ids_out;
   float* w_out;
-  uint32_t *sync, *a_ready, *comb;
-  float* logits;
+  uint32_t *sync, *comb;
+  uint64_t* logits;  // tagged [T][E]
   uint8_t *xq4, *xs4, *xq8, *xs8;
-  float *a_r, *a_s, *d_part, *s_part;
+  uint64_t* a_r;  // tagged [T*k][I]
+  float *a_s, *d_part, *s_part;
   uint64_t* trace;
 };
 
@@ -140,6 +142,14 @@ struct Smem {
 // issued after the stores are outstanding), then the workgroup barrier, then
 // one atomic add.  A consumer polls the counter and issues its data loads
 // only after the poll has returned.
+//
+// Where many producers feed one consumer set (128 router units, 64 gate/up
+// strips per expert), a shared counter would serialize the atomics at the
+// memory side; there the data carries the call's tag instead: each value is
+// stored as one 64-bit word (tag << 32 | fp32 bits), single-copy atomic, and a
+// consumer reads the words until every tag is this call's.  The tag is one
+// more than the epoch word, which the last workgroup of a call advances, so
+// words of an earlier call (or the zero-filled workspace) never match.
 template <class T>
 __device__ __forceinline__ T ld_dev(const T* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -230,6 +240,24 @@ __device__ __forceinline__ bool wg_arrive(uint32_t* c, int after, bool last, uin
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return (g / (1.f + expf(-g))) * u; }
 
+__device__ __forceinline__ uint64_t tagged(uint32_t tag, float v) {
+  return ((uint64_t)tag << 32) | __float_as_uint(v);
+}
+__device__ __forceinline__ bool tag_ok(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
+
+// Workgroup-uniform bounded retry: true to go on polling.  Gives up (marking
+// the status word) after the spin bound or once another wait has given up.
+__device__ __forceinline__ bool keep_polling(bool all_ok, uint64_t t0, uint32_t* status) {
+  if (__syncthreads_and(all_ok)) return false;
+  const bool late = wall_clock64() - t0 > kSpinTicks || ld_dev(status) != 0;
+  if (__syncthreads_or(late)) {
+    if (threadIdx.x == 0) __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return false;
+  }
+  __builtin_amdgcn_s_sleep(1);
+  return true;
+}
+
 __device__ __forceinline__ uint32_t scale_byte(uint32_t word, int tile) { return (word >> (8 * (tile & 3))) & 0xffu; }
 
 // w[i] for a run-time i in 0..2, without indexing a register array.
@@ -312,7 +340,7 @@ __device__ __forceinline__ void unit_xq(const DA& A, int u) {
 // of the expert's weights is loaded once, then the rows go through it two at
 // a time.
 template <class DA>
-__device__ __forceinline__ void unit_router(const DA& A, int e, int lane, int wave) {
+__device__ __forceinline__ void unit_router(const DA& A, uint32_t tag, int e, int lane, int wave) {
   const float* wrow = A.router_w + (size_t)e * A.h();
   const int H = A.h();
   float p[4] = {0.f, 0.f, 0.f, 0.f};
@@ -357,13 +385,8 @@ __device__ __forceinline__ void unit_router(const DA& A, int e, int lane, int wa
     if (r < nr) {
       float v = wave_sum_butterfly(p[r]);
       if (A.router_bias) v = v + b;
-      if (lane == 0) st_dev(&A.logits[(wave + kWaves * r) * A.e() + e], v);
+      if (lane == 0) st_dev(&A.logits[(wave + kWaves * r) * A.e() + e], tagged(tag, v));
     }
-  compiler_fence();
-  wait_vm<0>();
-  __syncthreads();
-  if (threadIdx.x == 0)
-    __hip_atomic_fetch_add(ctr(A.sync, S_ROUTER), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Chunk sums of a gate/up unit in sm.red, added in chunk order, then SwiGLU:
@@ -598,11 +621,35 @@ __device__ __forceinline__ void gu_compute(const DA& A, Smem& sm, const uint8_t*
   }
 }
 
+// Four consecutive fp32 values, plain or tagged (the value is the low word).
+__device__ __forceinline__ float4 load4(const float* p) { return ld_dev_f4(p); }
+__device__ __forceinline__ float4 load4(const uint64_t* p) {
+  return make_float4(__uint_as_float((uint32_t)ld_dev(p)), __uint_as_float((uint32_t)ld_dev(p + 1)),
+                     __uint_as_float((uint32_t)ld_dev(p + 2)), __uint_as_float((uint32_t)ld_dev(p + 3)));
+}
+
+// Waits until rows slots[0..n) of a tagged [*, K] array all carry this call's
+// tag (only the tag halves are read).
+template <class DA>
+__device__ __forceinline__ void wait_tagged_rows(const DA& A, uint32_t tag, const uint64_t* src, int K, int n,
+                                                 const uint8_t* slots) {
+  const uint64_t t0 = wall_clock64();
+  const uint32_t* hi = reinterpret_cast<const uint32_t*>(src) + 1;
+  bool ok;
+  do {
+    ok = true;
+    for (int idx = threadIdx.x; idx < n * K; idx += kThreads) {
+      const int m = idx / K, c = idx % K;
+      ok &= ld_dev(&hi[2 * ((size_t)slots[m] * K + c)]) == tag;
+    }
+  } while (keep_polling(ok, t0, A.sync));
+}
+
 // Re-quantizes the fp32 intermediate rows of one down unit into LDS (row m of
 // the staged block = routed slot tl[dd][m], or shared row m): codes [n, K/2]
 // (FP4) or [n, K] (FP8), scales [n, K/32].
-template <class F>
-__device__ __forceinline__ void stage_intermediate(const float* src, int K, int n, const uint8_t* slots,
+template <class F, class Src>
+__device__ __forceinline__ void stage_intermediate(const Src* src, int K, int n, const uint8_t* slots,
                                                    uint8_t* codes, uint8_t* scales) {
   const int nb = K / 32, tasks = n * nb;
   const int j = threadIdx.x & 7;
@@ -615,7 +662,7 @@ __device__ __forceinline__ void stage_intermediate(const float* src, int K, int 
       if (task < tasks) {
         const int m = task / nb, b = task % nb;
         const int row = slots ? slots[m] : m;
-        v[p] = ld_dev_f4(src + (size_t)row * K + 32 * b + 4 * j);
+        v[p] = load4(src + (size_t)row * K + 32 * b + 4 * j);
       }
     }
 #pragma unroll
@@ -711,11 +758,10 @@ __device__ __forceinline__ void combine(const DA& A, const Smem& sm, int hg) {
   }
 }
 
-// One sequence entry: compute from buf, store, move the next entry's tiles
-// (requested one entry earlier) from nxt to buf, request entry j + 2 into nxt,
-// release.
+// One sequence entry: compute from buf, store, request entry j + 2 into buf,
+// release (waiting only for what was issued before that request).
 template <class DA>
-__device__ __forceinline__ void run_entry(const DA& A, Smem& sm, const Seq& S, int j, Buf& buf, Buf& nxt,
+__device__ __forceinline__ void run_entry(const DA& A, uint32_t tag, Smem& sm, const Seq& S, int j, Buf& buf,
                                           uint8_t* xq4_lds, uint8_t* xs4_lds, uint8_t* stage, int lane, int wave) {
   if (j < S.nb) {
     const int u = S.b0 + j, per = A.i() / 16;
@@ -726,14 +772,12 @@ __device__ __forceinline__ void run_entry(const DA& A, Smem& sm, const Seq& S, i
     int row, col;
     float a;
     if (gu_finish(sm, A.nc1(), sm.ecount[dd], &row, &col, &a))
-      st_dev(&A.a_r[(size_t)sm.tl[dd][row] * A.i() + 16 * i + col], a);
+      st_dev(&A.a_r[(size_t)sm.tl[dd][row] * A.i() + 16 * i + col], tagged(tag, a));
     compiler_fence();
     if (j == 0) trace_at(A, TR_B_STORED);
-    buf = nxt;
+    issue(A, sm, S, j + 2, lane, wave, buf);
     if (j == 0) trace_at(A, TR_B_NEXT);
-    const int after = issue_count(A, S, j + 2, wave);
-    issue(A, sm, S, j + 2, lane, wave, nxt);
-    wg_arrive(ctr(A.a_ready, sm.elist[dd]), after, false, 0, sm);
+    __syncthreads();  // sm.red is rewritten by the next unit
     if (j == 0) trace_at(A, TR_B_RELEASED);
     return;
   }
@@ -750,7 +794,7 @@ __device__ __forceinline__ void run_entry(const DA& A, Smem& sm, const Seq& S, i
     uint8_t* codes = stage;
     uint8_t* scales = stage + kDecodeMaxT * (K / 2);
     if (sm.staged != e) {
-      wg_wait(ctr(A.a_ready, e), (uint32_t)(A.i() / 16), A.sync);
+      wait_tagged_rows(A, tag, A.a_r, K, n, sm.tl[dd]);
       stage_intermediate<FP4>(A.a_r, K, n, sm.tl[dd], codes, scales);
       __syncthreads();
       if (threadIdx.x == 0) sm.staged = e;
@@ -769,7 +813,7 @@ __device__ __forceinline__ void run_entry(const DA& A, Smem& sm, const Seq& S, i
     uint8_t* scales = stage + kDecodeMaxT * K;
     if (sm.staged != -1) {
       wg_wait(ctr(A.sync, S_SA), (uint32_t)(A.is() / 16), A.sync);
-      stage_intermediate<FP8>(A.a_s, K, A.T, nullptr, codes, scales);
+      stage_intermediate<FP8>(A.a_s, K, A.T, static_cast<const uint8_t*>(nullptr), codes, scales);
       __syncthreads();
       if (threadIdx.x == 0) sm.staged = -1;
     }
@@ -782,9 +826,8 @@ __device__ __forceinline__ void run_entry(const DA& A, Smem& sm, const Seq& S, i
       if (4 * q + r < A.T) st_dev(&A.s_part[(size_t)(4 * q + r) * A.h() + 16 * hs + m], out[r]);
   }
   compiler_fence();
-  buf = nxt;
   const int after = issue_count(A, S, j + 2, wave);
-  issue(A, sm, S, j + 2, lane, wave, nxt);
+  issue(A, sm, S, j + 2, lane, wave, buf);
   uint32_t* c = ctr(A.comb, hg);
   const uint32_t target = (uint32_t)(S.D + (A.is() ? 1 : 0));
   if (wg_arrive(c, after, true, target, sm)) {
@@ -800,6 +843,7 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
   extern __shared__ __align__(16) unsigned char dyn[];  // logits, then MXFP4 x; staged intermediates
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int G = A.G, T = A.T, E = A.e();
+  const uint32_t tag = ld_dev(ctr(A.sync, S_EPOCH)) + 1u;
   uint64_t* tr = A.trace + (size_t)blockIdx.x * kTraceWords;
   if (threadIdx.x == 0) {
     tr[TR_START] = wall_clock64();
@@ -813,23 +857,30 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
     if (u < n_xq)
       unit_xq(A, u);
     else if (u < n_xq + E)
-      unit_router(A, u - n_xq, lane, wave);
+      unit_router(A, tag, u - n_xq, lane, wave);
     else
       unit_shared_gu(A, sm, u - n_xq - E, lane, wave);
     if (threadIdx.x == 0 && u == (int)blockIdx.x) tr[TR_FIRST] = wall_clock64();
   }
-  if (threadIdx.x == 0) {
-    tr[TR_A] = wall_clock64();
-    wait_count(ctr(A.sync, S_ROUTER), (uint32_t)E, A.sync);
-    tr[TR_LOGITS] = wall_clock64();
-  }
-  __syncthreads();
+  trace_at(A, TR_A);
   compiler_fence();
 
-  // routing, identical in every workgroup
+  // routing, identical in every workgroup: read the tagged logits until all
+  // are this call's
   float* logits_lds = reinterpret_cast<float*>(dyn);
-  for (int i = threadIdx.x; i < T * E; i += kThreads) logits_lds[i] = ld_dev(&A.logits[i]);
-  __syncthreads();
+  {
+    const uint64_t t0 = wall_clock64();
+    bool ok;
+    do {
+      ok = true;
+      for (int i = threadIdx.x; i < T * E; i += kThreads) {
+        const uint64_t w = ld_dev(&A.logits[i]);
+        ok &= tag_ok(w, tag);
+        logits_lds[i] = __uint_as_float((uint32_t)w);
+      }
+    } while (keep_polling(ok, t0, A.sync));
+  }
+  trace_at(A, TR_LOGITS);
   trace_at(A, TR_LOGITS_LDS);
   if (T <= kWaves) {  // a wavefront per row
     const int row = wave < T ? wave : 0;
@@ -884,9 +935,13 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
   Buf X, Y;
   issue(A, sm, S, 0, lane, wave, X);
   issue(A, sm, S, 1, lane, wave, Y);
-  for (int j = 0; j < total; ++j) {
-    run_entry(A, sm, S, j, X, Y, xq4_lds, xs4_lds, stage, lane, wave);
+  for (int j = 0; j < total; j += 2) {  // entries alternate between the two buffers
+    run_entry(A, tag, sm, S, j, X, xq4_lds, xs4_lds, stage, lane, wave);
     if (j == S.nb - 1 && threadIdx.x == 0) tr[TR_B] = wall_clock64();
+    if (j + 1 < total) {
+      run_entry(A, tag, sm, S, j + 1, Y, xq4_lds, xs4_lds, stage, lane, wave);
+      if (j + 1 == S.nb - 1 && threadIdx.x == 0) tr[TR_B] = wall_clock64();
+    }
   }
 
   // exit: the last workgroup resets the launch-wide counters
@@ -899,10 +954,9 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
     const uint32_t old = __hip_atomic_fetch_add(ctr(A.sync, S_DONE), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     compiler_fence();
     if (old + 1 == (uint32_t)G) {
-      st_dev(ctr(A.sync, S_ROUTER), 0u);
+      st_dev(ctr(A.sync, S_EPOCH), tag);  // the next call's tag is one more
       st_dev(ctr(A.sync, S_XQ), 0u);
       st_dev(ctr(A.sync, S_SA), 0u);
-      for (int e = 0; e < E; ++e) st_dev(ctr(A.a_ready, e), 0u);
       compiler_fence();
       wait_vm<0>();
       st_dev(ctr(A.sync, S_DONE), 0u);
@@ -912,7 +966,7 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
 
 // ------------------------------------------------------------------ host side
 struct Carve {
-  size_t sync, a_ready, comb, sync_end;
+  size_t sync, comb, sync_end;
   size_t logits, xq4, xs4, xq8, xs8, a_r, a_s, d_part, s_part, trace, total;
 };
 
@@ -924,15 +978,14 @@ Carve carve(const moe_layer_t& L) {
   auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, 256); return at; };
   const size_t line = kLine * 4;
   c.sync = take(kSyncLines * line);
-  c.a_ready = take(E * line);
   c.comb = take((H / 64) * line);
   c.sync_end = o;
-  c.logits = take(T * E * 4);
+  c.logits = take(T * E * 8);
   c.xq4 = take(T * H / 2);
   c.xs4 = take(T * H / 32);
   c.xq8 = take(T * H);
   c.xs8 = take(T * H / 32);
-  c.a_r = take(T * k * I * 4);
+  c.a_r = take(T * k * I * 8);
   c.a_s = take(T * Is * 4 + 16);
   c.d_part = take(T * k * H * 4);
   c.s_part = take(T * H * 4);
@@ -1039,14 +1092,13 @@ hipError_t launch_decode(const moe_layer_t& L, const uint16_t* x, int T, const u
   A.ids_out = ids_out;
   A.w_out = w_out;
   A.sync = reinterpret_cast<uint32_t*>(base + c.sync);
-  A.a_ready = reinterpret_cast<uint32_t*>(base + c.a_ready);
   A.comb = reinterpret_cast<uint32_t*>(base + c.comb);
-  A.logits = reinterpret_cast<float*>(base + c.logits);
+  A.logits = reinterpret_cast<uint64_t*>(base + c.logits);
   A.xq4 = reinterpret_cast<uint8_t*>(base + c.xq4);
   A.xs4 = reinterpret_cast<uint8_t*>(base + c.xs4);
   A.xq8 = reinterpret_cast<uint8_t*>(base + c.xq8);
   A.xs8 = reinterpret_cast<uint8_t*>(base + c.xs8);
-  A.a_r = reinterpret_cast<float*>(base + c.a_r);
+  A.a_r = reinterpret_cast<uint64_t*>(base + c.a_r);
   A.a_s = reinterpret_cast<float*>(base + c.a_s);
   A.d_part = reinterpret_cast<float*>(base + c.d_part);
   A.s_part = reinterpret_cast<float*>(base + c.s_part);
