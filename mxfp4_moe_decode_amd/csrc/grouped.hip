@@ -38,7 +38,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBM = 128;  // rows of a routed block (the align-sort block size)
-constexpr int kNF = 4;    // column strips per wavefront
 
 enum Mode { GU_ROUTED = 0, GU_SHARED = 1, DOWN_ROUTED = 2, DOWN_SHARED = 3 };
 
@@ -64,12 +63,26 @@ struct GemmArgs {
   uint16_t* y;              // shared down: output [T, H]
 };
 
-template <class F>
-struct Frag {
-  static constexpr int R = F::MB == 1 ? 1 : 2;    // 16-byte register quads per operand row
-  static constexpr int MF = F::MB == 1 ? 4 : 2;   // row fragments per wavefront
-  static constexpr int BM = 2 * 16 * MF;          // rows per workgroup
-  static constexpr int TB = 1024 * R;             // bytes of one weight tile
+// Workgroup tile geometry per format.  A 16x128 operand tile is one 1 KiB
+// block (FP4) or two (FP8, R = 2 halves); lane l's 16 bytes of a block are the
+// bytes that lane feeds the matrix instruction.
+// Wavefronts form a 2 x WN grid; each holds MF row fragments of 16 and four
+// column strips of 16.
+template <class F, int WN>
+struct Geo {
+  static constexpr int R = F::MB == 1 ? 1 : 2;
+  static constexpr int MF = F::MB == 1 ? 4 : 2;  // row fragments per wavefront
+  static constexpr int WAVES = 2 * WN;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BM = 2 * 16 * MF;         // rows per workgroup
+  static constexpr int STRIPS = 4 * WN;          // 16-column weight strips per workgroup
+  static constexpr int A_TILES = (BM / 16) * R;  // 1 KiB blocks of A per K-tile
+  static constexpr int B_TILES = STRIPS * R;     // 1 KiB blocks of B per K-tile
+  static constexpr int TILES = A_TILES + B_TILES;
+  static constexpr int TPW = TILES / WAVES;      // blocks each wavefront moves per K-tile
+  static constexpr int NS = F::MB == 1 ? 5 : 3;  // K-tiles in the LDS ring
+  static constexpr int STAGE = TILES * 1024;
+  static_assert(TILES % WAVES == 0, "blocks split evenly over the wavefronts");
 };
 
 __device__ __forceinline__ uint32_t row_move32(uint32_t v) {  // neighbour swap inside a quad
@@ -85,76 +98,79 @@ __device__ __forceinline__ uint32_t row16_max32(uint32_t v) {
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return (g / (1.f + expf(-g))) * u; }
 
-template <class F>
-struct Stage {
-  v4i a[Frag<F>::MF][Frag<F>::R];
-  v4i b[kNF][Frag<F>::R];
-  uint32_t sa[Frag<F>::MF];
-  uint32_t sw[kNF];
-};
-
-template <class F>
-__device__ __forceinline__ void load_stage(const GemmArgs& g, int kt, const int (&arow)[Frag<F>::MF],
-                                           const uint8_t* const (&bp)[kNF], const uint8_t* const (&sp)[kNF],
-                                           int q, Stage<F>& s) {
-  constexpr int MF = Frag<F>::MF, R = Frag<F>::R, TB = Frag<F>::TB;
-#pragma unroll
-  for (int i = 0; i < MF; ++i) {
-    if (arow[i] >= 0) {
-      const uint8_t* ap = g.a + (size_t)arow[i] * g.a_stride + (size_t)kt * 64 * R + 16 * q;
-#pragma unroll
-      for (int r = 0; r < R; ++r) s.a[i][r] = *reinterpret_cast<const v4i*>(ap + 64 * r);
-      const uint32_t w4 = *reinterpret_cast<const uint32_t*>(g.as + (size_t)arow[i] * g.as_stride + 4 * kt);
-      s.sa[i] = (w4 >> (8 * q)) & 0xffu;
-    } else {
-#pragma unroll
-      for (int r = 0; r < R; ++r) s.a[i][r] = v4i{0, 0, 0, 0};
-      s.sa[i] = 127u;
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < kNF; ++j) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) s.b[j][r] = *reinterpret_cast<const v4i*>(bp[j] + (size_t)kt * TB + 1024 * r);
-    s.sw[j] = *reinterpret_cast<const uint32_t*>(sp[j] + (size_t)(kt >> 2) * 256);
-  }
+// s_waitcnt vmcnt(N), other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <class F>
-__device__ __forceinline__ void mma_stage(const Stage<F>& s, int kt, v4f (&acc)[Frag<F>::MF][kNF]) {
-  constexpr int MF = Frag<F>::MF;
+// One K-tile of matrix instructions; the first tile of a chunk starts its
+// chain from zero.
+template <class F, int MF, int R>
+__device__ __forceinline__ void mma_tile(const v4i (&a)[MF][R], const v4i (&b)[4][R], const uint32_t (&sa)[MF],
+                                         const uint32_t (&sb)[4], bool first, v4f (&acc)[MF][4]) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < MF; ++i)
 #pragma unroll
-    for (int j = 0; j < kNF; ++j) {
-      const uint32_t sb = (s.sw[j] >> (8 * (kt & 3))) & 0xffu;
-      if constexpr (F::MB == 1)
-        acc[i][j] = mfma_fp4(s.a[i][0], s.b[j][0], acc[i][j], s.sa[i], sb);
-      else
-        acc[i][j] = mfma_fp8(s.a[i][0], s.a[i][1], s.b[j][0], s.b[j][1], acc[i][j], s.sa[i], sb);
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (F::MB == 1) {
+        acc[i][j] = first ? mfma_fp4(a[i][0], b[j][0], zero, sa[i], sb[j])
+                          : mfma_fp4(a[i][0], b[j][0], acc[i][j], sa[i], sb[j]);
+      } else {
+        acc[i][j] = first ? mfma_fp8(a[i][0], a[i][R - 1], b[j][0], b[j][R - 1], zero, sa[i], sb[j])
+                          : mfma_fp8(a[i][0], a[i][R - 1], b[j][0], b[j][R - 1], acc[i][j], sa[i], sb[j]);
+      }
     }
 }
 
-template <class F>
-__device__ __forceinline__ void end_chunk(int kt, int CT, v4f (&acc)[Frag<F>::MF][kNF],
-                                          v4f (&sum)[Frag<F>::MF][kNF]) {
-  if ((kt + 1) % CT) return;
-#pragma unroll
-  for (int i = 0; i < Frag<F>::MF; ++i)
-#pragma unroll
-    for (int j = 0; j < kNF; ++j) {
-      sum[i][j] = kt + 1 == CT ? acc[i][j] : sum[i][j] + acc[i][j];
-      acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-    }
+// Operand row of the workgroup's row rl: padding rows read the block's first
+// row (a real one) and their results are discarded.
+template <int MODE, int BM>
+__device__ __forceinline__ int a_row(const GemmArgs& g, const int32_t* slots, int S, int mb, int rl) {
+  const int rr = slots[rl] < S ? rl : 0;
+  if constexpr (MODE == GU_ROUTED) return slots[rr] / g.k;
+  return mb * BM + rr;
 }
 
-template <class F, int MODE>
-__global__ void __launch_bounds__(kThreads) grouped_gemm_kernel(GemmArgs g) {
-  using Fr = Frag<F>;
-  constexpr int MF = Fr::MF, BM = Fr::BM, TB = Fr::TB;
+// Weight strip of the workgroup's strip s (0..4 WN - 1): gate/up tiles take the
+// two gate strips and the two matching up strips of each of their WN 32-column
+// intermediate blocks; down tiles take 4 WN consecutive strips.
+template <int MODE, int WN>
+__device__ __forceinline__ int w_strip(const GemmArgs& g, int nt, int s) {
+  if constexpr (MODE == GU_ROUTED || MODE == GU_SHARED) {
+    const int nb = WN * nt + (s >> 2), jj = s & 3;
+    return (jj < 2 ? 0 : g.inter / 16) + 2 * nb + (jj & 1);
+  }
+  return 4 * WN * nt + s;
+}
+
+// Direct global -> LDS loads of this wavefront's blocks of K-tile kt into its
+// ring slot (block t = wave + WAVES i, 1 KiB each, lane l's 16 bytes at l*16).
+template <int TPW, int NS, int STAGE, int WAVES>
+__device__ __forceinline__ void issue_blocks(const uint8_t* (&src)[TPW], const int (&step)[TPW],
+                                             unsigned char* ring, int wave, int kt) {
+  unsigned char* st = ring + (kt % NS) * STAGE;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the builtin only type-checks in the device pass
+    __builtin_amdgcn_global_load_lds(src[i] + (size_t)kt * step[i], st + (wave + WAVES * i) * 1024, 16, 0, 0);
+#endif
+  }
+}
+
+// Main loop.  The operands of K-tile kt travel global -> LDS with direct
+// (LDS-destination) 16-byte loads into slot kt % NS of a ring, NS - 1 K-tiles
+// ahead of the matrix instructions; each wavefront moves TPW of the tile's
+// 1 KiB blocks.  Block scales of the whole K range sit in LDS from the start.
+template <class F, int MODE, int WN>
+__global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  // 2 x WN wavefronts
+  using Gm = Geo<F, WN>;
+  constexpr int MF = Gm::MF, BM = Gm::BM, R = Gm::R, TPW = Gm::TPW, NS = Gm::NS;
+  constexpr int WAVES = Gm::WAVES, THREADS = Gm::THREADS, STRIPS = Gm::STRIPS;
   constexpr bool kRouted = MODE == GU_ROUTED || MODE == DOWN_ROUTED;
   constexpr bool kGateUp = MODE == GU_ROUTED || MODE == GU_SHARED;
-  __shared__ int32_t slots[BM];
+  extern __shared__ __align__(16) unsigned char smem[];
 
   // XCD-aware order: consecutive workgroup ids go to different XCDs, so XCD x
   // is given the contiguous run of tiles x*G/8 .. (x+1)*G/8 (G % 8 == 0).
@@ -167,65 +183,103 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_kernel(GemmArgs g) {
     if (mb * BM >= *g.num_padded) return;
     e = g.block_expert[mb];
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / WN, wn = wave % WN;
   const int m = lane & 15, q = lane >> 4;
   const int S = g.T * g.k;
+  const int KT = g.KT, KG = g.KG, KS = KT * 4;  // KS: scale bytes per row
+
+  unsigned char* ring = smem;
+  unsigned char* as_lds = smem + NS * Gm::STAGE;                  // [BM][KS] bytes
+  uint32_t* bs_lds = reinterpret_cast<uint32_t*>(as_lds + BM * KS);  // [STRIPS][KG][64] words
+  int32_t* slots = reinterpret_cast<int32_t*>(bs_lds + STRIPS * KG * 64);
+
   if (threadIdx.x < BM) {
     const int r = mb * BM + (int)threadIdx.x;
     slots[threadIdx.x] = kRouted ? g.sorted_slots[r] : (r < g.T ? r : S);
   }
   __syncthreads();
 
-  // A rows of this lane's fragments (-1: padding, multiplied as zeros)
-  int arow[MF];
-#pragma unroll
-  for (int i = 0; i < MF; ++i) {
-    const int rl = wm * 16 * MF + 16 * i + m;
-    const int slot = slots[rl];
-    if constexpr (MODE == GU_ROUTED)
-      arow[i] = slot < S ? slot / g.k : -1;
-    else if constexpr (MODE == DOWN_ROUTED)
-      arow[i] = slot < S ? mb * BM + rl : -1;
-    else
-      arow[i] = slot < S ? mb * BM + rl : -1;  // shared: slot == row for real rows
+  // scales of the whole K range into LDS
+  for (int idx = threadIdx.x; idx < BM * (KS / 4); idx += THREADS) {
+    const int rl = idx / (KS / 4), c = idx % (KS / 4);
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(g.as + (size_t)a_row<MODE, BM>(g, slots, S, mb, rl) * g.as_stride + 4 * c);
+    *reinterpret_cast<uint32_t*>(as_lds + rl * KS + 4 * c) = v;
   }
-  // weight strips of this wavefront
-  int strip[kNF];
-  if constexpr (kGateUp) {
-    const int nb = 2 * nt + wn;
-    strip[0] = 2 * nb;
-    strip[1] = 2 * nb + 1;
-    strip[2] = g.inter / 16 + 2 * nb;
-    strip[3] = g.inter / 16 + 2 * nb + 1;
-  } else {
-#pragma unroll
-    for (int j = 0; j < kNF; ++j) strip[j] = 8 * nt + 4 * wn + j;
-  }
-  const uint8_t* bp[kNF];
-  const uint8_t* sp[kNF];
-#pragma unroll
-  for (int j = 0; j < kNF; ++j) {
-    bp[j] = g.b + (size_t)e * g.b_estride + (size_t)strip[j] * g.KT * TB + lane * 16;
-    sp[j] = g.bs + (size_t)e * g.bs_estride + ((size_t)strip[j] * g.KG * 64 + lane) * 4;
+  const uint8_t* bsb = g.bs + (size_t)e * g.bs_estride;
+  for (int idx = threadIdx.x; idx < STRIPS * KG * 64; idx += THREADS) {
+    const int sidx = idx / (KG * 64), rem = idx % (KG * 64);
+    bs_lds[idx] = *reinterpret_cast<const uint32_t*>(bsb + ((size_t)w_strip<MODE, WN>(g, nt, sidx) * KG * 64 + rem) * 4);
   }
 
-  v4f acc[MF][kNF], sum[MF][kNF];
+  // the blocks this wavefront moves: block t = wave + WAVES i of every K-tile
+  const uint8_t* src[TPW];
+  int step[TPW];
+  const uint8_t* bb = g.b + (size_t)e * g.b_estride;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int t = wave + WAVES * i;
+    if (t < Gm::A_TILES) {
+      const int f = t / R, r = t % R;
+      src[i] = g.a + (size_t)a_row<MODE, BM>(g, slots, S, mb, 16 * f + m) * g.a_stride + 64 * r + 16 * q;
+      step[i] = 64 * R;
+    } else {
+      const int sb = (t - Gm::A_TILES) / R, r = (t - Gm::A_TILES) % R;
+      src[i] = bb + (size_t)w_strip<MODE, WN>(g, nt, sb) * KT * 1024 * R + 1024 * r + lane * 16;
+      step[i] = 1024 * R;
+    }
+  }
+
+  // chunk sums: -0 + x == x bit for bit (signed zeros included), so starting
+  // from -0 and always adding equals taking the first chunk's sum as it is
+  v4f acc[MF][4], sum[MF][4];
 #pragma unroll
   for (int i = 0; i < MF; ++i)
 #pragma unroll
-    for (int j = 0; j < kNF; ++j) acc[i][j] = sum[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = sum[i][j] = v4f{-0.f, -0.f, -0.f, -0.f};
 
-  Stage<F> s0, s1;
-  const int KT = g.KT, CT = g.CT;
-  load_stage<F>(g, 0, arow, bp, sp, q, s0);
-  for (int kt = 0; kt < KT; kt += 2) {
-    if (kt + 1 < KT) load_stage<F>(g, kt + 1, arow, bp, sp, q, s1);
-    mma_stage<F>(s0, kt, acc);
-    end_chunk<F>(kt, CT, acc, sum);
-    if (kt + 1 < KT) {
-      if (kt + 2 < KT) load_stage<F>(g, kt + 2, arow, bp, sp, q, s0);
-      mma_stage<F>(s1, kt + 1, acc);
-      end_chunk<F>(kt + 1, CT, acc, sum);
+#pragma unroll
+  for (int s0 = 0; s0 < NS - 1; ++s0)
+    if (s0 < KT) issue_blocks<TPW, NS, Gm::STAGE, WAVES>(src, step, ring, wave, s0);
+  for (int kt = 0, t_in = 0; kt < KT; ++kt) {
+    // K-tile kt has landed once only the K-tiles issued after it are pending
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const int ahead = min(NS - 2, KT - 1 - kt);  // K-tiles issued after kt
+    switch (ahead) {
+      case 0: wait_vm<0>(); break;
+      case 1: wait_vm<TPW>(); break;
+      case 2: wait_vm<2 * TPW>(); break;
+      default: wait_vm<3 * TPW>(); break;
+    }
+    __syncthreads();
+    if (kt + NS - 1 < KT) issue_blocks<TPW, NS, Gm::STAGE, WAVES>(src, step, ring, wave, kt + NS - 1);
+    const unsigned char* st = ring + (kt % NS) * Gm::STAGE;
+    v4i a[MF][R], b[4][R];
+    uint32_t sa[MF], sb[4];
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      const int f = wm * MF + i;
+#pragma unroll
+      for (int r = 0; r < R; ++r) a[i][r] = *reinterpret_cast<const v4i*>(st + (f * R + r) * 1024 + lane * 16);
+      sa[i] = as_lds[(16 * f + m) * KS + 4 * kt + q];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = 4 * wn + j;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        b[j][r] = *reinterpret_cast<const v4i*>(st + (Gm::A_TILES + s * R + r) * 1024 + lane * 16);
+      sb[j] = (bs_lds[(s * KG + (kt >> 2)) * 64 + lane] >> (8 * (kt & 3))) & 0xffu;
+    }
+    if (t_in == 0)
+      mma_tile<F, MF, R>(a, b, sa, sb, true, acc);
+    else
+      mma_tile<F, MF, R>(a, b, sa, sb, false, acc);
+    if (++t_in == g.CT) {  // end of a chunk: add its sum in chunk order
+      t_in = 0;
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sum[i][j] = sum[i][j] + acc[i][j];
     }
   }
 
@@ -235,7 +289,7 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_kernel(GemmArgs g) {
     // row's block.  sum[i][0], sum[i][1]: gate columns m and 16 + m; sum[i][2],
     // sum[i][3]: the matching up columns.  Output row of the intermediate: the
     // sorted position (routed) or the row (shared).
-    const int nb = 2 * nt + wn;
+    const int nb = WN * nt + wn;
 #pragma unroll
     for (int i = 0; i < MF; ++i)
 #pragma unroll
@@ -272,7 +326,7 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_kernel(GemmArgs g) {
         const int slot = slots[wm * 16 * MF + 16 * i + 4 * q + r];
         if (slot < S) {
 #pragma unroll
-          for (int j = 0; j < kNF; ++j) g.d_part[(size_t)slot * g.H + 16 * strip[j] + m] = sum[i][j][r];
+          for (int j = 0; j < 4; ++j) g.d_part[(size_t)slot * g.H + 16 * w_strip<MODE, WN>(g, nt, 4 * wn + j) + m] = sum[i][j][r];
         }
       }
   } else {
@@ -284,8 +338,8 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_kernel(GemmArgs g) {
         const int t = mb * BM + wm * 16 * MF + 16 * i + 4 * q + r;
         if (t < g.T) {
 #pragma unroll
-          for (int j = 0; j < kNF; ++j) {
-            const int h = 16 * strip[j] + m;
+          for (int j = 0; j < 4; ++j) {
+            const int h = 16 * w_strip<MODE, WN>(g, nt, 4 * wn + j) + m;
             float c = 0.f;
             for (int jj = 0; jj < g.k; ++jj)
               c = fmaf(g.topk_w[t * g.k + jj], g.d_part[(size_t)(t * g.k + jj) * g.H + h], c);
@@ -350,9 +404,20 @@ GCarve gcarve(const moe_layer_t& L, int T) {
 
 unsigned grid8(int tiles) { return (unsigned)((tiles + 7) / 8 * 8); }
 
-template <class F, int MODE>
+template <class F, int MODE, int WN>
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
-  hipLaunchKernelGGL((grouped_gemm_kernel<F, MODE>), dim3(grid8(g.MB * g.NT)), dim3(kThreads), 0, stream, g);
+  using Gm = Geo<F, WN>;
+  const size_t lds = (size_t)Gm::NS * Gm::STAGE + (size_t)Gm::BM * g.KT * 4 +
+                     (size_t)Gm::STRIPS * g.KG * 64 * 4 + (size_t)Gm::BM * 4;
+  static size_t lds_set = 0;  // largest dynamic LDS size enabled so far for this kernel
+  if (lds > 64 * 1024 && lds > lds_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_kernel<F, MODE, WN>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return hipErrorInvalidValue;
+    lds_set = lds;
+  }
+  hipLaunchKernelGGL((grouped_gemm_kernel<F, MODE, WN>), dim3(grid8(g.MB * g.NT)), dim3(Gm::THREADS), lds, stream,
+                     g);
   return hipGetLastError();
 }
 
@@ -394,7 +459,7 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
   {
     GemmArgs r = g;
     r.MB = (int)c.nblk;
-    r.NT = I / 64;
+    r.NT = I / 128;
     r.KT = H / 128;
     r.CT = pick_chunk(r.KT);
     r.KG = (r.KT + 3) / 4;
@@ -409,13 +474,13 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
     r.inter = I;
     r.oc = a4;
     r.os = as4;
-    if ((err = launch_gemm<FP4, GU_ROUTED>(r, stream)) != hipSuccess) return err;
+    if ((err = launch_gemm<FP4, GU_ROUTED, 4>(r, stream)) != hipSuccess) return err;
   }
   // routed down: A = intermediate in sorted order, B = W2[e], out d_part[slot]
   {
     GemmArgs r = g;
     r.MB = (int)c.nblk;
-    r.NT = H / 128;
+    r.NT = H % 256 ? H / 128 : H / 256;
     r.KT = I / 128;
     r.CT = pick_chunk(r.KT);
     r.KG = (r.KT + 3) / 4;
@@ -428,7 +493,8 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
     r.b_estride = tiled_codes_bytes(H, I, MX_FMT_FP4);
     r.bs_estride = tiled_scales_bytes(H, I);
     r.d_part = d_part;
-    if ((err = launch_gemm<FP4, DOWN_ROUTED>(r, stream)) != hipSuccess) return err;
+    err = H % 256 ? launch_gemm<FP4, DOWN_ROUTED, 2>(r, stream) : launch_gemm<FP4, DOWN_ROUTED, 4>(r, stream);
+    if (err != hipSuccess) return err;
   }
   if (Is == 0) {
     const size_t n = (size_t)T * H;
@@ -441,12 +507,12 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
   uint8_t* a8 = reinterpret_cast<uint8_t*>(at(c.a8));
   uint8_t* as8 = reinterpret_cast<uint8_t*>(at(c.as8));
   if ((err = launch_quant_act(x, T, H, MX_FMT_FP8, xq8, xs8, stream)) != hipSuccess) return err;
-  constexpr int BM8 = Frag<FP8>::BM;
+  constexpr int BM8 = Geo<FP8, 4>::BM;
   // shared gate/up: A = MXFP8 x, B = Ws13
   {
     GemmArgs r = g;
     r.MB = (T + BM8 - 1) / BM8;
-    r.NT = Is / 64;
+    r.NT = Is / 128;
     r.KT = H / 128;
     r.CT = pick_chunk(r.KT);
     r.KG = (r.KT + 3) / 4;
@@ -459,13 +525,13 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
     r.inter = Is;
     r.oc = a8;
     r.os = as8;
-    if ((err = launch_gemm<FP8, GU_SHARED>(r, stream)) != hipSuccess) return err;
+    if ((err = launch_gemm<FP8, GU_SHARED, 4>(r, stream)) != hipSuccess) return err;
   }
   // shared down + combine
   {
     GemmArgs r = g;
     r.MB = (T + BM8 - 1) / BM8;
-    r.NT = H / 128;
+    r.NT = H % 256 ? H / 128 : H / 256;
     r.KT = Is / 128;
     r.CT = pick_chunk(r.KT);
     r.KG = (r.KT + 3) / 4;
@@ -479,7 +545,8 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
     r.topk_w = w;
     r.residual = residual;
     r.y = y;
-    if ((err = launch_gemm<FP8, DOWN_SHARED>(r, stream)) != hipSuccess) return err;
+    err = H % 256 ? launch_gemm<FP8, DOWN_SHARED, 2>(r, stream) : launch_gemm<FP8, DOWN_SHARED, 4>(r, stream);
+    if (err != hipSuccess) return err;
   }
   return hipSuccess;
 }
