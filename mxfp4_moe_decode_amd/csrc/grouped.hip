@@ -79,10 +79,16 @@ struct Geo {
   static constexpr int A_TILES = (BM / 16) * R;  // 1 KiB blocks of A per K-tile
   static constexpr int B_TILES = STRIPS * R;     // 1 KiB blocks of B per K-tile
   static constexpr int TILES = A_TILES + B_TILES;
-  static constexpr int TPW = TILES / WAVES;      // blocks each wavefront moves per K-tile
-  static constexpr int NS = F::MB == 1 ? 5 : 3;  // K-tiles in the LDS ring
-  static constexpr int STAGE = TILES * 1024;
-  static_assert(TILES % WAVES == 0, "blocks split evenly over the wavefronts");
+  static constexpr int TPW = TILES / WAVES;      // code blocks each wavefront moves per K-tile
+  static constexpr int A_SC = BM / 64;           // 256-byte A-scale pieces per K-tile (waves 0..A_SC-1)
+  static constexpr int B_SC = STRIPS / WAVES;    // 256-byte B-scale lines each wavefront moves
+  static constexpr int NS = F::MB == 1 ? 4 : 3;  // K-tiles in the LDS ring
+  static constexpr int A_SC_OFF = TILES * 1024;  // stage layout: code blocks, A scales, B scales
+  static constexpr int B_SC_OFF = A_SC_OFF + BM * 4;
+  static constexpr int STAGE = B_SC_OFF + STRIPS * 256;
+  static_assert(TILES % WAVES == 0 && STRIPS % WAVES == 0, "work splits evenly over the wavefronts");
+  // loads per wavefront per K-tile, for the wavefronts that move an A-scale piece and for the others
+  static constexpr int CNT_A = TPW + 1 + B_SC, CNT_B = TPW + B_SC;
 };
 
 __device__ __forceinline__ uint32_t row_move32(uint32_t v) {  // neighbour swap inside a quad
@@ -145,17 +151,36 @@ __device__ __forceinline__ int w_strip(const GemmArgs& g, int nt, int s) {
   return 4 * WN * nt + s;
 }
 
-// Direct global -> LDS loads of this wavefront's blocks of K-tile kt into its
-// ring slot (block t = wave + WAVES i, 1 KiB each, lane l's 16 bytes at l*16).
-template <int TPW, int NS, int STAGE, int WAVES>
-__device__ __forceinline__ void issue_blocks(const uint8_t* (&src)[TPW], const int (&step)[TPW],
-                                             unsigned char* ring, int wave, int kt) {
-  unsigned char* st = ring + (kt % NS) * STAGE;
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) {
+// Direct global -> LDS loads of this wavefront's share of K-tile kt into its
+// ring slot: code blocks t = wave + WAVES i (1 KiB each, lane l's 16 bytes at
+// l*16), one 256-byte piece of the rows' A scales (wavefronts < A_SC: lane l
+// brings the 4 scale bytes of row 64*wave + l) and B_SC lines of B scales
+// (lane l's word of strip wave + WAVES i, for the K-tile's group of 4).
+template <class Gm>
+__device__ __forceinline__ void issue_ktile(const uint8_t* (&src)[Gm::TPW], const int (&step)[Gm::TPW],
+                                            const uint8_t* as_src, const uint8_t* (&bs_src)[Gm::B_SC],
+                                            unsigned char* ring, int wave, int kt) {
+  unsigned char* st = ring + (kt % Gm::NS) * Gm::STAGE;
 #if defined(__HIP_DEVICE_COMPILE__)  // the builtin only type-checks in the device pass
-    __builtin_amdgcn_global_load_lds(src[i] + (size_t)kt * step[i], st + (wave + WAVES * i) * 1024, 16, 0, 0);
+#pragma unroll
+  for (int i = 0; i < Gm::TPW; ++i)
+    __builtin_amdgcn_global_load_lds(src[i] + (size_t)kt * step[i], st + (wave + Gm::WAVES * i) * 1024, 16, 0, 0);
+  if (wave < Gm::A_SC) __builtin_amdgcn_global_load_lds(as_src + 4 * kt, st + Gm::A_SC_OFF + wave * 256, 4, 0, 0);
+#pragma unroll
+  for (int i = 0; i < Gm::B_SC; ++i)
+    __builtin_amdgcn_global_load_lds(bs_src[i] + (size_t)(kt >> 2) * 256, st + Gm::B_SC_OFF + (wave + Gm::WAVES * i) * 256,
+                                     4, 0, 0);
 #endif
+}
+
+// s_waitcnt until at most `ahead` K-tiles of this wavefront's loads are pending.
+template <int CNT>
+__device__ __forceinline__ void wait_ktiles(int ahead) {
+  switch (ahead) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<CNT>(); break;
+    case 2: wait_vm<2 * CNT>(); break;
+    default: wait_vm<3 * CNT>(); break;
   }
 }
 
@@ -186,12 +211,10 @@ __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  /
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / WN, wn = wave % WN;
   const int m = lane & 15, q = lane >> 4;
   const int S = g.T * g.k;
-  const int KT = g.KT, KG = g.KG, KS = KT * 4;  // KS: scale bytes per row
+  const int KT = g.KT, KG = g.KG;
 
   unsigned char* ring = smem;
-  unsigned char* as_lds = smem + NS * Gm::STAGE;                  // [BM][KS] bytes
-  uint32_t* bs_lds = reinterpret_cast<uint32_t*>(as_lds + BM * KS);  // [STRIPS][KG][64] words
-  int32_t* slots = reinterpret_cast<int32_t*>(bs_lds + STRIPS * KG * 64);
+  int32_t* slots = reinterpret_cast<int32_t*>(smem + NS * Gm::STAGE);
 
   if (threadIdx.x < BM) {
     const int r = mb * BM + (int)threadIdx.x;
@@ -199,17 +222,14 @@ __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  /
   }
   __syncthreads();
 
-  // scales of the whole K range into LDS
-  for (int idx = threadIdx.x; idx < BM * (KS / 4); idx += THREADS) {
-    const int rl = idx / (KS / 4), c = idx % (KS / 4);
-    const uint32_t v = *reinterpret_cast<const uint32_t*>(g.as + (size_t)a_row<MODE, BM>(g, slots, S, mb, rl) * g.as_stride + 4 * c);
-    *reinterpret_cast<uint32_t*>(as_lds + rl * KS + 4 * c) = v;
-  }
+  // scale sources: A, the 4 bytes of K-tile 0 of row 64*wave + lane; B, lane's
+  // word of group 0 of each strip this wavefront moves
+  const uint8_t* as_src = g.as + (size_t)a_row<MODE, BM>(g, slots, S, mb, (64 * wave + lane) % BM) * g.as_stride;
+  const uint8_t* bs_src[Gm::B_SC];
   const uint8_t* bsb = g.bs + (size_t)e * g.bs_estride;
-  for (int idx = threadIdx.x; idx < STRIPS * KG * 64; idx += THREADS) {
-    const int sidx = idx / (KG * 64), rem = idx % (KG * 64);
-    bs_lds[idx] = *reinterpret_cast<const uint32_t*>(bsb + ((size_t)w_strip<MODE, WN>(g, nt, sidx) * KG * 64 + rem) * 4);
-  }
+#pragma unroll
+  for (int i = 0; i < Gm::B_SC; ++i)
+    bs_src[i] = bsb + ((size_t)w_strip<MODE, WN>(g, nt, wave + WAVES * i) * KG * 64 + lane) * 4;
 
   // the blocks this wavefront moves: block t = wave + WAVES i of every K-tile
   const uint8_t* src[TPW];
@@ -239,19 +259,17 @@ __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  /
 
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; ++s0)
-    if (s0 < KT) issue_blocks<TPW, NS, Gm::STAGE, WAVES>(src, step, ring, wave, s0);
+    if (s0 < KT) issue_ktile<Gm>(src, step, as_src, bs_src, ring, wave, s0);
   for (int kt = 0, t_in = 0; kt < KT; ++kt) {
     // K-tile kt has landed once only the K-tiles issued after it are pending
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     const int ahead = min(NS - 2, KT - 1 - kt);  // K-tiles issued after kt
-    switch (ahead) {
-      case 0: wait_vm<0>(); break;
-      case 1: wait_vm<TPW>(); break;
-      case 2: wait_vm<2 * TPW>(); break;
-      default: wait_vm<3 * TPW>(); break;
-    }
+    if (wave < Gm::A_SC)
+      wait_ktiles<Gm::CNT_A>(ahead);
+    else
+      wait_ktiles<Gm::CNT_B>(ahead);
     __syncthreads();
-    if (kt + NS - 1 < KT) issue_blocks<TPW, NS, Gm::STAGE, WAVES>(src, step, ring, wave, kt + NS - 1);
+    if (kt + NS - 1 < KT) issue_ktile<Gm>(src, step, as_src, bs_src, ring, wave, kt + NS - 1);
     const unsigned char* st = ring + (kt % NS) * Gm::STAGE;
     v4i a[MF][R], b[4][R];
     uint32_t sa[MF], sb[4];
@@ -260,7 +278,7 @@ __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  /
       const int f = wm * MF + i;
 #pragma unroll
       for (int r = 0; r < R; ++r) a[i][r] = *reinterpret_cast<const v4i*>(st + (f * R + r) * 1024 + lane * 16);
-      sa[i] = as_lds[(16 * f + m) * KS + 4 * kt + q];
+      sa[i] = st[Gm::A_SC_OFF + (16 * f + m) * 4 + q];
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -268,7 +286,7 @@ __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  /
 #pragma unroll
       for (int r = 0; r < R; ++r)
         b[j][r] = *reinterpret_cast<const v4i*>(st + (Gm::A_TILES + s * R + r) * 1024 + lane * 16);
-      sb[j] = (bs_lds[(s * KG + (kt >> 2)) * 64 + lane] >> (8 * (kt & 3))) & 0xffu;
+      sb[j] = (reinterpret_cast<const uint32_t*>(st + Gm::B_SC_OFF)[s * 64 + lane] >> (8 * (kt & 3))) & 0xffu;
     }
     if (t_in == 0)
       mma_tile<F, MF, R>(a, b, sa, sb, true, acc);
@@ -407,8 +425,7 @@ unsigned grid8(int tiles) { return (unsigned)((tiles + 7) / 8 * 8); }
 template <class F, int MODE, int WN>
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
   using Gm = Geo<F, WN>;
-  const size_t lds = (size_t)Gm::NS * Gm::STAGE + (size_t)Gm::BM * g.KT * 4 +
-                     (size_t)Gm::STRIPS * g.KG * 64 * 4 + (size_t)Gm::BM * 4;
+  const size_t lds = (size_t)Gm::NS * Gm::STAGE + (size_t)Gm::BM * 4;
   static size_t lds_set = 0;  // largest dynamic LDS size enabled so far for this kernel
   if (lds > 64 * 1024 && lds > lds_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_kernel<F, MODE, WN>),
@@ -459,7 +476,7 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
   {
     GemmArgs r = g;
     r.MB = (int)c.nblk;
-    r.NT = I / 128;
+    r.NT = I / 64;
     r.KT = H / 128;
     r.CT = pick_chunk(r.KT);
     r.KG = (r.KT + 3) / 4;
@@ -474,13 +491,13 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
     r.inter = I;
     r.oc = a4;
     r.os = as4;
-    if ((err = launch_gemm<FP4, GU_ROUTED, 4>(r, stream)) != hipSuccess) return err;
+    if ((err = launch_gemm<FP4, GU_ROUTED, 2>(r, stream)) != hipSuccess) return err;
   }
   // routed down: A = intermediate in sorted order, B = W2[e], out d_part[slot]
   {
     GemmArgs r = g;
     r.MB = (int)c.nblk;
-    r.NT = H % 256 ? H / 128 : H / 256;
+    r.NT = H / 128;
     r.KT = I / 128;
     r.CT = pick_chunk(r.KT);
     r.KG = (r.KT + 3) / 4;
@@ -493,8 +510,7 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
     r.b_estride = tiled_codes_bytes(H, I, MX_FMT_FP4);
     r.bs_estride = tiled_scales_bytes(H, I);
     r.d_part = d_part;
-    err = H % 256 ? launch_gemm<FP4, DOWN_ROUTED, 2>(r, stream) : launch_gemm<FP4, DOWN_ROUTED, 4>(r, stream);
-    if (err != hipSuccess) return err;
+    if ((err = launch_gemm<FP4, DOWN_ROUTED, 2>(r, stream)) != hipSuccess) return err;
   }
   if (Is == 0) {
     const size_t n = (size_t)T * H;
@@ -507,12 +523,12 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
   uint8_t* a8 = reinterpret_cast<uint8_t*>(at(c.a8));
   uint8_t* as8 = reinterpret_cast<uint8_t*>(at(c.as8));
   if ((err = launch_quant_act(x, T, H, MX_FMT_FP8, xq8, xs8, stream)) != hipSuccess) return err;
-  constexpr int BM8 = Geo<FP8, 4>::BM;
+  constexpr int BM8 = Geo<FP8, 2>::BM;
   // shared gate/up: A = MXFP8 x, B = Ws13
   {
     GemmArgs r = g;
     r.MB = (T + BM8 - 1) / BM8;
-    r.NT = Is / 128;
+    r.NT = Is / 64;
     r.KT = H / 128;
     r.CT = pick_chunk(r.KT);
     r.KG = (r.KT + 3) / 4;
@@ -525,13 +541,13 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
     r.inter = Is;
     r.oc = a8;
     r.os = as8;
-    if ((err = launch_gemm<FP8, GU_SHARED, 4>(r, stream)) != hipSuccess) return err;
+    if ((err = launch_gemm<FP8, GU_SHARED, 2>(r, stream)) != hipSuccess) return err;
   }
   // shared down + combine
   {
     GemmArgs r = g;
     r.MB = (T + BM8 - 1) / BM8;
-    r.NT = H % 256 ? H / 128 : H / 256;
+    r.NT = H / 128;
     r.KT = Is / 128;
     r.CT = pick_chunk(r.KT);
     r.KG = (r.KT + 3) / 4;
@@ -545,8 +561,7 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
     r.topk_w = w;
     r.residual = residual;
     r.y = y;
-    err = H % 256 ? launch_gemm<FP8, DOWN_SHARED, 2>(r, stream) : launch_gemm<FP8, DOWN_SHARED, 4>(r, stream);
-    if (err != hipSuccess) return err;
+    if ((err = launch_gemm<FP8, DOWN_SHARED, 2>(r, stream)) != hipSuccess) return err;
   }
   return hipSuccess;
 }

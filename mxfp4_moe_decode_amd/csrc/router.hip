@@ -10,6 +10,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
+constexpr int kRouterRows = 8;  // rows a workgroup keeps in LDS
 
 __global__ void __launch_bounds__(kThreads) router_topk_kernel(
     const uint16_t* __restrict__ x, int T, int H, int E, int k, int rows_per_wg,
@@ -31,15 +32,43 @@ __global__ void __launch_bounds__(kThreads) router_topk_kernel(
   }
   __syncthreads();
 
+  // A wavefront per expert: each batch of up to 16 strides of the expert's
+  // weights is loaded once into registers and applied to every staged row, so
+  // each (row, expert) sum keeps the order of router_lane_partial.
   for (int e = wave; e < E; e += kWaves) {
     const float* wrow = wr + (size_t)e * H;
-    const float b = bias ? bias[e] : 0.f;
-    for (int r = 0; r < nrows; ++r) {
-      float p = router_lane_partial(xs + (size_t)r * H, wrow, H, lane);
-      p = wave_sum_butterfly(p);
-      if (bias) p = p + b;
-      if (lane == 0) ls[r * E + e] = p;
+    float p[kRouterRows];
+#pragma unroll
+    for (int r = 0; r < kRouterRows; ++r) p[r] = 0.f;
+    for (int h0 = 4 * lane; h0 < H; h0 += 16 * 256) {
+      float4 w[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (h0 + 256 * j < H) w[j] = *reinterpret_cast<const float4*>(wrow + h0 + 256 * j);
+#pragma unroll
+      for (int r = 0; r < kRouterRows; ++r) {
+        if (r < nrows) {
+          const uint16_t* xr = xs + (size_t)r * H;
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (h0 + 256 * j < H) {
+              const uint2 xv = *reinterpret_cast<const uint2*>(xr + h0 + 256 * j);
+              p[r] = fmaf(bf16_to_f32(xv.x & 0xffffu), w[j].x, p[r]);
+              p[r] = fmaf(bf16_to_f32(xv.x >> 16), w[j].y, p[r]);
+              p[r] = fmaf(bf16_to_f32(xv.y & 0xffffu), w[j].z, p[r]);
+              p[r] = fmaf(bf16_to_f32(xv.y >> 16), w[j].w, p[r]);
+            }
+        }
+      }
     }
+    const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+    for (int r = 0; r < kRouterRows; ++r)
+      if (r < nrows) {
+        float v = wave_sum_butterfly(p[r]);
+        if (bias) v = v + b;
+        if (lane == 0) ls[r * E + e] = v;
+      }
   }
   __syncthreads();
 
@@ -61,8 +90,8 @@ __global__ void __launch_bounds__(kThreads) router_topk_kernel(
 hipError_t launch_router_topk(const moe_layer_t& L, const uint16_t* x, int T, float* logits,
                               int32_t* ids, float* w, hipStream_t stream) {
   const int H = L.hidden, E = L.num_experts;
-  int rows = 32768 / H;
-  rows = rows < 1 ? 1 : (rows > 8 ? 8 : rows);
+  int rows = 65536 / H;
+  rows = rows < 1 ? 1 : (rows > kRouterRows ? kRouterRows : rows);
   const size_t lds = align_up((size_t)rows * H * 2, 16) + (size_t)rows * E * 4;
   const unsigned grid = (unsigned)((T + rows - 1) / rows);
   hipLaunchKernelGGL(router_topk_kernel, dim3(grid), dim3(kThreads), lds, stream, x, T, H, E,
