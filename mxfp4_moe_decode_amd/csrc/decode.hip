@@ -19,14 +19,16 @@
 //   phase C  routed down units (selected expert, 64 output columns, one
 //            16-column strip per wavefront) and shared down units; a down unit
 //            re-quantizes the intermediate it needs (MXFP4 routed, MXFP8
-//            shared) into LDS itself.  The last unit to finish a 64-column
-//            group combines it.
+//            shared) into LDS itself;
+//   combine  workgroup b combines the 64-column groups b, b+G, ... once all
+//            their down outputs are in.
 //
 // Phases B and C give each workgroup a contiguous run of units and are one
-// software pipeline over two register buffers: while a unit computes from one,
-// the next unit's tiles land in the other; after its stores a unit requests
-// the tiles of the unit after next into its own buffer, and its release waits
-// only for memory operations issued before that request.  A unit only waits for
+// software pipeline over three register buffers: while a unit computes from
+// one, the next two units' tiles land in the others, and as soon as its matrix
+// products have read its buffer a unit requests the tiles of the unit three
+// places on into it.  Results of phases B and C carry the call's tag (below), so no unit
+// waits for its own stores.  A unit only waits for
 // units of an earlier phase, so with every workgroup resident the smallest
 // unfinished unit can always progress.
 //
@@ -50,6 +52,7 @@ constexpr int kMaxSlots = kDecodeMaxT * kMaxK;
 constexpr int kMaxCT = 6;      // tiles of a gate/up K-chunk held in registers
 constexpr int kBufQuads = 12;  // 16-byte weight loads one prefetch buffer holds per lane
 constexpr int kBufWords = 6;   // scale words one prefetch buffer holds per lane
+constexpr int kBufs = 3;       // register buffers of the unit pipeline
 constexpr int kDownBatch = 8;  // routed (MXFP4) down tiles per register batch; MXFP8: half
 constexpr uint64_t kSpinTicks = 100000000ull;  // ~1 s of the 100 MHz constant clock
 
@@ -81,11 +84,12 @@ struct DecodeArgs {
   uint16_t* y;
   int32_t* ids_out;
   float* w_out;
-  uint32_t *sync, *comb;
+  uint32_t* sync;
   uint64_t* logits;  // tagged [T][E]
   uint8_t *xq4, *xs4, *xq8, *xs8;
   uint64_t* a_r;  // tagged [T*k][I]
-  float *a_s, *d_part, *s_part;
+  float* a_s;
+  uint64_t *d_part, *s_part;  // tagged [T*k][H], [T][H]
   uint64_t* trace;
 };
 
@@ -181,26 +185,6 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
-// Waits until at most n of this wavefront's vector memory operations are
-// outstanding (n uniform, 0 <= n <= 40).
-__device__ __forceinline__ void wait_vm_at_most(int n) {
-  compiler_fence();
-  switch (n) {
-#define MXMOE_VM_CASE(i) case i: wait_vm<i>(); break;
-    MXMOE_VM_CASE(1) MXMOE_VM_CASE(2) MXMOE_VM_CASE(3) MXMOE_VM_CASE(4) MXMOE_VM_CASE(5)
-    MXMOE_VM_CASE(6) MXMOE_VM_CASE(7) MXMOE_VM_CASE(8) MXMOE_VM_CASE(9) MXMOE_VM_CASE(10)
-    MXMOE_VM_CASE(11) MXMOE_VM_CASE(12) MXMOE_VM_CASE(13) MXMOE_VM_CASE(14) MXMOE_VM_CASE(15)
-    MXMOE_VM_CASE(16) MXMOE_VM_CASE(17) MXMOE_VM_CASE(18) MXMOE_VM_CASE(19) MXMOE_VM_CASE(20)
-    MXMOE_VM_CASE(21) MXMOE_VM_CASE(22) MXMOE_VM_CASE(23) MXMOE_VM_CASE(24) MXMOE_VM_CASE(25)
-    MXMOE_VM_CASE(26) MXMOE_VM_CASE(27) MXMOE_VM_CASE(28) MXMOE_VM_CASE(29) MXMOE_VM_CASE(30)
-    MXMOE_VM_CASE(31) MXMOE_VM_CASE(32) MXMOE_VM_CASE(33) MXMOE_VM_CASE(34) MXMOE_VM_CASE(35)
-    MXMOE_VM_CASE(36) MXMOE_VM_CASE(37) MXMOE_VM_CASE(38) MXMOE_VM_CASE(39) MXMOE_VM_CASE(40)
-#undef MXMOE_VM_CASE
-    default: wait_vm<0>(); break;
-  }
-  compiler_fence();
-}
-
 __device__ __forceinline__ void wait_count(uint32_t* c, uint32_t target, uint32_t* status) {
   const uint64_t t0 = wall_clock64();
   while (ld_dev(c) < target) {
@@ -219,23 +203,6 @@ __device__ __forceinline__ void wg_wait(uint32_t* c, uint32_t target, uint32_t* 
   if (threadIdx.x == 0) wait_count(c, target, status);
   __syncthreads();
   compiler_fence();
-}
-
-// The workgroup's stores issued before the last `after` memory operations of
-// each wavefront are acknowledged; then thread 0 adds 1 to *c.  With `last`,
-// returns in every thread whether this arrival completed the count to target.
-__device__ __forceinline__ bool wg_arrive(uint32_t* c, int after, bool last, uint32_t target, Smem& sm) {
-  wait_vm_at_most(after);
-  __syncthreads();
-  if (!last) {
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return false;
-  }
-  if (threadIdx.x == 0)
-    sm.flag = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 == target;
-  __syncthreads();
-  compiler_fence();
-  return sm.flag != 0;
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return (g / (1.f + expf(-g))) * u; }
@@ -519,17 +486,6 @@ struct Buf {
   uint32_t w[kBufWords];
 };
 
-// Number of weight loads `issue` makes for sequence entry j (per wavefront).
-template <class DA>
-__device__ __forceinline__ int issue_count(const DA& A, const Seq& S, int j, int wave) {
-  if (j >= S.nb + S.nc) return 0;
-  if (j < S.nb) return wave < A.nc1() ? 2 * A.ct1() + 6 : 0;
-  const int u = S.c0 + j - S.nb;
-  const int nt = min(A.kt2(), kDownBatch);
-  if (u < S.D * S.nhg) return nt + 2;
-  return 2 * min(A.kts(), kDownBatch / 2) + 2;
-}
-
 // Requests the weight tiles and scale words of sequence entry j into buf.
 template <class DA>
 __device__ __forceinline__ void issue(const DA& A, const Smem& sm, const Seq& S, int j, int lane, int wave,
@@ -738,28 +694,56 @@ __device__ __forceinline__ v4f down_compute(const uint8_t* w, const uint8_t* ws_
   return out;
 }
 
-// Combine of output columns 64 hg .. +64 for every row.
+// Combine of output columns 64 hg .. +64 for every row: reads the tagged down
+// outputs of the group until all are this call's, then
+// y = bf16( sum_j w_j d_j (j in order) + s + residual ).
 template <class DA>
-__device__ __forceinline__ void combine(const DA& A, const Smem& sm, int hg) {
+__device__ __forceinline__ void combine(const DA& A, uint32_t tag, const Smem& sm, int hg) {
   const int H = A.h(), k = A.kk();
-  for (int idx = threadIdx.x; idx < A.T * 64; idx += kThreads) {
-    const int t = idx >> 6, h = 64 * hg + (idx & 63);
-    float d[kMaxK];
+  constexpr int kPer = kDecodeMaxT * 64 / kThreads;  // (row, column) pairs per thread
+  float d[kPer][kMaxK], s[kPer];
+  const uint64_t t0 = wall_clock64();
+  bool ok;
+  do {
+    ok = true;
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) d[j] = j < k ? ld_dev(&A.d_part[(size_t)(t * k + j) * H + h]) : 0.f;
-    const float s = A.is() ? ld_dev(&A.s_part[(size_t)t * H + h]) : 0.f;
-    float acc = 0.f;
+    for (int p = 0; p < kPer; ++p) {
+      const int idx = threadIdx.x + p * kThreads;
+      if (idx < A.T * 64) {
+        const int t = idx >> 6, h = 64 * hg + (idx & 63);
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (j < k) acc = fmaf(sm.w[t * k + j], d[j], acc);
-    if (A.is()) acc = acc + s;
-    if (A.residual) acc = acc + bf16_to_f32(A.residual[(size_t)t * H + h]);
-    A.y[(size_t)t * H + h] = f32_to_bf16(acc);
+        for (int j = 0; j < kMaxK; ++j)
+          if (j < k) {
+            const uint64_t w = ld_dev(&A.d_part[(size_t)(t * k + j) * H + h]);
+            ok &= tag_ok(w, tag);
+            d[p][j] = __uint_as_float((uint32_t)w);
+          }
+        if (A.is()) {
+          const uint64_t w = ld_dev(&A.s_part[(size_t)t * H + h]);
+          ok &= tag_ok(w, tag);
+          s[p] = __uint_as_float((uint32_t)w);
+        }
+      }
+    }
+  } while (keep_polling(ok, t0, A.sync));
+#pragma unroll
+  for (int p = 0; p < kPer; ++p) {
+    const int idx = threadIdx.x + p * kThreads;
+    if (idx < A.T * 64) {
+      const int t = idx >> 6, h = 64 * hg + (idx & 63);
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j)
+        if (j < k) acc = fmaf(sm.w[t * k + j], d[p][j], acc);
+      if (A.is()) acc = acc + s[p];
+      if (A.residual) acc = acc + bf16_to_f32(A.residual[(size_t)t * H + h]);
+      A.y[(size_t)t * H + h] = f32_to_bf16(acc);
+    }
   }
 }
 
-// One sequence entry: compute from buf, store, request entry j + 2 into buf,
-// release (waiting only for what was issued before that request).
+// One sequence entry: compute from buf, request entry j + kBufs into buf,
+// store the results.
 template <class DA>
 __device__ __forceinline__ void run_entry(const DA& A, uint32_t tag, Smem& sm, const Seq& S, int j, Buf& buf,
                                           uint8_t* xq4_lds, uint8_t* xs4_lds, uint8_t* stage, int lane, int wave) {
@@ -768,15 +752,14 @@ __device__ __forceinline__ void run_entry(const DA& A, uint32_t tag, Smem& sm, c
     const int dd = u / per, i = u % per;
     gu_compute(A, sm, xq4_lds, xs4_lds, dd, buf, lane, wave);
     if (j == 0) trace_at(A, TR_B_MMA);
+    issue(A, sm, S, j + kBufs, lane, wave, buf);  // buf is free once the matrix products have read it
+    if (j == 0) trace_at(A, TR_B_NEXT);
     __syncthreads();
     int row, col;
     float a;
     if (gu_finish(sm, A.nc1(), sm.ecount[dd], &row, &col, &a))
       st_dev(&A.a_r[(size_t)sm.tl[dd][row] * A.i() + 16 * i + col], tagged(tag, a));
-    compiler_fence();
     if (j == 0) trace_at(A, TR_B_STORED);
-    issue(A, sm, S, j + 2, lane, wave, buf);
-    if (j == 0) trace_at(A, TR_B_NEXT);
     __syncthreads();  // sm.red is rewritten by the next unit
     if (j == 0) trace_at(A, TR_B_RELEASED);
     return;
@@ -784,7 +767,7 @@ __device__ __forceinline__ void run_entry(const DA& A, uint32_t tag, Smem& sm, c
   const int u = S.c0 + j - S.nb;
   const bool routed = u < S.D * S.nhg;
   const int dd = routed ? u / S.nhg : -1;
-  const int hg = routed ? u % S.nhg : u - S.D * S.nhg;
+  const int hg = routed ? u % S.nhg : u - S.D * S.nhg;  // 64-column group
   const int hs = 4 * hg + wave;
   const int m = lane & 15, q = lane >> 4;
   v4f out;
@@ -804,9 +787,11 @@ __device__ __forceinline__ void run_entry(const DA& A, uint32_t tag, Smem& sm, c
     const uint8_t* w = A.w2 + (size_t)e * ((size_t)A.h() * A.i() / 2) + (size_t)hs * A.kt2() * 1024 + lane * 16;
     const uint8_t* sw = A.w2s + (size_t)e * ((size_t)(A.h() / 16) * KG * 256) + ((size_t)hs * KG * 64 + lane) * 4;
     out = down_compute<FP4>(w, sw, A.kt2(), A.ct2(), codes, scales, n, buf, lane);
+    issue(A, sm, S, j + kBufs, lane, wave, buf);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (4 * q + r < n) st_dev(&A.d_part[(size_t)sm.tl[dd][4 * q + r] * A.h() + 16 * hs + m], out[r]);
+      if (4 * q + r < n)
+        st_dev(&A.d_part[(size_t)sm.tl[dd][4 * q + r] * A.h() + 16 * hs + m], tagged(tag, out[r]));
   } else {
     const int K = A.is();
     uint8_t* codes = stage;
@@ -821,18 +806,10 @@ __device__ __forceinline__ void run_entry(const DA& A, uint32_t tag, Smem& sm, c
     const uint8_t* w = A.ws2 + (size_t)hs * A.kts() * 2048 + lane * 16;
     const uint8_t* sw = A.ws2s + ((size_t)hs * KG * 64 + lane) * 4;
     out = down_compute<FP8>(w, sw, A.kts(), A.cts(), codes, scales, A.T, buf, lane);
+    issue(A, sm, S, j + kBufs, lane, wave, buf);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (4 * q + r < A.T) st_dev(&A.s_part[(size_t)(4 * q + r) * A.h() + 16 * hs + m], out[r]);
-  }
-  compiler_fence();
-  const int after = issue_count(A, S, j + 2, wave);
-  issue(A, sm, S, j + 2, lane, wave, buf);
-  uint32_t* c = ctr(A.comb, hg);
-  const uint32_t target = (uint32_t)(S.D + (A.is() ? 1 : 0));
-  if (wg_arrive(c, after, true, target, sm)) {
-    combine(A, sm, hg);
-    if (threadIdx.x == 0) st_dev(c, 0u);
+      if (4 * q + r < A.T) st_dev(&A.s_part[(size_t)(4 * q + r) * A.h() + 16 * hs + m], tagged(tag, out[r]));
   }
 }
 
@@ -932,17 +909,25 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
   }
   uint8_t* stage = dyn + align_up((size_t)kDecodeMaxT * (A.h() / 2 + A.h() / 32), 16);
   const int total = S.nb + S.nc;
-  Buf X, Y;
+  Buf X, Y, Z;
   issue(A, sm, S, 0, lane, wave, X);
   issue(A, sm, S, 1, lane, wave, Y);
-  for (int j = 0; j < total; j += 2) {  // entries alternate between the two buffers
+  issue(A, sm, S, 2, lane, wave, Z);
+  for (int j = 0; j < total; j += kBufs) {  // entries rotate over the three buffers
     run_entry(A, tag, sm, S, j, X, xq4_lds, xs4_lds, stage, lane, wave);
     if (j == S.nb - 1 && threadIdx.x == 0) tr[TR_B] = wall_clock64();
     if (j + 1 < total) {
       run_entry(A, tag, sm, S, j + 1, Y, xq4_lds, xs4_lds, stage, lane, wave);
       if (j + 1 == S.nb - 1 && threadIdx.x == 0) tr[TR_B] = wall_clock64();
     }
+    if (j + 2 < total) {
+      run_entry(A, tag, sm, S, j + 2, Z, xq4_lds, xs4_lds, stage, lane, wave);
+      if (j + 2 == S.nb - 1 && threadIdx.x == 0) tr[TR_B] = wall_clock64();
+    }
   }
+
+  // combines: workgroup b takes column groups b, b + G, ...
+  for (int hg = blockIdx.x; hg < S.nhg; hg += G) combine(A, tag, sm, hg);
 
   // exit: the last workgroup resets the launch-wide counters
   __syncthreads();
@@ -966,7 +951,7 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
 
 // ------------------------------------------------------------------ host side
 struct Carve {
-  size_t sync, comb, sync_end;
+  size_t sync, sync_end;
   size_t logits, xq4, xs4, xq8, xs8, a_r, a_s, d_part, s_part, trace, total;
 };
 
@@ -978,7 +963,6 @@ Carve carve(const moe_layer_t& L) {
   auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, 256); return at; };
   const size_t line = kLine * 4;
   c.sync = take(kSyncLines * line);
-  c.comb = take((H / 64) * line);
   c.sync_end = o;
   c.logits = take(T * E * 8);
   c.xq4 = take(T * H / 2);
@@ -987,8 +971,8 @@ Carve carve(const moe_layer_t& L) {
   c.xs8 = take(T * H / 32);
   c.a_r = take(T * k * I * 8);
   c.a_s = take(T * Is * 4 + 16);
-  c.d_part = take(T * k * H * 4);
-  c.s_part = take(T * H * 4);
+  c.d_part = take(T * k * H * 8);
+  c.s_part = take(T * H * 8);
   c.trace = take((size_t)kDecodeMaxGrid * kTraceWords * 8);
   c.total = o;
   return c;
@@ -1092,7 +1076,6 @@ hipError_t launch_decode(const moe_layer_t& L, const uint16_t* x, int T, const u
   A.ids_out = ids_out;
   A.w_out = w_out;
   A.sync = reinterpret_cast<uint32_t*>(base + c.sync);
-  A.comb = reinterpret_cast<uint32_t*>(base + c.comb);
   A.logits = reinterpret_cast<uint64_t*>(base + c.logits);
   A.xq4 = reinterpret_cast<uint8_t*>(base + c.xq4);
   A.xs4 = reinterpret_cast<uint8_t*>(base + c.xs4);
@@ -1100,8 +1083,8 @@ hipError_t launch_decode(const moe_layer_t& L, const uint16_t* x, int T, const u
   A.xs8 = reinterpret_cast<uint8_t*>(base + c.xs8);
   A.a_r = reinterpret_cast<uint64_t*>(base + c.a_r);
   A.a_s = reinterpret_cast<float*>(base + c.a_s);
-  A.d_part = reinterpret_cast<float*>(base + c.d_part);
-  A.s_part = reinterpret_cast<float*>(base + c.s_part);
+  A.d_part = reinterpret_cast<uint64_t*>(base + c.d_part);
+  A.s_part = reinterpret_cast<uint64_t*>(base + c.s_part);
   A.trace = reinterpret_cast<uint64_t*>(base + c.trace);
   if (A.H == 3072 && A.I == 1024 && A.Is == 1024 && A.E == 128 && A.k == 4)
     return launch_instance<MiniMaxShape>(A, lds, stream);
