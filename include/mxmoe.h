@@ -188,8 +188,9 @@ moe_status moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
  * combine order are those of the oracle.  fused_moe_mxfp4_grouped uses the same
  * arithmetic, so both give identical bits for the same rows.
  * Output row t depends only on x[t] (and residual[t]): results are bit-identical
- * for any T and any row order.  Shapes with (H/128)/NC > 8 give
- * MOE_ERR_UNSUPPORTED (the grouped call handles them).  The launch is a persistent grid sized to the
+ * for any T and any row order.  Shapes whose gate/up K-chunk is longer than 6
+ * tiles ((H/128)/NC > 6), or whose staged x and intermediates exceed the
+ * 160 KiB of LDS, give MOE_ERR_UNSUPPORTED (the grouped call handles them).  The launch is a persistent grid sized to the
  * device's co-resident capacity; its device-side waits are bounded, and a wait
  * that gives up marks the workspace (see moe_decode_status) instead of hanging.
  */
