@@ -226,7 +226,8 @@ moe_status moe_decode_status(const void* ws, size_t ws_bytes);
  * combines done, end of its first such unit (0 if it had none), logits in LDS,
  * top-k done, expert list done, then for its first routed gate/up unit: matrix
  * products done, results stored, next tiles in place, released; then its first
- * down unit's intermediate staged (0 where it had no such unit).
+ * down unit's intermediate staged (0 where it had no such unit), and the
+ * time its first load (the call's epoch word) returned.
  * Copies at most n_words words to host memory and returns
  * the number of workgroups of that call (0 if none ran yet), or a negative
  * moe_status.

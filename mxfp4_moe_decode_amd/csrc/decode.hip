@@ -62,13 +62,15 @@ constexpr int kLine = 64;  // words
 __device__ __forceinline__ uint32_t* ctr(uint32_t* base, int i) { return base + (size_t)i * kLine; }
 // Lines of the sync block: status, done, x-quant, shared-intermediate ready,
 // grid size of the last call, call epoch.
-enum { S_STATUS = 0, S_DONE = 1, S_XQ = 2, S_SA = 3, S_GRID = 4, S_EPOCH = 5, kSyncLines = 6 };
+enum { S_STATUS = 0, S_DONE = 1, S_GRID = 2, S_EPOCH = 3, kSyncLines = 4 };
+static_assert(kDecodeGridOffset == (size_t)S_GRID * kLine * 4, "grid word offset");
+static_assert(kDecodeStatusOffset == (size_t)S_STATUS * kLine * 4, "status word offset");
 
 // Timestamps each workgroup records (100 MHz device clock).
 enum {
   TR_START = 0, TR_A = 1, TR_LOGITS = 2, TR_ROUTED = 3, TR_B = 4, TR_C = 5, TR_FIRST = 6,
-  TR_LOGITS_LDS = 7, TR_TOPK = 8, TR_ELIST = 9,
-  TR_B_MMA = 10, TR_B_STORED = 11, TR_B_NEXT = 12, TR_B_RELEASED = 13, TR_C_STAGED = 14
+  TR_XQ = 7, TR_TOPK = 8, TR_ELIST = 9,
+  TR_B_MMA = 10, TR_B_STORED = 11, TR_S_MMA = 12, TR_B_RELEASED = 13, TR_C_STAGED = 14, TR_TAG = 15
 };
 
 struct DecodeArgs {
@@ -86,9 +88,8 @@ struct DecodeArgs {
   float* w_out;
   uint32_t* sync;
   uint64_t* logits;  // tagged [T][E]
-  uint8_t *xq4, *xs4, *xq8, *xs8;
   uint64_t* a_r;  // tagged [T*k][I]
-  float* a_s;
+  uint64_t* a_s;  // tagged [T][2 I_s]
   uint64_t *d_part, *s_part;  // tagged [T*k][H], [T][H]
   uint64_t* trace;
 };
@@ -136,24 +137,17 @@ struct Smem {
 };
 
 // ------------------------------------------------------------------ synchronisation
-// Data handed from one workgroup to another (logits, quantized x, fp32
-// intermediates and partial outputs) is written and read with relaxed
-// agent-scope atomic accesses, which gfx950 issues with the sc1 bit: they are
-// served at the device's coherence point, past the per-XCD L2 caches, so no L2
-// write-back or invalidate is needed.  Before a counter is bumped each
-// wavefront waits for its stores to be acknowledged (vector memory operations
-// complete in issue order, so it waits until no more than the operations
-// issued after the stores are outstanding), then the workgroup barrier, then
-// one atomic add.  A consumer polls the counter and issues its data loads
-// only after the poll has returned.
-//
-// Where many producers feed one consumer set (128 router units, 64 gate/up
-// strips per expert), a shared counter would serialize the atomics at the
-// memory side; there the data carries the call's tag instead: each value is
-// stored as one 64-bit word (tag << 32 | fp32 bits), single-copy atomic, and a
-// consumer reads the words until every tag is this call's.  The tag is one
-// more than the epoch word, which the last workgroup of a call advances, so
-// words of an earlier call (or the zero-filled workspace) never match.
+// Data handed from one workgroup to another (logits, gate/up results,
+// partial outputs) is written and read with relaxed agent-scope atomic
+// accesses, which gfx950 issues with the sc1 bit: they are served at the
+// device's coherence point, past the per-XCD L2 caches, so no L2 write-back
+// or invalidate is needed.  Each value is stored as one 64-bit word (tag << 32
+// | fp32 bits), single-copy atomic, and a consumer reads the words until
+// every tag is this call's: no counter is bumped, so producers never wait for
+// their stores to be acknowledged and many producers never serialize on one
+// address.  The tag is one more than the epoch word, which the last workgroup
+// of a call advances, so words of an earlier call (or the zero-filled
+// workspace) never match.
 template <class T>
 __device__ __forceinline__ T ld_dev(const T* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -161,17 +155,6 @@ __device__ __forceinline__ T ld_dev(const T* p) {
 template <class T>
 __device__ __forceinline__ void st_dev(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ v4i ld_dev16(const uint8_t* p) {
-  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
-  const uint64_t a = ld_dev(q), b = ld_dev(q + 1);
-  return v4i{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)(uint32_t)b, (int)(uint32_t)(b >> 32)};
-}
-__device__ __forceinline__ float4 ld_dev_f4(const float* p) {
-  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
-  const uint64_t a = ld_dev(q), b = ld_dev(q + 1);
-  return make_float4(__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
-                     __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
 }
 // Keeps the compiler from moving memory accesses (and, for the machine
 // scheduler, any instruction) across this point.
@@ -185,31 +168,10 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
-__device__ __forceinline__ void wait_count(uint32_t* c, uint32_t target, uint32_t* status) {
-  const uint64_t t0 = wall_clock64();
-  while (ld_dev(c) < target) {
-    if (ld_dev(status)) return;
-    if (wall_clock64() - t0 > kSpinTicks) {
-      __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-}
-
-// Workgroup-wide wait: thread 0 polls, the barrier releases everyone.
-__device__ __forceinline__ void wg_wait(uint32_t* c, uint32_t target, uint32_t* status) {
-  compiler_fence();
-  if (threadIdx.x == 0) wait_count(c, target, status);
-  __syncthreads();
-  compiler_fence();
-}
-
 __device__ __forceinline__ float silu_mul(float g, float u) { return (g / (1.f + expf(-g))) * u; }
 
-__device__ __forceinline__ uint64_t tagged(uint32_t tag, float v) {
-  return ((uint64_t)tag << 32) | __float_as_uint(v);
-}
+__device__ __forceinline__ uint64_t tagged_u(uint32_t tag, uint32_t v) { return ((uint64_t)tag << 32) | v; }
+__device__ __forceinline__ uint64_t tagged(uint32_t tag, float v) { return tagged_u(tag, __float_as_uint(v)); }
 __device__ __forceinline__ bool tag_ok(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
 
 // Workgroup-uniform bounded retry: true to go on polling.  Gives up (marking
@@ -233,75 +195,91 @@ __device__ __forceinline__ uint32_t pick3(uint32_t w0, uint32_t w1, uint32_t w2,
 }
 
 // ------------------------------------------------------------------ MX block quantization by 8 lanes
-// Eight consecutive lanes hold the 32 values of one block (lane j: values
-// 4j..4j+3, fp32 bit patterns) and agree on the block scale with three
-// butterfly steps.  Returns the four codes packed (FP4: 16 bits, element 4j+i
+// Eight consecutive lanes (8i .. 8i+7) hold the 32 values of one block (lane
+// j: values 4j..4j+3, fp32 bit patterns) and agree on the block scale in
+// three steps.  Returns the four codes packed (FP4: 16 bits, element 4j+i
 // in nibble i; FP8: 32 bits, byte i) and the E8M0 code in *scale.
 template <class F>
 __device__ __forceinline__ uint32_t quant_block8(const uint32_t (&bits)[4], uint32_t* scale) {
   uint32_t am = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) am = max(am, bits[i] & 0x7fffffffu);
-#pragma unroll
-  for (int off = 1; off < 8; off <<= 1) am = max(am, (uint32_t)__shfl_xor((int)am, off, 8));
+  // maximum over the eight lanes with data-parallel moves (every lane of the
+  // group is active): swap neighbours, swap pairs, mirror the half row
+  am = max(am, (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0xB1, 0xf, 0xf, false));
+  am = max(am, (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0x4E, 0xf, 0xf, false));
+  am = max(am, (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0x141, 0xf, 0xf, false));
   const int e = block_exponent<F>(am);
+  const float inv = block_inv_scale(e);
   uint32_t packed = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) packed |= quant_elem<F>(bits[i], e) << ((F::MB == 1 ? 4 : 8) * i);
+  for (int i = 0; i < 4; ++i) packed |= quant_elem_fast<F>(bits[i], inv) << ((F::MB == 1 ? 4 : 8) * i);
   *scale = (uint32_t)(e + 127);
   return packed;
 }
 
-// ------------------------------------------------------------------ phase A
-// x quantization: block task i of T * nb * F (nb = H/32 blocks per row, F = 2
-// formats with a shared expert, else 1) is (row, format, block); a unit is 32
-// tasks.
-__host__ __device__ __forceinline__ int xq_units(int T, int H, int Is) {
-  return (T * (H / 32) * (Is ? 2 : 1) + kThreads / 8 - 1) / (kThreads / 8);
-}
+// ------------------------------------------------------------------ x quantization
+// Every workgroup quantizes the rows of x it needs itself, into LDS.  A task
+// is one 32-value block (row m, block b) of the T * H/32; the eight lanes of
+// group g = threadIdx / 8 handle tasks t0 + p * 32 + g of a batch (p <
+// kQBatch), lane j taking values 4j .. 4j+3 (bf16 x, read with plain loads: x
+// does not change during the call).  A batch's loads are all issued before
+// any of its blocks is quantized.
+constexpr int kQBatch = 16;
+constexpr int kQGroups = kThreads / 8;
 
 template <class DA>
-__device__ __forceinline__ void unit_xq(const DA& A, int u) {
-  const int nb = A.h() / 32, F = A.is() ? 2 : 1;
-  const int task = u * (kThreads / 8) + (int)threadIdx.x / 8;
-  const int j = threadIdx.x & 7;
-  const bool act = task < A.T * nb * F;
-  int t = 0, fp8 = 0, b = 0;
-  if (act) {
-    t = task / (nb * F);
-    const int r = task % (nb * F);
-    fp8 = r / nb;
-    b = r % nb;
-  }
-  uint32_t bits[4] = {0u, 0u, 0u, 0u};
-  if (act) {
-    const uint2 v = *reinterpret_cast<const uint2*>(A.x + (size_t)t * A.h() + 32 * b + 4 * j);
-    bits[0] = v.x << 16;
-    bits[1] = v.x & 0xffff0000u;
-    bits[2] = v.y << 16;
-    bits[3] = v.y & 0xffff0000u;
-  }
-  // the eight lanes of a task share fp8 (same task), so the branch is uniform per group
-  uint32_t sc;
-  if (fp8) {
-    const uint32_t word = quant_block8<FP8>(bits, &sc);
-    if (act) {
-      st_dev(reinterpret_cast<uint32_t*>(A.xq8 + (size_t)t * A.h() + 32 * b + 4 * j), word);
-      if (j == 0) st_dev(&A.xs8[t * nb + b], (uint8_t)sc);
-    }
-  } else {
-    const uint32_t half = quant_block8<FP4>(bits, &sc);
-    if (act) {
-      st_dev(reinterpret_cast<uint16_t*>(A.xq4 + (size_t)t * (A.h() / 2) + 16 * b + 2 * j), (uint16_t)half);
-      if (j == 0) st_dev(&A.xs4[t * nb + b], (uint8_t)sc);
+__device__ __forceinline__ void x_batch_load(const DA& A, int t0, uint32_t (&bits)[kQBatch][4]) {
+  const int H = A.h(), nb = H / 32, tasks = A.T * nb, j = threadIdx.x & 7, grp = threadIdx.x / 8;
+#pragma unroll
+  for (int p = 0; p < kQBatch; ++p) {
+    const int task = t0 + p * kQGroups + grp;
+    bits[p][0] = bits[p][1] = bits[p][2] = bits[p][3] = 0u;
+    if (task < tasks) {
+      const uint2 v = *reinterpret_cast<const uint2*>(A.x + (size_t)(task / nb) * H + 32 * (task % nb) + 4 * j);
+      bits[p][0] = v.x << 16;
+      bits[p][1] = v.x & 0xffff0000u;
+      bits[p][2] = v.y << 16;
+      bits[p][3] = v.y & 0xffff0000u;
     }
   }
-  compiler_fence();
-  wait_vm<0>();
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr(A.sync, S_XQ), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Quantizes a loaded batch to format F: codes [T][H * bytes per element],
+// scales [T][H/32].
+template <class F, class DA>
+__device__ __forceinline__ void x_batch_quant(const DA& A, int t0, const uint32_t (&bits)[kQBatch][4],
+                                              uint8_t* codes, uint8_t* scales) {
+  const int H = A.h(), nb = H / 32, tasks = A.T * nb, j = threadIdx.x & 7, grp = threadIdx.x / 8;
+#pragma unroll
+  for (int p = 0; p < kQBatch; ++p) {
+    if (t0 + p * kQGroups >= tasks) break;  // uniform
+    const int task = t0 + p * kQGroups + grp;
+    uint32_t sc;
+    const uint32_t packed = quant_block8<F>(bits[p], &sc);
+    if (task < tasks) {
+      const int m = task / nb, b = task % nb;
+      if constexpr (F::MB == 1)
+        *reinterpret_cast<uint16_t*>(codes + (size_t)m * (H / 2) + 16 * b + 2 * j) = (uint16_t)packed;
+      else
+        *reinterpret_cast<uint32_t*>(codes + (size_t)m * H + 32 * b + 4 * j) = packed;
+      if (j == 0) scales[m * nb + b] = (uint8_t)sc;
+    }
+  }
+}
+
+// MXFP4 copy of all T rows: codes [T][H/2], scales [T][H/32].
+template <class DA>
+__device__ __forceinline__ void quant_x_fp4(const DA& A, uint8_t* codes, uint8_t* scales) {
+  const int tasks = A.T * (A.h() / 32);
+  for (int t0 = 0; t0 < tasks; t0 += kQBatch * kQGroups) {
+    uint32_t bits[kQBatch][4];
+    x_batch_load(A, t0, bits);
+    x_batch_quant<FP4>(A, t0, bits, codes, scales);
+  }
+}
+
+// ------------------------------------------------------------------ phase A
 // Logits of expert e for all rows; wave w takes rows w, w+4, ...  Same
 // per-row arithmetic as router_lane_partial: each batch of up to 16 strides
 // of the expert's weights is loaded once, then the rows go through it two at
@@ -313,6 +291,7 @@ __device__ __forceinline__ void unit_router(const DA& A, uint32_t tag, int e, in
   float p[4] = {0.f, 0.f, 0.f, 0.f};
   int nr = 0;
   for (int t = wave; t < A.T; t += kWaves) ++nr;
+  if (nr == 0) return;
   for (int h0 = 4 * lane; h0 < H; h0 += 16 * 256) {
     float4 w[16];
 #pragma unroll
@@ -356,8 +335,79 @@ __device__ __forceinline__ void unit_router(const DA& A, uint32_t tag, int e, in
     }
 }
 
-// Chunk sums of a gate/up unit in sm.red, added in chunk order, then SwiGLU:
-// thread (row, column) for row < n; returns false for idle threads.
+// Shared gate/up strip st (0 <= st < 2 I_s/16: gate strips, then up strips):
+// wave w computes K-chunk w (MXFP8 x MXFP8); the chunk sums meet in LDS and
+// are added in chunk order.  The workgroup first quantizes x itself, to MXFP8
+// (x8: codes [T][H], scales at kDecodeMaxT * H) and to MXFP4 (the copy the
+// routed gate/up units read later); the first batch of x is requested before
+// the weights, so that quantizing does not wait for them.  The fp32 result
+// goes to a_s[row][16 st + col] as tagged words (gate columns, then up
+// columns); SwiGLU is applied where it is staged.
+template <class DA>
+__device__ __forceinline__ void unit_shared_strip(const DA& A, uint32_t tag, Smem& sm, int st, uint8_t* x8,
+                                                  uint8_t* xq4, uint8_t* xs4, int lane, int wave) {
+  const int CT = A.ct1(), KG = (A.kt1() + 3) / 4;
+  const int m = lane & 15, q = lane >> 4;
+  const bool act = wave < A.nc1();
+  const int t0 = wave * CT;
+  uint8_t* xs8 = x8 + (size_t)kDecodeMaxT * A.h();
+  const int tasks = A.T * (A.h() / 32);
+  uint32_t bits[kQBatch][4];
+  x_batch_load(A, 0, bits);
+  v4i B[kMaxCT][2];
+  uint32_t sw[3];
+  if (act) {
+    const uint8_t* wb = A.ws13 + ((size_t)st * A.kt1() + t0) * 2048 + lane * 16;
+#pragma unroll
+    for (int j = 0; j < kMaxCT; ++j)
+      if (j < CT) {
+        B[j][0] = load_stream16(wb + j * 2048);
+        B[j][1] = load_stream16(wb + j * 2048 + 1024);
+      }
+    const uint8_t* sp = A.ws13s + ((size_t)st * KG * 64 + lane) * 4;
+#pragma unroll
+    for (int g = 0; g < 3; ++g) sw[g] = load_stream4(sp + (size_t)min(t0 / 4 + g, KG - 1) * 256);
+  }
+  for (int b0 = 0; b0 < tasks; b0 += kQBatch * kQGroups) {
+    if (b0 > 0) x_batch_load(A, b0, bits);
+    x_batch_quant<FP8>(A, b0, bits, x8, xs8);
+    x_batch_quant<FP4>(A, b0, bits, xq4, xs4);
+  }
+  trace_at(A, TR_XQ);
+  __syncthreads();
+  if (act) {
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kMaxCT; ++j)
+      if (j < CT) {
+        const int kt = t0 + j;
+        v4i a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
+        uint32_t sa = 127;
+        if (m < A.T) {
+          const uint8_t* ap = x8 + (size_t)m * A.h() + kt * 128 + 16 * q;
+          a0 = *reinterpret_cast<const v4i*>(ap);
+          a1 = *reinterpret_cast<const v4i*>(ap + 64);
+          sa = xs8[m * (A.h() / 32) + 4 * kt + q];
+        }
+        const uint32_t word = pick3(sw[0], sw[1], sw[2], kt / 4 - t0 / 4);
+        acc = mfma_fp8(a0, a1, B[j][0], B[j][1], acc, sa, scale_byte(word, kt));
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.red[wave][0][4 * q + r][m] = acc[r];
+  }
+  trace_at(A, TR_S_MMA);
+  __syncthreads();
+  const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
+  if (r < A.T) {
+    float v = sm.red[0][0][r][c];
+    for (int ch = 1; ch < A.nc1(); ++ch) v = v + sm.red[ch][0][r][c];
+    st_dev(&A.a_s[(size_t)r * (2 * A.is()) + 16 * st + c], tagged(tag, v));
+  }
+  __syncthreads();  // sm.red and x8 are reused
+}
+
+// Chunk sums of a routed gate/up unit in sm.red, added in chunk order, then
+// SwiGLU: thread (row, column) for row < n; returns false for idle threads.
 __device__ __forceinline__ bool gu_finish(const Smem& sm, int nc, int n, int* row, int* col, float* a) {
   const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
   if (r >= n) return false;
@@ -370,73 +420,6 @@ __device__ __forceinline__ bool gu_finish(const Smem& sm, int nc, int n, int* ro
   *col = c;
   *a = silu_mul(g, u);
   return true;
-}
-
-// Shared gate/up strip i: wave w computes K-chunk w of the gate strip i and
-// the up strip I_s/16 + i (MXFP8 x MXFP8); the chunk sums meet in LDS.
-template <class DA>
-__device__ __forceinline__ void unit_shared_gu(const DA& A, Smem& sm, int i, int lane, int wave) {
-  const int CT = A.ct1(), KG = (A.kt1() + 3) / 4;
-  const int m = lane & 15, q = lane >> 4;
-  const bool act = wave < A.nc1();
-  const int t0 = wave * CT;
-  v4i B[2][kMaxCT][2];
-  uint32_t sw[2][3];
-  if (act) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int st = s == 0 ? i : A.is() / 16 + i;
-      const uint8_t* wb = A.ws13 + ((size_t)st * A.kt1() + t0) * 2048 + lane * 16;
-#pragma unroll
-      for (int j = 0; j < kMaxCT; ++j)
-        if (j < CT) {
-          B[s][j][0] = load_stream16(wb + j * 2048);
-          B[s][j][1] = load_stream16(wb + j * 2048 + 1024);
-        }
-      const uint8_t* sp = A.ws13s + ((size_t)st * KG * 64 + lane) * 4;
-#pragma unroll
-      for (int g = 0; g < 3; ++g)
-        sw[s][g] = load_stream4(sp + (size_t)min(t0 / 4 + g, KG - 1) * 256);
-    }
-  }
-  wg_wait(ctr(A.sync, S_XQ), (uint32_t)xq_units(A.T, A.h(), A.is()), A.sync);
-  if (act) {
-    v4i a0[kMaxCT], a1[kMaxCT];
-    uint32_t sa[kMaxCT];
-#pragma unroll
-    for (int j = 0; j < kMaxCT; ++j) {
-      a0[j] = a1[j] = v4i{0, 0, 0, 0};
-      sa[j] = 127;
-      if (j < CT && m < A.T) {
-        const int kt = t0 + j;
-        const uint8_t* ap = A.xq8 + (size_t)m * A.h() + kt * 128 + 16 * q;
-        a0[j] = ld_dev16(ap);
-        a1[j] = ld_dev16(ap + 64);
-        sa[j] = ld_dev(&A.xs8[m * (A.h() / 32) + 4 * kt + q]);
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < kMaxCT; ++j)
-        if (j < CT) {
-          const int kt = t0 + j;
-          const uint32_t word = pick3(sw[s][0], sw[s][1], sw[s][2], kt / 4 - t0 / 4);
-          acc = mfma_fp8(a0[j], a1[j], B[s][j][0], B[s][j][1], acc, sa[j], scale_byte(word, kt));
-        }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm.red[wave][s][4 * q + r][m] = acc[r];
-    }
-  }
-  __syncthreads();
-  int row, col;
-  float a;
-  if (gu_finish(sm, A.nc1(), A.T, &row, &col, &a)) st_dev(&A.a_s[(size_t)row * A.is() + 16 * i + col], a);
-  compiler_fence();
-  wait_vm<0>();
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr(A.sync, S_SA), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ routing
@@ -478,7 +461,7 @@ __device__ __forceinline__ void build_expert_list(const DA& A, Smem& sm, int lan
 // phase-C units [c0, c1).
 struct Seq {
   int b0, nb, c0, nc;
-  int D, nhg;
+  int D, nhg, ns;  // selected experts, 64-column groups, shared down units (nhg or 0)
 };
 
 struct Buf {
@@ -514,8 +497,9 @@ __device__ __forceinline__ void issue(const DA& A, const Smem& sm, const Seq& S,
     return;
   }
   const int u = S.c0 + j - S.nb;
-  if (u < S.D * S.nhg) {
-    const int e = sm.elist[u / S.nhg], hs = 4 * (u % S.nhg) + wave;
+  if (u >= S.ns) {
+    const int ur = u - S.ns;
+    const int e = sm.elist[ur / S.nhg], hs = 4 * (ur % S.nhg) + wave;
     const int KG = (A.kt2() + 3) / 4, nt = min(A.kt2(), kDownBatch);
     const uint8_t* wb = A.w2 + (size_t)e * ((size_t)A.h() * A.i() / 2) + (size_t)hs * A.kt2() * 1024 + lane * 16;
 #pragma unroll
@@ -525,7 +509,7 @@ __device__ __forceinline__ void issue(const DA& A, const Smem& sm, const Seq& S,
 #pragma unroll
     for (int g = 0; g < 2; ++g) buf.w[g] = load_stream4(sp + (size_t)min(g, KG - 1) * 256);
   } else {
-    const int hs = 4 * (u - S.D * S.nhg) + wave;
+    const int hs = 4 * u + wave;
     const int KG = (A.kts() + 3) / 4, nt = min(A.kts(), kDownBatch / 2);
     const uint8_t* wb = A.ws2 + (size_t)hs * A.kts() * 2048 + lane * 16;
 #pragma unroll
@@ -577,67 +561,100 @@ __device__ __forceinline__ void gu_compute(const DA& A, Smem& sm, const uint8_t*
   }
 }
 
-// Four consecutive fp32 values, plain or tagged (the value is the low word).
-__device__ __forceinline__ float4 load4(const float* p) { return ld_dev_f4(p); }
-__device__ __forceinline__ float4 load4(const uint64_t* p) {
-  return make_float4(__uint_as_float((uint32_t)ld_dev(p)), __uint_as_float((uint32_t)ld_dev(p + 1)),
-                     __uint_as_float((uint32_t)ld_dev(p + 2)), __uint_as_float((uint32_t)ld_dev(p + 3)));
-}
+// Staging of a down unit's intermediate rows into LDS as MX blocks: codes
+// [n, K/2] (FP4) or [n, K] (FP8), scales [n, K/32].  Task t = (row m, block b)
+// of n * K/32 is handled by the eight lanes 8(t mod 32) .. +8 of pass t / 128
+// slot (t / 32) mod 4; each lane holds four consecutive values.
+constexpr int kStagePass = 4 * (kThreads / 8);  // tasks per pass
 
-// Waits until rows slots[0..n) of a tagged [*, K] array all carry this call's
-// tag (only the tag halves are read).
-template <class DA>
-__device__ __forceinline__ void wait_tagged_rows(const DA& A, uint32_t tag, const uint64_t* src, int K, int n,
-                                                 const uint8_t* slots) {
-  const uint64_t t0 = wall_clock64();
-  const uint32_t* hi = reinterpret_cast<const uint32_t*>(src) + 1;
-  bool ok;
-  do {
-    ok = true;
-    for (int idx = threadIdx.x; idx < n * K; idx += kThreads) {
-      const int m = idx / K, c = idx % K;
-      ok &= ld_dev(&hi[2 * ((size_t)slots[m] * K + c)]) == tag;
+template <class F>
+__device__ __forceinline__ void stage_quantize(const float4 (&v)[4], int t0, int tasks, int K, uint8_t* codes,
+                                               uint8_t* scales) {
+  const int nb = K / 32, j = threadIdx.x & 7;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int task = t0 + p * (kThreads / 8) + (int)threadIdx.x / 8;
+    if (t0 + p * (kThreads / 8) >= tasks) break;  // uniform: whole slot beyond the end
+    const uint32_t bits[4] = {__float_as_uint(v[p].x), __float_as_uint(v[p].y), __float_as_uint(v[p].z),
+                              __float_as_uint(v[p].w)};
+    uint32_t sc;
+    const uint32_t packed = quant_block8<F>(bits, &sc);
+    if (task < tasks) {
+      const int m = task / nb, b = task % nb;
+      if constexpr (F::MB == 1)
+        *reinterpret_cast<uint16_t*>(codes + (size_t)m * (K / 2) + 16 * b + 2 * j) = (uint16_t)packed;
+      else
+        *reinterpret_cast<uint32_t*>(codes + (size_t)m * K + 32 * b + 4 * j) = packed;
+      if (j == 0) scales[m * nb + b] = (uint8_t)sc;
     }
-  } while (keep_polling(ok, t0, A.sync));
+  }
 }
 
-// Re-quantizes the fp32 intermediate rows of one down unit into LDS (row m of
-// the staged block = routed slot tl[dd][m], or shared row m): codes [n, K/2]
-// (FP4) or [n, K] (FP8), scales [n, K/32].
-template <class F, class Src>
-__device__ __forceinline__ void stage_intermediate(const Src* src, int K, int n, const uint8_t* slots,
-                                                   uint8_t* codes, uint8_t* scales) {
-  const int nb = K / 32, tasks = n * nb;
-  const int j = threadIdx.x & 7;
-  for (int t0 = 0; t0 < tasks; t0 += 4 * (kThreads / 8)) {
+// Routed intermediate: the tagged SwiGLU values of slots[0..n) (row stride
+// K), polled pass by pass until every word of the pass carries this call's
+// tag, then quantized to MXFP4.
+template <class DA>
+__device__ __forceinline__ void stage_routed(const DA& A, uint32_t tag, int K, int n, const uint8_t* slots,
+                                             uint8_t* codes, uint8_t* scales) {
+  const int nb = K / 32, tasks = n * nb, j = threadIdx.x & 7;
+  const uint64_t tw = wall_clock64();
+  for (int t0 = 0; t0 < tasks; t0 += kStagePass) {
+    float4 v[4];
+    bool ok;
+    do {
+      ok = true;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int task = t0 + p * (kThreads / 8) + (int)threadIdx.x / 8;
+        v[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (task < tasks) {
+          const uint64_t* src = A.a_r + (size_t)slots[task / nb] * K + 32 * (task % nb) + 4 * j;
+          const uint64_t w0 = ld_dev(src), w1 = ld_dev(src + 1), w2 = ld_dev(src + 2), w3 = ld_dev(src + 3);
+          ok &= tag_ok(w0, tag) & tag_ok(w1, tag) & tag_ok(w2, tag) & tag_ok(w3, tag);
+          v[p] = make_float4(__uint_as_float((uint32_t)w0), __uint_as_float((uint32_t)w1),
+                             __uint_as_float((uint32_t)w2), __uint_as_float((uint32_t)w3));
+        }
+      }
+    } while (keep_polling(ok, tw, A.sync));
+    stage_quantize<FP4>(v, t0, tasks, K, codes, scales);
+  }
+}
+
+// Shared intermediate: SwiGLU of the tagged gate and up sums of a_s (row
+// stride 2K: gate columns, then up columns), polled pass by pass until every
+// word of the pass carries this call's tag, then quantized to MXFP8.
+template <class DA>
+__device__ __forceinline__ void stage_shared(const DA& A, uint32_t tag, int K, uint8_t* codes, uint8_t* scales) {
+  const int nb = K / 32, tasks = A.T * nb, j = threadIdx.x & 7;
+  const uint64_t tw = wall_clock64();
+  for (int t0 = 0; t0 < tasks; t0 += kStagePass) {
+    float g[4][4], u[4][4];
+    bool ok;
+    do {
+      ok = true;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int task = t0 + p * (kThreads / 8) + (int)threadIdx.x / 8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) g[p][i] = u[p][i] = 0.f;
+        if (task < tasks) {
+          const uint64_t* src = A.a_s + (size_t)(task / nb) * (2 * K) + 32 * (task % nb) + 4 * j;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint64_t wg = ld_dev(src + i), wu = ld_dev(src + K + i);
+            ok &= tag_ok(wg, tag) & tag_ok(wu, tag);
+            g[p][i] = __uint_as_float((uint32_t)wg);
+            u[p][i] = __uint_as_float((uint32_t)wu);
+          }
+        }
+      }
+    } while (keep_polling(ok, tw, A.sync));
     float4 v[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {  // all loads first
-      const int task = t0 + p * (kThreads / 8) + (int)threadIdx.x / 8;
-      v[p] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (task < tasks) {
-        const int m = task / nb, b = task % nb;
-        const int row = slots ? slots[m] : m;
-        v[p] = load4(src + (size_t)row * K + 32 * b + 4 * j);
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int task = t0 + p * (kThreads / 8) + (int)threadIdx.x / 8;
-      if (t0 + p * (kThreads / 8) >= tasks) break;  // uniform: whole pass beyond the end
-      const uint32_t bits[4] = {__float_as_uint(v[p].x), __float_as_uint(v[p].y), __float_as_uint(v[p].z),
-                                __float_as_uint(v[p].w)};
-      uint32_t sc;
-      const uint32_t packed = quant_block8<F>(bits, &sc);
-      if (task < tasks) {
-        const int m = task / nb, b = task % nb;
-        if constexpr (F::MB == 1)
-          *reinterpret_cast<uint16_t*>(codes + (size_t)m * (K / 2) + 16 * b + 2 * j) = (uint16_t)packed;
-        else
-          *reinterpret_cast<uint32_t*>(codes + (size_t)m * K + 32 * b + 4 * j) = packed;
-        if (j == 0) scales[m * nb + b] = (uint8_t)sc;
-      }
-    }
+    for (int p = 0; p < 4; ++p)
+      v[p] = make_float4(silu_mul(g[p][0], u[p][0]), silu_mul(g[p][1], u[p][1]), silu_mul(g[p][2], u[p][2]),
+                         silu_mul(g[p][3], u[p][3]));
+    stage_quantize<FP8>(v, t0, tasks, K, codes, scales);
   }
 }
 
@@ -753,7 +770,6 @@ __device__ __forceinline__ void run_entry(const DA& A, uint32_t tag, Smem& sm, c
     gu_compute(A, sm, xq4_lds, xs4_lds, dd, buf, lane, wave);
     if (j == 0) trace_at(A, TR_B_MMA);
     issue(A, sm, S, j + kBufs, lane, wave, buf);  // buf is free once the matrix products have read it
-    if (j == 0) trace_at(A, TR_B_NEXT);
     __syncthreads();
     int row, col;
     float a;
@@ -764,10 +780,10 @@ __device__ __forceinline__ void run_entry(const DA& A, uint32_t tag, Smem& sm, c
     if (j == 0) trace_at(A, TR_B_RELEASED);
     return;
   }
-  const int u = S.c0 + j - S.nb;
-  const bool routed = u < S.D * S.nhg;
-  const int dd = routed ? u / S.nhg : -1;
-  const int hg = routed ? u % S.nhg : u - S.D * S.nhg;  // 64-column group
+  const int u = S.c0 + j - S.nb;  // shared down units first, then routed
+  const bool routed = u >= S.ns;
+  const int dd = routed ? (u - S.ns) / S.nhg : -1;
+  const int hg = routed ? (u - S.ns) % S.nhg : u;  // 64-column group
   const int hs = 4 * hg + wave;
   const int m = lane & 15, q = lane >> 4;
   v4f out;
@@ -777,8 +793,7 @@ __device__ __forceinline__ void run_entry(const DA& A, uint32_t tag, Smem& sm, c
     uint8_t* codes = stage;
     uint8_t* scales = stage + kDecodeMaxT * (K / 2);
     if (sm.staged != e) {
-      wait_tagged_rows(A, tag, A.a_r, K, n, sm.tl[dd]);
-      stage_intermediate<FP4>(A.a_r, K, n, sm.tl[dd], codes, scales);
+      stage_routed(A, tag, K, n, sm.tl[dd], codes, scales);
       __syncthreads();
       if (threadIdx.x == 0) sm.staged = e;
       if (j == S.nb) trace_at(A, TR_C_STAGED);
@@ -797,8 +812,7 @@ __device__ __forceinline__ void run_entry(const DA& A, uint32_t tag, Smem& sm, c
     uint8_t* codes = stage;
     uint8_t* scales = stage + kDecodeMaxT * K;
     if (sm.staged != -1) {
-      wg_wait(ctr(A.sync, S_SA), (uint32_t)(A.is() / 16), A.sync);
-      stage_intermediate<FP8>(A.a_s, K, A.T, static_cast<const uint8_t*>(nullptr), codes, scales);
+      stage_shared(A, tag, K, codes, scales);
       __syncthreads();
       if (threadIdx.x == 0) sm.staged = -1;
     }
@@ -816,35 +830,51 @@ __device__ __forceinline__ void run_entry(const DA& A, uint32_t tag, Smem& sm, c
 // ------------------------------------------------------------------ kernel
 template <class DA>
 __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
+  const uint64_t t_entry = wall_clock64();
   __shared__ Smem sm;
-  extern __shared__ __align__(16) unsigned char dyn[];  // logits, then MXFP4 x; staged intermediates
+  extern __shared__ __align__(16) unsigned char dyn[];
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int G = A.G, T = A.T, E = A.e();
   const uint32_t tag = ld_dev(ctr(A.sync, S_EPOCH)) + 1u;
   uint64_t* tr = A.trace + (size_t)blockIdx.x * kTraceWords;
   if (threadIdx.x == 0) {
-    tr[TR_START] = wall_clock64();
-    for (int i = 1; i < kTraceWords; ++i) tr[i] = 0;
+    tr[TR_START] = t_entry;
+    for (int i = 1; i < kTraceWords - 1; ++i) tr[i] = 0;
+    wait_vm<0>();
+    tr[TR_TAG] = wall_clock64() + (tag == 0u ? 1u : 0u);
   }
 
-  // phase A
-  const int n_xq = xq_units(T, A.h(), A.is());
-  const int n_sgu = A.is() ? A.is() / 16 : 0;
-  for (int u = blockIdx.x; u < n_xq + E + n_sgu; u += G) {
-    if (u < n_xq)
-      unit_xq(A, u);
-    else if (u < n_xq + E)
-      unit_router(A, tag, u - n_xq, lane, wave);
-    else
-      unit_shared_gu(A, sm, u - n_xq - E, lane, wave);
+  // dynamic LDS: logits, the MXFP4 x, then the MXFP8 x of a shared strip
+  // (phase A) or the staged down-unit intermediate (later)
+  float* logits_lds = reinterpret_cast<float*>(dyn);
+  uint8_t* xq4_lds = dyn + align_up((size_t)kDecodeMaxT * E * 4, 16);
+  uint8_t* xs4_lds = xq4_lds + (size_t)T * (A.h() / 2);
+  uint8_t* stage = xq4_lds + align_up((size_t)kDecodeMaxT * (A.h() / 2 + A.h() / 32), 16);
+  uint8_t* x8_lds = stage;
+
+  // phase A: router units, then shared gate/up strips, strided over the grid.
+  // A strip leaves the MXFP4 copy of x in LDS; other workgroups make it after.
+  if (threadIdx.x == 0) sm.staged = -2;
+  const int n_ss = A.is() ? 2 * A.is() / 16 : 0;
+  bool have_x4 = false;
+  for (int u = blockIdx.x; u < E + n_ss; u += G) {
+    if (u < E) {
+      unit_router(A, tag, u, lane, wave);
+    } else {
+      unit_shared_strip(A, tag, sm, u - E, x8_lds, xq4_lds, xs4_lds, lane, wave);
+      have_x4 = true;
+    }
     if (threadIdx.x == 0 && u == (int)blockIdx.x) tr[TR_FIRST] = wall_clock64();
+  }
+  if (!have_x4) {
+    quant_x_fp4(A, xq4_lds, xs4_lds);
+    trace_at(A, TR_XQ);
   }
   trace_at(A, TR_A);
   compiler_fence();
 
   // routing, identical in every workgroup: read the tagged logits until all
   // are this call's
-  float* logits_lds = reinterpret_cast<float*>(dyn);
   {
     const uint64_t t0 = wall_clock64();
     bool ok;
@@ -858,7 +888,6 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
     } while (keep_polling(ok, t0, A.sync));
   }
   trace_at(A, TR_LOGITS);
-  trace_at(A, TR_LOGITS_LDS);
   if (T <= kWaves) {  // a wavefront per row
     const int row = wave < T ? wave : 0;
     row_topk64(logits_lds + row * E, wave < T, E, A.kk(), lane, sm.ids + row * A.kk(), sm.w + row * A.kk());
@@ -871,20 +900,6 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
   trace_at(A, TR_TOPK);
   build_expert_list(A, sm, lane, wave);
   trace_at(A, TR_ELIST);
-  if (threadIdx.x == 0) {
-    wait_count(ctr(A.sync, S_XQ), (uint32_t)n_xq, A.sync);
-    sm.staged = -2;
-  }
-  __syncthreads();
-  compiler_fence();
-  uint8_t* xq4_lds = dyn;
-  uint8_t* xs4_lds = dyn + (size_t)T * (A.h() / 2);
-  {
-    const uint64_t* src = reinterpret_cast<const uint64_t*>(A.xq4);
-    uint64_t* dst = reinterpret_cast<uint64_t*>(xq4_lds);
-    for (int i = threadIdx.x; i < T * A.h() / 16; i += kThreads) dst[i] = ld_dev(src + i);
-    for (int i = threadIdx.x; i < T * A.h() / 32; i += kThreads) xs4_lds[i] = ld_dev(&A.xs4[i]);
-  }
   if (blockIdx.x == 0) {
     for (int i = threadIdx.x; i < T * A.kk(); i += kThreads) {
       if (A.ids_out) A.ids_out[i] = sm.ids[i];
@@ -898,16 +913,16 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
   Seq S;
   S.D = sm.D;
   S.nhg = A.h() / 64;
+  S.ns = A.is() ? S.nhg : 0;
   {
     const int NB = S.D * (A.i() / 16);
-    const int NCU = S.D * S.nhg + (A.is() ? S.nhg : 0);
+    const int NCU = S.ns + S.D * S.nhg;
     const unsigned b = blockIdx.x, g = (unsigned)G;  // products stay below 2^24
     S.b0 = (int)((unsigned)NB * b / g);
     S.nb = (int)((unsigned)NB * (b + 1) / g) - S.b0;
     S.c0 = (int)((unsigned)NCU * b / g);
     S.nc = (int)((unsigned)NCU * (b + 1) / g) - S.c0;
   }
-  uint8_t* stage = dyn + align_up((size_t)kDecodeMaxT * (A.h() / 2 + A.h() / 32), 16);
   const int total = S.nb + S.nc;
   Buf X, Y, Z;
   issue(A, sm, S, 0, lane, wave, X);
@@ -940,8 +955,6 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
     compiler_fence();
     if (old + 1 == (uint32_t)G) {
       st_dev(ctr(A.sync, S_EPOCH), tag);  // the next call's tag is one more
-      st_dev(ctr(A.sync, S_XQ), 0u);
-      st_dev(ctr(A.sync, S_SA), 0u);
       compiler_fence();
       wait_vm<0>();
       st_dev(ctr(A.sync, S_DONE), 0u);
@@ -952,7 +965,7 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
 // ------------------------------------------------------------------ host side
 struct Carve {
   size_t sync, sync_end;
-  size_t logits, xq4, xs4, xq8, xs8, a_r, a_s, d_part, s_part, trace, total;
+  size_t logits, a_r, a_s, d_part, s_part, trace, total;
 };
 
 Carve carve(const moe_layer_t& L) {
@@ -965,12 +978,8 @@ Carve carve(const moe_layer_t& L) {
   c.sync = take(kSyncLines * line);
   c.sync_end = o;
   c.logits = take(T * E * 8);
-  c.xq4 = take(T * H / 2);
-  c.xs4 = take(T * H / 32);
-  c.xq8 = take(T * H);
-  c.xs8 = take(T * H / 32);
   c.a_r = take(T * k * I * 8);
-  c.a_s = take(T * Is * 4 + 16);
+  c.a_s = take(T * 2 * Is * 8 + 16);
   c.d_part = take(T * k * H * 8);
   c.s_part = take(T * H * 8);
   c.trace = take((size_t)kDecodeMaxGrid * kTraceWords * 8);
@@ -978,14 +987,17 @@ Carve carve(const moe_layer_t& L) {
   return c;
 }
 
-// Dynamic LDS: max(logits, MXFP4 x) followed by the staged intermediate.
+// Dynamic LDS: logits, the MXFP4 x, then either the MXFP8 x of a shared strip
+// (phase A) or the staged intermediate.
 size_t dyn_lds_bytes(const moe_layer_t& L) {
   const size_t T = kDecodeMaxT;
-  const size_t logits = T * L.num_experts * 4;
+  const size_t logits = align_up(T * L.num_experts * 4, 16);
   const size_t xq = align_up(T * (L.hidden / 2 + L.hidden / 32), 16);
   const size_t st4 = T * (L.inter / 2 + L.inter / 32);
   const size_t st8 = T * ((size_t)L.shared_inter + L.shared_inter / 32);
-  return align_up(logits > xq ? logits : xq, 16) + align_up(st4 > st8 ? st4 : st8, 16);
+  const size_t st = align_up(st4 > st8 ? st4 : st8, 16);
+  const size_t x8 = L.shared_inter ? align_up(T * (L.hidden + L.hidden / 32), 16) : 0;
+  return logits + xq + (st > x8 ? st : x8);
 }
 
 template <class DA>
@@ -997,7 +1009,7 @@ int grid_size(size_t lds) {
   if (dev == cached_dev && lds == cached_lds) return cached_grid;
   int cus = 0, occ = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (lds > 64 * 1024 &&
+  if (lds + sizeof(Smem) > 64 * 1024 &&
       hipFuncSetAttribute(reinterpret_cast<const void*>(fused_decode_kernel<DA>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return 0;
@@ -1077,12 +1089,9 @@ hipError_t launch_decode(const moe_layer_t& L, const uint16_t* x, int T, const u
   A.w_out = w_out;
   A.sync = reinterpret_cast<uint32_t*>(base + c.sync);
   A.logits = reinterpret_cast<uint64_t*>(base + c.logits);
-  A.xq4 = reinterpret_cast<uint8_t*>(base + c.xq4);
-  A.xs4 = reinterpret_cast<uint8_t*>(base + c.xs4);
-  A.xq8 = reinterpret_cast<uint8_t*>(base + c.xq8);
-  A.xs8 = reinterpret_cast<uint8_t*>(base + c.xs8);
   A.a_r = reinterpret_cast<uint64_t*>(base + c.a_r);
-  A.a_s = reinterpret_cast<float*>(base + c.a_s);
+  A.a_s = reinterpret_cast<uint64_t*>(base + c.a_s);
+
   A.d_part = reinterpret_cast<uint64_t*>(base + c.d_part);
   A.s_part = reinterpret_cast<uint64_t*>(base + c.s_part);
   A.trace = reinterpret_cast<uint64_t*>(base + c.trace);

@@ -319,7 +319,8 @@ __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  /
         const uint32_t a1 = __float_as_uint(silu_mul(sum[i][1][r], sum[i][3][r]));
         const uint32_t am = row16_max32(max(a0 & 0x7fffffffu, a1 & 0x7fffffffu));
         const int ex = block_exponent<F>(am);
-        const uint32_t c0 = quant_elem<F>(a0, ex), c1 = quant_elem<F>(a1, ex);
+        const float inv = block_inv_scale(ex);
+        const uint32_t c0 = quant_elem_fast<F>(a0, inv), c1 = quant_elem_fast<F>(a1, inv);
         if constexpr (F::MB == 1) {
           const uint32_t n0 = row_move32(c0), n1 = row_move32(c1);
           if (valid && !(m & 1)) {

@@ -56,7 +56,7 @@ constexpr size_t kDecodeStatusOffset = 0;
 // Bytes of the counter region at the start of a decode workspace (zero at rest).
 size_t decode_sync_bytes(const moe_layer_t& L);
 size_t decode_trace_offset(const moe_layer_t& L);
-constexpr size_t kDecodeGridOffset = 4 * 256;  // word holding the grid size of the last call
+constexpr size_t kDecodeGridOffset = 2 * 256;  // word holding the grid size of the last call
 
 // ------------------------------------------------------------------ grouped path
 size_t grouped_ws_bytes(const moe_layer_t& L, int T);

@@ -32,39 +32,39 @@ __device__ __forceinline__ int block_exponent(uint32_t amax_bits) {
   return e < -127 ? -127 : e;
 }
 
-// Element code of v * 2^-e, v given as an fp32 bit pattern: round to nearest,
-// ties to the even code, saturate to MAXC, sign bit copied.  Integer-only, so
-// the result does not depend on the floating-point or denormal mode.
-//   |v| = M * 2^(Ev-150) (M the 24-bit significand), q = |v| * 2^-e,
-//   p = floor(log2 q); the element grid spacing is 2^qe with
-//   qe = max(p, EMIN) - MB; n = RNE(q / 2^qe);
-//   code = (max(p - EMIN, 0) << MB) + n  (a carry into the next binade is
-//   absorbed by the same formula).  The right shift s below is always >= 1
-//   for e >= -127.
+// 2^-e as an fp32 value (e = block exponent, -127 <= e <= 126).
+__device__ __forceinline__ float block_inv_scale(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+
+// Element code of v * 2^-e (v an fp32 bit pattern, inv = block_inv_scale(e)):
+// round to nearest, ties to the even code, saturate to MAXC, sign bit copied
+// (also onto a zero code), with no branches.  q = |v| * 2^-e is exact whenever it is an fp32 normal (a power of
+// two scaling), and when it is not, q < 2^-126 lies far below the first
+// rounding threshold, so the code is 0 either way; q never overflows since
+// |v| <= amax < 2^(e + EMAX + 1).
+//   FP4 (E2M1, magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6): the code counts the
+//   midpoints q has passed; at a midpoint the comparison is strict where the
+//   lower neighbour's code is even and inclusive where the upper one's is, so
+//   ties go to the even code; above 5 (the last midpoint) it is 7, which also
+//   saturates.
+//   FP8 (E4M3): below 2^-6 the code is the subnormal count RNE(q * 2^9),
+//   rounded by adding and removing 2^23 in fp32 (round to nearest even); from
+//   2^-6 up, q's fp32 pattern rounded to 3 mantissa bits (ties to even, a
+//   carry moving into the exponent), re-biased from 127 to 7, saturated at
+//   0x7E (448).
 template <class F>
-__device__ __forceinline__ uint32_t quant_elem(uint32_t bits, int e) {
+__device__ __forceinline__ uint32_t quant_elem_fast(uint32_t bits, float inv) {
   const uint32_t sign = bits >> 31;
-  const uint32_t a = bits & 0x7fffffffu;
-  const int E = (int)(a >> 23);
-  uint32_t M = a & 0x7fffffu;
-  int Ev = 1;
-  if (E) { M |= 0x800000u; Ev = E; }
-  uint32_t code = 0;
-  if (M) {
-    const int msb = 31 - __clz(M);
-    const int p = msb + Ev - 150 - e;
-    const int pe = p > F::EMIN ? p : F::EMIN;
-    const int s = 150 + e + (pe - F::MB) - Ev;
-    uint32_t n = 0;
-    if (s < 32) {
-      n = M >> s;
-      const uint32_t rem = M & ((1u << s) - 1u);
-      const uint32_t half = 1u << (s - 1);
-      n += (rem > half) || (rem == half && (n & 1u));
-    }
-    const int base = p > F::EMIN ? p - F::EMIN : 0;
-    code = ((uint32_t)base << F::MB) + n;
-    if (code > (uint32_t)F::MAXC) code = F::MAXC;
+  const float q = __uint_as_float(bits & 0x7fffffffu) * inv;
+  uint32_t code;
+  if constexpr (F::MB == 1) {
+    code = (uint32_t)(q > 0.25f) + (uint32_t)(q >= 0.75f) + (uint32_t)(q > 1.25f) + (uint32_t)(q >= 1.75f) +
+           (uint32_t)(q > 2.5f) + (uint32_t)(q >= 3.5f) + (uint32_t)(q > 5.0f);
+  } else {
+    const uint32_t sub = (uint32_t)((q * 512.0f + 8388608.0f) - 8388608.0f);
+    const uint32_t b = __float_as_uint(q);
+    uint32_t nrm = ((b + 0x7ffffu + ((b >> 20) & 1u)) >> 20) - (120u << 3);
+    nrm = nrm > (uint32_t)F::MAXC ? (uint32_t)F::MAXC : nrm;
+    code = q < 0.015625f ? sub : nrm;
   }
   return code | (sign << F::SIGN);
 }
@@ -87,12 +87,13 @@ __device__ __forceinline__ uint32_t quant_block32(const uint32_t* bits, uint32_t
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = max(amax, bits[i] & 0x7fffffffu);
   const int e = block_exponent<F>(amax);
+  const float inv = block_inv_scale(e);
   if constexpr (F::MB == 1) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       uint32_t word = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) word |= quant_elem<F>(bits[8 * w + i], e) << (4 * i);
+      for (int i = 0; i < 8; ++i) word |= quant_elem_fast<F>(bits[8 * w + i], inv) << (4 * i);
       out_words[w] = word;
     }
   } else {
@@ -100,7 +101,7 @@ __device__ __forceinline__ uint32_t quant_block32(const uint32_t* bits, uint32_t
     for (int w = 0; w < 8; ++w) {
       uint32_t word = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) word |= quant_elem<F>(bits[4 * w + i], e) << (8 * i);
+      for (int i = 0; i < 4; ++i) word |= quant_elem_fast<F>(bits[4 * w + i], inv) << (8 * i);
       out_words[w] = word;
     }
   }
@@ -239,48 +240,77 @@ __device__ __forceinline__ uint64_t row16_max64(uint64_t v) {
   return v;
 }
 
-// Maximum over the whole wavefront, returned uniform: row maxima, then
-// lane 15 of rows 0 and 2 folded into rows 1 and 3, then lane 31 into rows 2
-// and 3; lane 63 ends with the maximum.
-__device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
-  v = row16_max64(v);
-  {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v, 0x142, 0xA, 0xF, false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), 0x142, 0xA, 0xF, false);
-    v = max_u64(v, ((uint64_t)hi << 32) | lo);
-  }
-  {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v, 0x143, 0xC, 0xF, false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), 0x143, 0xC, 0xF, false);
-    v = max_u64(v, ((uint64_t)hi << 32) | lo);
-  }
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-  return ((uint64_t)hi << 32) | lo;
+// Order-preserving 32-bit image of a logit (-0 counted as +0): a larger
+// image means a larger logit, and 0 is below every image.
+__device__ __forceinline__ uint32_t logit_order_bits(float logit) {
+  const uint32_t b = __float_as_uint(logit + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float logit_from_order_bits(uint32_t b) {
+  return __uint_as_float((b & 0x80000000u) ? (b & 0x7fffffffu) : ~b);
+}
+
+// Maximum over the wavefront, returned uniform: each step moves a value with
+// one data-parallel permutation (swap neighbours, swap pairs, mirror each half
+// row, mirror the row, then lane 15 of rows 0/2 into rows 1/3 and lane 31
+// into rows 2/3); lane 63 ends with the maximum.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Top k of one row of E <= 256 logits on a whole wavefront (lane l holds the
-// keys of experts l, l+64, ...); same result and outputs as rows_topk16 (lane
-// 0 writes).  Every lane of the wavefront must call it; k is uniform.
+// logits of experts l, l+64, ...); same result and outputs as rows_topk16.
+// Each of the k rounds takes the wavefront maximum of the 32-bit logit images
+// and, among the experts holding it, the lowest index (first set bit of the
+// ballots, expert l + 64 r in r-major order), then retires that expert.  Lane j
+// keeps round j's logit; the weights are formed in parallel with the sum taken
+// in j order, as topk_weights_inplace does.  Lanes j < k of an active row
+// write ids[j] and w[j].  Every lane must call it; k is uniform.
 __device__ __forceinline__ void row_topk64(const float* logits_row, bool active, int E, int k, int lane,
                                            int32_t* ids, float* w) {
-  uint64_t key[4];
+  uint32_t kv[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int e = lane + 64 * r;
-    key[r] = (active && e < E) ? topk_key(logits_row[e], e) : 0ull;
+    kv[r] = (active && e < E) ? logit_order_bits(logits_row[e]) : 0u;
   }
-#pragma unroll 1
-  for (int j = 0; j < k; ++j) {
-    const uint64_t m = wave_max64(max_u64(max_u64(key[0], key[1]), max_u64(key[2], key[3])));
+  float my_l = 0.f;
+  int my_e = 0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) key[r] = key[r] == m ? 0ull : key[r];
-    if (active && lane == 0) {
-      ids[j] = topk_key_expert(m);
-      w[j] = topk_key_logit(m);
+  for (int j = 0; j < kTopkMax; ++j) {
+    if (j < k) {
+      const uint32_t m = wave_max_u32(max(max(kv[0], kv[1]), max(kv[2], kv[3])));
+      int best = -1;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint64_t bal = __ballot(kv[r] == m);
+        if (best < 0 && bal != 0ull) best = 64 * r + (__ffsll((unsigned long long)bal) - 1);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (lane + 64 * r == best) kv[r] = 0u;
+      if (lane == j) {
+        my_l = logit_from_order_bits(m);
+        my_e = best;
+      }
     }
   }
-  if (active && lane == 0) topk_weights_inplace(w, k);
+  const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_l), 0));
+  const float z = expf(my_l - l0);
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < kTopkMax; ++j)
+    if (j < k) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), j));
+  if (active && lane < k) {
+    ids[lane] = my_e;
+    w[lane] = z / sum;
+  }
 }
 
 // Top k of one row of E <= 256 logits on the 16 lanes of a row: lane `sub`
