@@ -466,14 +466,31 @@ struct Seq {
 
 struct Buf {
   v4i q[kBufQuads];
-  uint32_t w[kBufWords];
+  // scale words as separate members: every index below is a constant once
+  // the loops are unrolled, and an array here has ended up in scratch memory
+  uint32_t w0, w1, w2, w3, w4, w5;
+  __device__ __forceinline__ uint32_t& w(int i) {
+    switch (i) {
+      case 0: return w0;
+      case 1: return w1;
+      case 2: return w2;
+      case 3: return w3;
+      case 4: return w4;
+      default: return w5;
+    }
+  }
+  __device__ __forceinline__ uint32_t w(int i) const { return const_cast<Buf*>(this)->w(i); }
 };
 
 // Requests the weight tiles and scale words of sequence entry j into buf.
+// The scale words are gathered in scalars and stored to buf once, on a single
+// path: stores to different members on different paths get merged into one
+// store through a pointer, which keeps buf in scratch memory.
 template <class DA>
 __device__ __forceinline__ void issue(const DA& A, const Smem& sm, const Seq& S, int j, int lane, int wave,
                                       Buf& buf) {
   if (j >= S.nb + S.nc) return;
+  uint32_t n0 = 0, n1 = 0, n2 = 0, n3 = 0, n4 = 0, n5 = 0;
   if (j < S.nb) {
     if (wave >= A.nc1()) return;
     const int u = S.b0 + j;
@@ -482,46 +499,55 @@ __device__ __forceinline__ void issue(const DA& A, const Smem& sm, const Seq& S,
     const int CT = A.ct1(), KG = (A.kt1() + 3) / 4, t0 = wave * CT;
     const uint8_t* base = A.w13 + (size_t)e * ((size_t)A.i() * A.h());
     const uint8_t* sbase = A.w13s + (size_t)e * ((size_t)(2 * A.i() / 16) * KG * 256);
+    const int st0 = i, st1 = A.i() / 16 + i;
+    const uint8_t* wb0 = base + ((size_t)st0 * A.kt1() + t0) * 1024 + lane * 16;
+    const uint8_t* wb1 = base + ((size_t)st1 * A.kt1() + t0) * 1024 + lane * 16;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int st = s == 0 ? i : A.i() / 16 + i;
-      const uint8_t* wb = base + ((size_t)st * A.kt1() + t0) * 1024 + lane * 16;
+    for (int jj = 0; jj < kMaxCT; ++jj)
+      if (jj < CT) buf.q[jj] = load_stream16(wb0 + jj * 1024);
 #pragma unroll
-      for (int jj = 0; jj < kMaxCT; ++jj)
-        if (jj < CT) buf.q[kMaxCT * s + jj] = load_stream16(wb + jj * 1024);
-      const uint8_t* sp = sbase + ((size_t)st * KG * 64 + lane) * 4;
-#pragma unroll
-      for (int g = 0; g < 3; ++g)
-        buf.w[3 * s + g] = load_stream4(sp + (size_t)min(t0 / 4 + g, KG - 1) * 256);
+    for (int jj = 0; jj < kMaxCT; ++jj)
+      if (jj < CT) buf.q[kMaxCT + jj] = load_stream16(wb1 + jj * 1024);
+    const uint8_t* sp0 = sbase + ((size_t)st0 * KG * 64 + lane) * 4;
+    const uint8_t* sp1 = sbase + ((size_t)st1 * KG * 64 + lane) * 4;
+    n0 = load_stream4(sp0 + (size_t)min(t0 / 4, KG - 1) * 256);
+    n1 = load_stream4(sp0 + (size_t)min(t0 / 4 + 1, KG - 1) * 256);
+    n2 = load_stream4(sp0 + (size_t)min(t0 / 4 + 2, KG - 1) * 256);
+    n3 = load_stream4(sp1 + (size_t)min(t0 / 4, KG - 1) * 256);
+    n4 = load_stream4(sp1 + (size_t)min(t0 / 4 + 1, KG - 1) * 256);
+    n5 = load_stream4(sp1 + (size_t)min(t0 / 4 + 2, KG - 1) * 256);
+  } else {
+    // down units: both kinds load 1 KB weight blocks at a 1 KB stride (a
+    // routed FP4 tile is one block, a shared FP8 tile two) and two scale words
+    const int u = S.c0 + j - S.nb;
+    const uint8_t *wb, *sp;
+    int nq, KG;
+    if (u >= S.ns) {
+      const int ur = u - S.ns;
+      const int e = sm.elist[ur / S.nhg], hs = 4 * (ur % S.nhg) + wave;
+      KG = (A.kt2() + 3) / 4;
+      nq = min(A.kt2(), kDownBatch);
+      wb = A.w2 + (size_t)e * ((size_t)A.h() * A.i() / 2) + (size_t)hs * A.kt2() * 1024 + lane * 16;
+      sp = A.w2s + (size_t)e * ((size_t)(A.h() / 16) * KG * 256) + ((size_t)hs * KG * 64 + lane) * 4;
+    } else {
+      const int hs = 4 * u + wave;
+      KG = (A.kts() + 3) / 4;
+      nq = 2 * min(A.kts(), kDownBatch / 2);
+      wb = A.ws2 + (size_t)hs * A.kts() * 2048 + lane * 16;
+      sp = A.ws2s + ((size_t)hs * KG * 64 + lane) * 4;
     }
-    return;
-  }
-  const int u = S.c0 + j - S.nb;
-  if (u >= S.ns) {
-    const int ur = u - S.ns;
-    const int e = sm.elist[ur / S.nhg], hs = 4 * (ur % S.nhg) + wave;
-    const int KG = (A.kt2() + 3) / 4, nt = min(A.kt2(), kDownBatch);
-    const uint8_t* wb = A.w2 + (size_t)e * ((size_t)A.h() * A.i() / 2) + (size_t)hs * A.kt2() * 1024 + lane * 16;
 #pragma unroll
     for (int jj = 0; jj < kDownBatch; ++jj)
-      if (jj < nt) buf.q[jj] = load_stream16(wb + jj * 1024);
-    const uint8_t* sp = A.w2s + (size_t)e * ((size_t)(A.h() / 16) * KG * 256) + ((size_t)hs * KG * 64 + lane) * 4;
-#pragma unroll
-    for (int g = 0; g < 2; ++g) buf.w[g] = load_stream4(sp + (size_t)min(g, KG - 1) * 256);
-  } else {
-    const int hs = 4 * u + wave;
-    const int KG = (A.kts() + 3) / 4, nt = min(A.kts(), kDownBatch / 2);
-    const uint8_t* wb = A.ws2 + (size_t)hs * A.kts() * 2048 + lane * 16;
-#pragma unroll
-    for (int jj = 0; jj < kDownBatch / 2; ++jj)
-      if (jj < nt) {
-        buf.q[2 * jj] = load_stream16(wb + jj * 2048);
-        buf.q[2 * jj + 1] = load_stream16(wb + jj * 2048 + 1024);
-      }
-    const uint8_t* sp = A.ws2s + ((size_t)hs * KG * 64 + lane) * 4;
-#pragma unroll
-    for (int g = 0; g < 2; ++g) buf.w[g] = load_stream4(sp + (size_t)min(g, KG - 1) * 256);
+      if (jj < nq) buf.q[jj] = load_stream16(wb + jj * 1024);
+    n0 = load_stream4(sp);
+    n1 = load_stream4(sp + (size_t)min(1, KG - 1) * 256);
   }
+  buf.w0 = n0;
+  buf.w1 = n1;
+  buf.w2 = n2;
+  buf.w3 = n3;
+  buf.w4 = n4;
+  buf.w5 = n5;
 }
 
 // Routed gate/up: MFMA chain of this wave's K-chunk for both strips into
@@ -553,7 +579,7 @@ __device__ __forceinline__ void gu_compute(const DA& A, Smem& sm, const uint8_t*
     for (int jj = 0; jj < kMaxCT; ++jj)
       if (jj < CT) {
         const int kt = t0 + jj;
-        const uint32_t word = pick3(buf.w[3 * s], buf.w[3 * s + 1], buf.w[3 * s + 2], kt / 4 - t0 / 4);
+        const uint32_t word = pick3(buf.w(3 * s), buf.w(3 * s + 1), buf.w(3 * s + 2), kt / 4 - t0 / 4);
         acc = mfma_fp4(a[jj], buf.q[kMaxCT * s + jj], acc, sa[jj], scale_byte(word, kt));
       }
 #pragma unroll
@@ -682,7 +708,7 @@ __device__ __forceinline__ v4f down_compute(const uint8_t* w, const uint8_t* ws_
         }
 #pragma unroll
       for (int g = 0; g < 2; ++g)
-        buf.w[g] = load_stream4(ws_scale + (size_t)min(b0 / 4 + g, KG - 1) * 256);
+        buf.w(g) = load_stream4(ws_scale + (size_t)min(b0 / 4 + g, KG - 1) * 256);
     }
 #pragma unroll
     for (int jj = 0; jj < NB; ++jj) {
@@ -696,7 +722,7 @@ __device__ __forceinline__ v4f down_compute(const uint8_t* w, const uint8_t* ws_
           if (R == 2) a1 = *reinterpret_cast<const v4i*>(ap + 64);
           sa = scales[m * (K / 32) + 4 * kt + q];
         }
-        const uint32_t sb = scale_byte(buf.w[jj / 4], kt);
+        const uint32_t sb = scale_byte(buf.w(jj / 4), kt);
         if constexpr (F::MB == 1)
           acc = mfma_fp4(a0, buf.q[jj], acc, sa, sb);
         else
