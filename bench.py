@@ -8,9 +8,13 @@ Weights rotate over --rotate distinct layer instances (full expert sets, each
 step touches are not served from the 256 MB last-level cache.  The 16-row
 workload is measured the same way and reported beside it.
 
-Prints one JSON line.  `value` is the mean device time of one launch (HIP
-events recorded around every launch on the stream it runs on); `ms_per_step`
-is wall-clock time per step over the timed region.
+Prints one JSON line.  `value` is the device time per launch over the timed
+region: K launches issued back to back on one stream (as a decode step issues
+its layers), bracketed by a synchronize and HIP events recorded on that
+stream, divided by K; `ms_per_step` is the wall-clock time per step over the
+same region.  The same launches timed one at a time (an event pair around
+each, so every launch starts on an idle GPU) are reported beside it as
+`us_isolated_*`.
 """
 
 import argparse
@@ -74,7 +78,7 @@ def build_layers(binding, synth, name, count):
     return cfg, layers
 
 
-def time_decode(binding, synth, name, rotate, steps, warmup, pool=64):
+def time_decode(binding, synth, name, rotate, steps, warmup, pool=64, isolated=True):
     import torch
     cfg, layers = build_layers(binding, synth, name, rotate)
     T = cfg["T"]
@@ -99,41 +103,42 @@ def time_decode(binding, synth, name, rotate, steps, warmup, pool=64):
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        ev0[i].record(stream)
-        launch(warmup + i, ids[i], w[i])
-        ev1[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    dur_ms = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)])
-    # the same launches back to back (queue kept full): one event pair around all
+    # timed region: `steps` launches back to back, bracketed by synchronize
     b0 = torch.cuda.Event(enable_timing=True)
     b1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     b0.record(stream)
     for i in range(steps):
-        launch(warmup + steps + i)
+        launch(warmup + i, ids[i], w[i])
     b1.record(stream)
     torch.cuda.synchronize()
-    b2b_us = b0.elapsed_time(b1) * 1e3 / steps
+    wall = time.perf_counter() - t0
+    us_launch = b0.elapsed_time(b1) * 1e3 / steps
+    # the same kind of launches one at a time: an event pair around each
+    iso = np.full(1, np.nan)
+    if isolated:
+        ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for i in range(steps):
+            ev0[i].record(stream)
+            launch(warmup + steps + i)
+            ev1[i].record(stream)
+        torch.cuda.synchronize()
+        iso = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)]) * 1e3
     if binding.moe_decode_status(ws) != 0:
         raise RuntimeError("a device-side wait timed out during the benchmark")
     ids_np = ids.cpu().numpy()
     D = np.array([len(np.unique(ids_np[i])) for i in range(steps)])
     nbytes = np.array([layer_bytes(cfg["H"], cfg["I"], cfg["E"], cfg["I_s"], d, T) for d in D])
-    us = dur_ms * 1e3
-    gbs = nbytes / (us * 1e-6) / 1e9
     del layers
     torch.cuda.empty_cache()
     return {
-        "cfg": cfg, "us_mean": float(us.mean()), "us_median": float(np.median(us)),
-        "us_p10": float(np.percentile(us, 10)), "us_p90": float(np.percentile(us, 90)),
-        "wall_ms_per_step": wall / steps * 1e3, "bytes_mean": float(nbytes.mean()),
-        "gbs": float(nbytes.mean() / (us.mean() * 1e-6) / 1e9), "gbs_median": float(np.median(gbs)),
-        "distinct_experts_mean": float(D.mean()), "us_back_to_back": float(b2b_us),
+        "cfg": cfg, "us_launch": float(us_launch), "wall_ms_per_step": wall / steps * 1e3,
+        "bytes_mean": float(nbytes.mean()), "gbs": float(nbytes.mean() / (us_launch * 1e-6) / 1e9),
+        "distinct_experts_mean": float(D.mean()),
+        "us_isolated_mean": float(iso.mean()), "us_isolated_median": float(np.median(iso)),
+        "us_isolated_p10": float(np.percentile(iso, 10)), "us_isolated_p90": float(np.percentile(iso, 90)),
     }
 
 
@@ -237,6 +242,8 @@ def main():
     ap.add_argument("--no-16", action="store_true", help="skip the 16-row measurement")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 8192-row grouped measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-isolated", action="store_true",
+                    help="skip the one-launch-at-a-time timing (profiler runs: only back-to-back launches)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the measurement, run 5 plain elementwise copies (torch.neg, fp32) of this "
                          "many MiB: a kernel of known traffic that calibrates the HBM byte counters")
@@ -253,14 +260,17 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     binding.load()
-    r1 = time_decode(binding, synth, "decode1", args.rotate, args.steps, args.warmup)
-    print(f"[bench] 1 row: {r1['us_mean']:.2f} us mean, {r1['us_median']:.2f} us median, "
-          f"{r1['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    r1 = time_decode(binding, synth, "decode1", args.rotate, args.steps, args.warmup,
+                     isolated=not args.no_isolated)
+    print(f"[bench] 1 row: {r1['us_launch']:.2f} us per launch back to back ({r1['gbs']:.0f} GB/s); "
+          f"isolated launches {r1['us_isolated_mean']:.2f} us mean", file=sys.stderr, flush=True)
     r16 = None
     if not args.no_16:
-        r16 = time_decode(binding, synth, "decode16", max(4, args.rotate // 2), args.steps, args.warmup)
-        print(f"[bench] 16 rows: {r16['us_mean']:.2f} us mean, {r16['gbs']:.0f} GB/s, "
-              f"D={r16['distinct_experts_mean']:.1f}", file=sys.stderr, flush=True)
+        r16 = time_decode(binding, synth, "decode16", max(4, args.rotate // 2), args.steps, args.warmup,
+                          isolated=not args.no_isolated)
+        print(f"[bench] 16 rows: {r16['us_launch']:.2f} us per launch back to back, {r16['gbs']:.0f} GB/s, "
+              f"D={r16['distinct_experts_mean']:.1f}; isolated {r16['us_isolated_mean']:.2f} us",
+              file=sys.stderr, flush=True)
     rp = None
     if not args.no_prefill:
         rp = time_grouped(binding, synth)
@@ -280,7 +290,7 @@ def main():
     traffic = load_traffic("decode1")
     out = {
         "metric": "fused MXFP4 MoE layer us at 1/16 rows; achieved HBM GB/s and % roofline",
-        "value": round(r1["us_mean"], 3),
+        "value": round(r1["us_launch"], 3),
         "unit": "us",
         "n_gpus": 1,
         "steps": args.steps,
@@ -295,19 +305,19 @@ def main():
                                "intermediate 1024, MXFP8 shared expert 1024, one launch per layer",
                    "rows": 1, "hidden": 3072, "experts": 128, "top_k": 4, "inter": 1024,
                    "shared_inter": 1024, "rotated_layer_instances": args.rotate},
-        "us_median": round(r1["us_median"], 3),
-        "us_p10": round(r1["us_p10"], 3),
-        "us_p90": round(r1["us_p90"], 3),
-        "us_back_to_back": round(r1["us_back_to_back"], 3),
+        "us_isolated_mean": round(r1["us_isolated_mean"], 3),
+        "us_isolated_median": round(r1["us_isolated_median"], 3),
+        "us_isolated_p10": round(r1["us_isolated_p10"], 3),
+        "us_isolated_p90": round(r1["us_isolated_p90"], 3),
         "roofline": {"bound": "hbm", "achieved": round(r1["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(r1["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": int(r1["bytes_mean"])},
     }
     if r16:
-        out["rows16"] = {"us_mean": round(r16["us_mean"], 3), "us_median": round(r16["us_median"], 3),
+        out["rows16"] = {"us_per_launch": round(r16["us_launch"], 3),
                          "gbs": round(r16["gbs"], 1), "frac": round(r16["gbs"] / HBM_PEAK_GBS, 4),
                          "distinct_experts_mean": round(r16["distinct_experts_mean"], 2),
-                         "us_back_to_back": round(r16["us_back_to_back"], 3),
+                         "us_isolated_mean": round(r16["us_isolated_mean"], 3),
                          "algorithmic_bytes_per_launch": int(r16["bytes_mean"]),
                          "ms_per_step": round(r16["wall_ms_per_step"], 5)}
     if rp:

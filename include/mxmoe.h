@@ -220,14 +220,16 @@ moe_status moe_decode_status(const void* ws, size_t ws_bytes);
 /*
  * Diagnostic (synchronizes the device): phase timestamps of the last fused
  * decode call on this workspace, in ticks of the device's 100 MHz constant
- * clock.  Workgroup g fills words [16g, 16g+16): launch start, its x-quant /
- * router / shared gate/up units done, all logits seen, routing known and x
- * staged, its routed gate/up units done (0 if it had none), its down units and
- * combines done, end of its first such unit (0 if it had none), logits in LDS,
- * top-k done, expert list done, then for its first routed gate/up unit: matrix
- * products done, results stored, next tiles in place, released; then its first
- * down unit's intermediate staged (0 where it had no such unit), and the
- * time its first load (the call's epoch word) returned.
+ * clock.  Workgroup g fills words [16g, 16g+16): 0 launch start; 1 its
+ * router / shared gate/up units done; 2 all logits seen; 3 routing known; 4
+ * its routed gate/up units done (0 if it had none); 5 its down units and
+ * combines done; 6 end of its first router or shared unit (0 if it had none);
+ * 7 its MXFP4 (and, in a shared unit, MXFP8) copy of x in LDS; 8 top-k done;
+ * 9 expert list done; for its first routed gate/up unit 10 matrix products
+ * done and 11 results stored; 12 a shared unit's matrix products done; 13 its
+ * first routed gate/up unit released; 14 its first down unit's intermediate
+ * staged (0 where it had no such unit); 15 the time its first load (the
+ * call's epoch word) returned.
  * Copies at most n_words words to host memory and returns
  * the number of workgroups of that call (0 if none ran yet), or a negative
  * moe_status.
