@@ -388,7 +388,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(int T, int k, int H, 
 int pick_chunk(int tiles) { return tiles / (tiles % 4 == 0 ? 4 : (tiles % 2 == 0 ? 2 : 1)); }
 
 struct GCarve {
-  size_t ids, w, sort_ws, sorted, bexp, eoff, npad, xq4, xs4, xq8, xs8, a4, as4, a8, as8, d_part, total;
+  size_t ids, w, logits, sort_ws, sorted, bexp, eoff, npad, xq4, xs4, xq8, xs8, a4, as4, a8, as8, d_part, total;
   size_t cap, nblk;
 };
 
@@ -403,6 +403,7 @@ GCarve gcarve(const moe_layer_t& L, int T) {
   auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, 256); return at; };
   c.ids = take(S * 4);
   c.w = take(S * 4);
+  c.logits = router_tiled(T) ? take((size_t)T * E * 4) : 0;
   c.sort_ws = take(align_sort_ws_bytes(T, (int)k, (int)E));
   c.sorted = take(rows * 4);
   c.bexp = take(c.nblk * 4);
@@ -460,7 +461,8 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
   uint8_t* as4 = reinterpret_cast<uint8_t*>(at(c.as4));
   float* d_part = reinterpret_cast<float*>(at(c.d_part));
   hipError_t err;
-  if ((err = launch_router_topk(L, x, T, nullptr, ids, w, stream)) != hipSuccess) return err;
+  if ((err = launch_router_topk(L, x, T, router_tiled(T) ? reinterpret_cast<float*>(at(c.logits)) : nullptr, ids, w,
+                               stream)) != hipSuccess) return err;
   if ((err = launch_align_sort(ids, T, k, E, kBM, sorted, bexp, reinterpret_cast<int32_t*>(at(c.eoff)), npad,
                                at(c.sort_ws), stream)) != hipSuccess)
     return err;

@@ -30,6 +30,10 @@ hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int fmt, uint
 hipError_t launch_fill_u32(void* p, size_t words, uint32_t value, hipStream_t stream);
 
 // ------------------------------------------------------------------ router
+// From this many rows on, a call that keeps the logits takes the tiled logits
+// kernel and a separate top-k pass (same arithmetic, identical results).
+constexpr int kRouterTiledMinT = 64;
+bool router_tiled(int T);
 hipError_t launch_router_topk(const moe_layer_t& L, const uint16_t* x, int T, float* logits,
                               int32_t* ids, float* w, hipStream_t stream);
 

@@ -1,7 +1,9 @@
 // Router logits and top-k for any number of rows (used on its own and by the
-// grouped path).  A workgroup takes a group of rows, keeps them in LDS, computes
-// the E logits of each row with the fixed-order dot product of mx_device.h and
-// then 16 lanes per row select the top k.
+// grouped path).  For a few rows a workgroup takes a group of rows, keeps them
+// in LDS, computes the E logits of each row with the fixed-order dot product of
+// mx_device.h and then 16 lanes per row select the top k.  For many rows a
+// register-tiled kernel writes the logits with the same arithmetic and a second
+// pass selects the top k.
 #include "internal.h"
 #include "mx_device.h"
 
@@ -85,11 +87,125 @@ __global__ void __launch_bounds__(kThreads) router_topk_kernel(
   }
 }
 
+
+// ------------------------------------------------------------------ many rows
+// Logits for many rows with the same per-logit arithmetic, organized for
+// throughput: a wavefront owns a tile of 16 rows x 8 experts and keeps its
+// 128 partial sums in registers, so each loaded x value feeds 8 FMAs and each
+// loaded weight 16.  Lane l visits h = 256 i + 4 l + c (i ascending, c =
+// 0..3) for every (row, expert) of the tile, exactly as router_lane_partial
+// does for one pair.  The 64 lanes' partial sums are then added by a halving
+// exchange: at lane distance d (32, 16, ..., 1) each lane keeps one half of
+// its values and adds its partner's copy of that half, so every sum it forms
+// is the sum the butterfly forms at that distance (same two operands), and
+// lane l ends with the finished logits of tile entries 2l and 2l + 1.
+constexpr int kTileRows = 16;
+constexpr int kTileExperts = 8;   // per wavefront
+constexpr int kTileVals = kTileRows * kTileExperts;
+
+__global__ void __launch_bounds__(kThreads, 2) router_logits_tiled_kernel(
+    const uint16_t* __restrict__ x, int T, int H, int E, const float* __restrict__ wr,
+    const float* __restrict__ bias, float* __restrict__ logits, int n_rblk, int n_eblk) {
+  // workgroups are dealt to the 8 XCDs in turn; renumber so that each XCD
+  // takes a contiguous run of tiles (the expert groups of one row block share
+  // that XCD's L2)
+  const int per = gridDim.x / 8;
+  const int tile = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (tile >= n_rblk * n_eblk) return;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int t0 = (tile / n_eblk) * kTileRows;
+  const int e0 = (tile % n_eblk) * (kTileExperts * kWaves) + wave * kTileExperts;
+  if (e0 >= E) return;
+  const uint16_t* xr[kTileRows];
+#pragma unroll
+  for (int r = 0; r < kTileRows; ++r) xr[r] = x + (size_t)min(t0 + r, T - 1) * H;
+  const float* wp[kTileExperts];
+#pragma unroll
+  for (int e = 0; e < kTileExperts; ++e) wp[e] = wr + (size_t)min(e0 + e, E - 1) * H;
+
+  float acc[kTileVals];
+#pragma unroll
+  for (int s = 0; s < kTileVals; ++s) acc[s] = 0.f;
+  for (int h = 4 * lane; h < H; h += 256) {  // a lane past the end of a partial stride does nothing
+    uint2 xv[kTileRows];
+    float4 wv[kTileExperts];
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) xv[r] = *reinterpret_cast<const uint2*>(xr[r] + h);
+#pragma unroll
+    for (int e = 0; e < kTileExperts; ++e) wv[e] = *reinterpret_cast<const float4*>(wp[e] + h);
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) {
+      const float x0 = bf16_to_f32(xv[r].x & 0xffffu), x1 = bf16_to_f32(xv[r].x >> 16);
+      const float x2 = bf16_to_f32(xv[r].y & 0xffffu), x3 = bf16_to_f32(xv[r].y >> 16);
+#pragma unroll
+      for (int e = 0; e < kTileExperts; ++e) {
+        float& a = acc[r * kTileExperts + e];
+        a = fmaf(x0, wv[e].x, a);
+        a = fmaf(x1, wv[e].y, a);
+        a = fmaf(x2, wv[e].z, a);
+        a = fmaf(x3, wv[e].w, a);
+      }
+    }
+  }
+  // halving exchange: before distance d the lane holds 2d values (entries
+  // whose higher index bits equal its lane bits above d); it keeps the upper
+  // half if lane & d, the lower half otherwise
+#pragma unroll
+  for (int d = 32, half = kTileVals / 2; d >= 1; d >>= 1, half >>= 1) {
+    const bool up = (lane & d) != 0;
+#pragma unroll
+    for (int s = 0; s < half; ++s) {
+      const float lo = acc[s], hi = acc[s + half];
+      const float send = up ? lo : hi;
+      const float keep = up ? hi : lo;
+      acc[s] = keep + __shfl_xor(send, d);
+    }
+  }
+  // lane l: entries 2l, 2l + 1 = row l / 4, experts 2 (l % 4) + j
+  const int t = t0 + lane / 4;
+  if (t < T) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int e = e0 + 2 * (lane % 4) + j;
+      if (e < E) {
+        float v = acc[j];
+        if (bias) v = v + bias[e];
+        logits[(size_t)t * E + e] = v;
+      }
+    }
+  }
+}
+
+// Top k of each row of a logits matrix: 16 lanes per row.
+__global__ void __launch_bounds__(kThreads) topk_rows_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                             int32_t* __restrict__ ids_out,
+                                                             float* __restrict__ w_out) {
+  const int r = blockIdx.x * (kThreads / 16) + (int)threadIdx.x / 16;
+  const bool act = r < T;
+  const int rr = act ? r : T - 1;
+  rows_topk16(logits + (size_t)rr * E, act, E, k, threadIdx.x & 15, ids_out + (size_t)rr * k,
+              w_out + (size_t)rr * k);
+}
+
 }  // namespace
+
+bool router_tiled(int T) { return T >= kRouterTiledMinT; }
 
 hipError_t launch_router_topk(const moe_layer_t& L, const uint16_t* x, int T, float* logits,
                               int32_t* ids, float* w, hipStream_t stream) {
   const int H = L.hidden, E = L.num_experts;
+  if (logits && router_tiled(T)) {
+    const int n_rblk = (T + kTileRows - 1) / kTileRows;
+    const int n_eblk = (E + kTileExperts * kWaves - 1) / (kTileExperts * kWaves);
+    const unsigned grid = (unsigned)((n_rblk * n_eblk + 7) / 8 * 8);
+    hipLaunchKernelGGL(router_logits_tiled_kernel, dim3(grid), dim3(kThreads), 0, stream, x, T, H, E,
+                       L.router_w, L.router_bias, logits, n_rblk, n_eblk);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)((T + 15) / 16)), dim3(kThreads), 0, stream, logits, T, E,
+                       L.top_k, ids, w);
+    return hipGetLastError();
+  }
   int rows = 65536 / H;
   rows = rows < 1 ? 1 : (rows > kRouterRows ? kRouterRows : rows);
   const size_t lds = align_up((size_t)rows * H * 2, 16) + (size_t)rows * E * 4;

@@ -96,3 +96,34 @@ def test_align_sort_all_to_one_expert():
     assert int(npad.cpu()[0]) == r_npad
     assert np.array_equal(slots.cpu().numpy()[:r_npad], r_slots)
     assert np.array_equal(offs.cpu().numpy(), r_offs)
+
+
+@pytest.mark.parametrize("H,E,k,T,with_bias", [(384, 40, 3, 77, True), (3072, 128, 4, 300, False)])
+def test_router_tiled_equals_rowwise(H, E, k, T, with_bias):
+    """From 64 rows on, a call that returns the logits takes the register-tiled
+    kernel (16-row x 32-expert workgroup tiles; here with a partial 256-wide
+    stride, a partial row tile and a partial expert tile).  Its logits must be
+    the per-row kernel's bit for bit, as both follow the documented order, and
+    lie within the fp32 bound of the oracle's."""
+    rng = np.random.default_rng(1000 * H + E + T)
+    wr_np = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    b_np = rng.standard_normal(E).astype(np.float32) if with_bias else None
+    wr = torch.from_numpy(wr_np).cuda()
+    bias = torch.from_numpy(b_np).cuda() if with_bias else None
+    dummy = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    layer = binding.MoELayer(H, 128, E, k, 0, wr, bias, dummy, dummy, dummy, dummy)
+    xf = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32))
+    x_bits = xf.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    xd = _x_dev(x_bits)
+    ids_t, w_t, l_t = binding.moe_router_topk(layer, xd, want_logits=True)
+    parts = [binding.moe_router_topk(layer, xd[c:c + 16].contiguous(), want_logits=True) for c in range(0, T, 16)]
+    torch.cuda.synchronize()
+    ids_r = torch.cat([p[0] for p in parts]).cpu().numpy()
+    w_r = torch.cat([p[1] for p in parts]).cpu().numpy()
+    l_r = torch.cat([p[2] for p in parts]).cpu().numpy()
+    l_t, ids_t, w_t = l_t.cpu().numpy(), ids_t.cpu().numpy(), w_t.cpu().numpy()
+    assert np.array_equal(l_t.view(np.uint32), l_r.view(np.uint32))
+    assert np.array_equal(ids_t, ids_r)
+    assert np.array_equal(w_t.view(np.uint32), w_r.view(np.uint32))
+    l_ref = moe.router_logits(mx.bf16_bits_to_f64(x_bits), wr_np, b_np)
+    helpers.check_logits(l_t, l_ref, helpers.logit_bound(x_bits, wr_np, l_ref))
