@@ -131,6 +131,7 @@ struct Smem {
   uint8_t tl[kMaxSlots][kDecodeMaxT];           // slots routed to each selected expert
   float red[kWaves][2][kDecodeMaxT][16];        // chunk sums [chunk][gate/up][row][column]
   int wave_cnt[kWaves];
+  uint8_t qrows[kDecodeMaxT];                   // rows of x quantized for this workgroup's gate/up units
   int D;
   int flag;
   int staged;                                   // expert whose intermediate is in LDS (-1 shared, -2 none)
@@ -219,24 +220,34 @@ __device__ __forceinline__ uint32_t quant_block8(const uint32_t (&bits)[4], uint
 }
 
 // ------------------------------------------------------------------ x quantization
-// Every workgroup quantizes the rows of x it needs itself, into LDS.  A task
-// is one 32-value block (row m, block b) of the T * H/32; the eight lanes of
-// group g = threadIdx / 8 handle tasks t0 + p * 32 + g of a batch (p <
-// kQBatch), lane j taking values 4j .. 4j+3 (bf16 x, read with plain loads: x
-// does not change during the call).  A batch's loads are all issued before
-// any of its blocks is quantized.
+// Every workgroup quantizes the rows of x it needs itself, into LDS: a shared
+// gate/up strip all T rows (MXFP8); for the routed gate/up units, with at most
+// kEarlyQuantT rows all rows before routing (while the workgroup would wait
+// for the logits anyway; a strip quantizes them from the x values it already
+// holds), with more rows only the rows of the tokens routed to their experts,
+// once routing is known (quantizing all 16 rows in every workgroup would cost
+// far more than the wait it fills).  A task
+// is one 32-value block (row, block b) of a list of rows: task t covers row
+// rows[t / (H/32)] (row t / (H/32) without a list) and block t mod (H/32).
+// The eight lanes of group g = threadIdx / 8 handle tasks t0 + p * 32 + g of a
+// batch (p < kQBatch), lane j taking values 4j .. 4j+3 (bf16 x, read with
+// plain loads: x does not change during the call).  A batch's loads are all
+// issued before any of its blocks is quantized.
 constexpr int kQBatch = 16;
+constexpr int kEarlyQuantT = 4;
 constexpr int kQGroups = kThreads / 8;
 
 template <class DA>
-__device__ __forceinline__ void x_batch_load(const DA& A, int t0, uint32_t (&bits)[kQBatch][4]) {
-  const int H = A.h(), nb = H / 32, tasks = A.T * nb, j = threadIdx.x & 7, grp = threadIdx.x / 8;
+__device__ __forceinline__ void x_batch_load(const DA& A, int t0, int tasks, const uint8_t* rows,
+                                             uint32_t (&bits)[kQBatch][4]) {
+  const int H = A.h(), nb = H / 32, j = threadIdx.x & 7, grp = threadIdx.x / 8;
 #pragma unroll
   for (int p = 0; p < kQBatch; ++p) {
     const int task = t0 + p * kQGroups + grp;
     bits[p][0] = bits[p][1] = bits[p][2] = bits[p][3] = 0u;
     if (task < tasks) {
-      const uint2 v = *reinterpret_cast<const uint2*>(A.x + (size_t)(task / nb) * H + 32 * (task % nb) + 4 * j);
+      const int m = rows ? rows[task / nb] : task / nb;
+      const uint2 v = *reinterpret_cast<const uint2*>(A.x + (size_t)m * H + 32 * (task % nb) + 4 * j);
       bits[p][0] = v.x << 16;
       bits[p][1] = v.x & 0xffff0000u;
       bits[p][2] = v.y << 16;
@@ -246,11 +257,12 @@ __device__ __forceinline__ void x_batch_load(const DA& A, int t0, uint32_t (&bit
 }
 
 // Quantizes a loaded batch to format F: codes [T][H * bytes per element],
-// scales [T][H/32].
+// scales [T][H/32] (indexed by the real row).
 template <class F, class DA>
-__device__ __forceinline__ void x_batch_quant(const DA& A, int t0, const uint32_t (&bits)[kQBatch][4],
-                                              uint8_t* codes, uint8_t* scales) {
-  const int H = A.h(), nb = H / 32, tasks = A.T * nb, j = threadIdx.x & 7, grp = threadIdx.x / 8;
+__device__ __forceinline__ void x_batch_quant(const DA& A, int t0, int tasks, const uint8_t* rows,
+                                              const uint32_t (&bits)[kQBatch][4], uint8_t* codes,
+                                              uint8_t* scales) {
+  const int H = A.h(), nb = H / 32, j = threadIdx.x & 7, grp = threadIdx.x / 8;
 #pragma unroll
   for (int p = 0; p < kQBatch; ++p) {
     if (t0 + p * kQGroups >= tasks) break;  // uniform
@@ -258,24 +270,13 @@ __device__ __forceinline__ void x_batch_quant(const DA& A, int t0, const uint32_
     uint32_t sc;
     const uint32_t packed = quant_block8<F>(bits[p], &sc);
     if (task < tasks) {
-      const int m = task / nb, b = task % nb;
+      const int m = rows ? rows[task / nb] : task / nb, b = task % nb;
       if constexpr (F::MB == 1)
         *reinterpret_cast<uint16_t*>(codes + (size_t)m * (H / 2) + 16 * b + 2 * j) = (uint16_t)packed;
       else
         *reinterpret_cast<uint32_t*>(codes + (size_t)m * H + 32 * b + 4 * j) = packed;
       if (j == 0) scales[m * nb + b] = (uint8_t)sc;
     }
-  }
-}
-
-// MXFP4 copy of all T rows: codes [T][H/2], scales [T][H/32].
-template <class DA>
-__device__ __forceinline__ void quant_x_fp4(const DA& A, uint8_t* codes, uint8_t* scales) {
-  const int tasks = A.T * (A.h() / 32);
-  for (int t0 = 0; t0 < tasks; t0 += kQBatch * kQGroups) {
-    uint32_t bits[kQBatch][4];
-    x_batch_load(A, t0, bits);
-    x_batch_quant<FP4>(A, t0, bits, codes, scales);
   }
 }
 
@@ -337,10 +338,11 @@ __device__ __forceinline__ void unit_router(const DA& A, uint32_t tag, int e, in
 
 // Shared gate/up strip st (0 <= st < 2 I_s/16: gate strips, then up strips):
 // wave w computes K-chunk w (MXFP8 x MXFP8); the chunk sums meet in LDS and
-// are added in chunk order.  The workgroup first quantizes x itself, to MXFP8
-// (x8: codes [T][H], scales at kDecodeMaxT * H) and to MXFP4 (the copy the
-// routed gate/up units read later); the first batch of x is requested before
-// the weights, so that quantizing does not wait for them.  The fp32 result
+// are added in chunk order.  The workgroup first quantizes x itself to MXFP8
+// (x8: codes [T][H], scales at kDecodeMaxT * H) and, with at most
+// kEarlyQuantT rows, to MXFP4 (the copy the routed gate/up units read later);
+// the first batch of x is requested before the weights, so that quantizing
+// does not wait for them.  The fp32 result
 // goes to a_s[row][16 st + col] as tagged words (gate columns, then up
 // columns); SwiGLU is applied where it is staged.
 template <class DA>
@@ -353,7 +355,7 @@ __device__ __forceinline__ void unit_shared_strip(const DA& A, uint32_t tag, Sme
   uint8_t* xs8 = x8 + (size_t)kDecodeMaxT * A.h();
   const int tasks = A.T * (A.h() / 32);
   uint32_t bits[kQBatch][4];
-  x_batch_load(A, 0, bits);
+  x_batch_load(A, 0, tasks, nullptr, bits);
   v4i B[kMaxCT][2];
   uint32_t sw[3];
   if (act) {
@@ -369,9 +371,9 @@ __device__ __forceinline__ void unit_shared_strip(const DA& A, uint32_t tag, Sme
     for (int g = 0; g < 3; ++g) sw[g] = load_stream4(sp + (size_t)min(t0 / 4 + g, KG - 1) * 256);
   }
   for (int b0 = 0; b0 < tasks; b0 += kQBatch * kQGroups) {
-    if (b0 > 0) x_batch_load(A, b0, bits);
-    x_batch_quant<FP8>(A, b0, bits, x8, xs8);
-    x_batch_quant<FP4>(A, b0, bits, xq4, xs4);
+    if (b0 > 0) x_batch_load(A, b0, tasks, nullptr, bits);
+    x_batch_quant<FP8>(A, b0, tasks, nullptr, bits, x8, xs8);
+    if (A.T <= kEarlyQuantT) x_batch_quant<FP4>(A, b0, tasks, nullptr, bits, xq4, xs4);
   }
   trace_at(A, TR_XQ);
   __syncthreads();
@@ -879,21 +881,28 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
   uint8_t* x8_lds = stage;
 
   // phase A: router units, then shared gate/up strips, strided over the grid.
-  // A strip leaves the MXFP4 copy of x in LDS; other workgroups make it after.
+  // With few rows a strip leaves the MXFP4 copy of x in LDS and the other
+  // workgroups make it after their units.
   if (threadIdx.x == 0) sm.staged = -2;
   const int n_ss = A.is() ? 2 * A.is() / 16 : 0;
+  const bool early_x4 = T <= kEarlyQuantT;
   bool have_x4 = false;
   for (int u = blockIdx.x; u < E + n_ss; u += G) {
     if (u < E) {
       unit_router(A, tag, u, lane, wave);
     } else {
       unit_shared_strip(A, tag, sm, u - E, x8_lds, xq4_lds, xs4_lds, lane, wave);
-      have_x4 = true;
+      have_x4 = early_x4;
     }
     if (threadIdx.x == 0 && u == (int)blockIdx.x) tr[TR_FIRST] = wall_clock64();
   }
-  if (!have_x4) {
-    quant_x_fp4(A, xq4_lds, xs4_lds);
+  if (early_x4 && !have_x4) {
+    const int tasks = T * (A.h() / 32);
+    for (int t0 = 0; t0 < tasks; t0 += kQBatch * kQGroups) {
+      uint32_t bits[kQBatch][4];
+      x_batch_load(A, t0, tasks, nullptr, bits);
+      x_batch_quant<FP4>(A, t0, tasks, nullptr, bits, xq4_lds, xs4_lds);
+    }
     trace_at(A, TR_XQ);
   }
   trace_at(A, TR_A);
@@ -950,6 +959,32 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
     S.nc = (int)((unsigned)NCU * (b + 1) / g) - S.c0;
   }
   const int total = S.nb + S.nc;
+
+  // With more than kEarlyQuantT rows: the MXFP4 copy of the x rows this
+  // workgroup's gate/up units read (the tokens routed to the experts of its
+  // run of phase-B units), listed in ascending order in sm.qrows.  It is made
+  // before the pipeline's weight tiles are requested: a wait for x issued
+  // after them would also wait for every tile in flight.
+  uint32_t need = 0;
+  if (!early_x4 && S.nb > 0) {
+    const int per = A.i() / 16;
+    for (int dd = S.b0 / per; dd <= (S.b0 + S.nb - 1) / per; ++dd)
+      for (int s = 0; s < sm.ecount[dd]; ++s) need |= 1u << (sm.tl[dd][s] / A.kk());
+  }
+  if (need) {  // uniform
+    if (threadIdx.x < kDecodeMaxT && ((need >> threadIdx.x) & 1u))
+      sm.qrows[__popc(need & ((1u << threadIdx.x) - 1u))] = (uint8_t)threadIdx.x;
+    __syncthreads();
+    const int q_tasks = __popc(need) * (A.h() / 32);
+    for (int t0 = 0; t0 < q_tasks; t0 += kQBatch * kQGroups) {
+      uint32_t bits[kQBatch][4];
+      x_batch_load(A, t0, q_tasks, sm.qrows, bits);
+      x_batch_quant<FP4>(A, t0, q_tasks, sm.qrows, bits, xq4_lds, xs4_lds);
+    }
+    trace_at(A, TR_XQ);
+    __syncthreads();  // the x rows are in LDS before any gate/up unit reads them
+  }
+
   Buf X, Y, Z;
   issue(A, sm, S, 0, lane, wave, X);
   issue(A, sm, S, 1, lane, wave, Y);

@@ -268,7 +268,17 @@ __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  /
       wait_ktiles<Gm::CNT_A>(ahead);
     else
       wait_ktiles<Gm::CNT_B>(ahead);
-    __syncthreads();
+    // Each wavefront's own loads of K-tile kt are in LDS (the wait above); the
+    // barrier makes that hold for all of them.  It is a bare s_barrier: the
+    // workgroup fence of __syncthreads() would wait for every direct-to-LDS
+    // load in flight, the later K-tiles' included, and empty the ring.  The
+    // LDS reads of K-tile kt - 1 are complete (its matrix instructions have
+    // consumed them), so its slot may be refilled once every wavefront is here.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (kt + NS - 1 < KT) issue_ktile<Gm>(src, step, as_src, bs_src, ring, wave, kt + NS - 1);
     const unsigned char* st = ring + (kt % NS) * Gm::STAGE;
     v4i a[MF][R], b[4][R];
@@ -349,25 +359,66 @@ __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  /
         }
       }
   } else {
-    // combine: y = bf16( sum_j w_j d_j (j in order) + s + residual )
+    // combine: y = bf16( sum_j w_j d_j (j in order) + s + residual ).  Per
+    // row fragment, every load of a batch of four choices (weights, routed
+    // outputs, residual) is issued before any of them is used, so the
+    // fragment waits for memory once rather than once per output.
+    const int k = g.k;
 #pragma unroll
-    for (int i = 0; i < MF; ++i)
+    for (int i = 0; i < MF; ++i) {
+      int tr[4];
+      float c[4][4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = mb * BM + wm * 16 * MF + 16 * i + 4 * q + r;
-        if (t < g.T) {
+        tr[r] = mb * BM + wm * 16 * MF + 16 * i + 4 * q + r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c[r][j] = 0.f;
+      }
+      for (int jc = 0; jc < k; jc += 4) {
+        float wv[4][4], dv[4][4][4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tc = min(tr[r], g.T - 1);  // rows past the end read a real row, nothing is stored
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const bool on = jc + jj < k;
+            wv[r][jj] = on ? g.topk_w[(size_t)tc * k + jc + jj] : 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int h = 16 * w_strip<MODE, WN>(g, nt, 4 * wn + j) + m;
+              dv[r][j][jj] = on ? g.d_part[((size_t)tc * k + jc + jj) * g.H + h] : 0.f;
+            }
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            if (jc + jj < k) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) c[r][j] = fmaf(wv[r][jj], dv[r][j][jj], c[r][j]);
+            }
+      }
+      float rv[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int h = 16 * w_strip<MODE, WN>(g, nt, 4 * wn + j) + m;
+          rv[r][j] = g.residual ? bf16_to_f32(g.residual[(size_t)min(tr[r], g.T - 1) * g.H + h]) : 0.f;
+        }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (tr[r] < g.T) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int h = 16 * w_strip<MODE, WN>(g, nt, 4 * wn + j) + m;
-            float c = 0.f;
-            for (int jj = 0; jj < g.k; ++jj)
-              c = fmaf(g.topk_w[t * g.k + jj], g.d_part[(size_t)(t * g.k + jj) * g.H + h], c);
-            c = c + sum[i][j][r];
-            if (g.residual) c = c + bf16_to_f32(g.residual[(size_t)t * g.H + h]);
-            g.y[(size_t)t * g.H + h] = f32_to_bf16(c);
+            float v = c[r][j] + sum[i][j][r];
+            if (g.residual) v = v + rv[r][j];
+            g.y[(size_t)tr[r] * g.H + h] = f32_to_bf16(v);
           }
         }
-      }
+    }
   }
 }
 
