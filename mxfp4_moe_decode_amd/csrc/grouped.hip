@@ -312,52 +312,82 @@ __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  /
   }
 
   // ---------------------------------------------------------------- epilogues
+  // The routed gate/up and down epilogues assemble the workgroup's output tile
+  // in the (now idle) LDS ring and write it out with 16-byte row-contiguous
+  // stores.
   if constexpr (kGateUp) {
     // SwiGLU on the 32 columns of block nb, then MX re-quantization of each
     // row's block.  sum[i][0], sum[i][1]: gate columns m and 16 + m; sum[i][2],
     // sum[i][3]: the matching up columns.  Output row of the intermediate: the
     // sorted position (routed) or the row (shared).
-    const int nb = WN * nt + wn;
+    constexpr int BPB = F::MB == 1 ? 16 : 32;  // code bytes of a row's 32-column block
+    constexpr int RB = WN * BPB;               // code bytes of a row of the tile
+    uint8_t* tc = ring;                        // [BM][RB] codes
+    uint8_t* ts = ring + BM * RB;              // [BM][WN] scales
+    __syncthreads();  // every wavefront is done reading the ring
 #pragma unroll
     for (int i = 0; i < MF; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int rl = wm * 16 * MF + 16 * i + 4 * q + r;
-        const bool valid = slots[rl] < S;
-        const int orow = mb * BM + rl;
         const uint32_t a0 = __float_as_uint(silu_mul(sum[i][0][r], sum[i][2][r]));
         const uint32_t a1 = __float_as_uint(silu_mul(sum[i][1][r], sum[i][3][r]));
         const uint32_t am = row16_max32(max(a0 & 0x7fffffffu, a1 & 0x7fffffffu));
         const int ex = block_exponent<F>(am);
         const float inv = block_inv_scale(ex);
         const uint32_t c0 = quant_elem_fast<F>(a0, inv), c1 = quant_elem_fast<F>(a1, inv);
+        uint8_t* op = tc + rl * RB + BPB * wn;
         if constexpr (F::MB == 1) {
           const uint32_t n0 = row_move32(c0), n1 = row_move32(c1);
-          if (valid && !(m & 1)) {
-            uint8_t* op = g.oc + (size_t)orow * (g.inter / 2) + 16 * nb + m / 2;
-            op[0] = (uint8_t)((c0 & 0xfu) | ((n0 & 0xfu) << 4));
-            op[8] = (uint8_t)((c1 & 0xfu) | ((n1 & 0xfu) << 4));
+          if (!(m & 1)) {
+            op[m / 2] = (uint8_t)((c0 & 0xfu) | ((n0 & 0xfu) << 4));
+            op[8 + m / 2] = (uint8_t)((c1 & 0xfu) | ((n1 & 0xfu) << 4));
           }
         } else {
-          if (valid) {
-            uint8_t* op = g.oc + (size_t)orow * g.inter + 32 * nb + m;
-            op[0] = (uint8_t)c0;
-            op[16] = (uint8_t)c1;
-          }
+          op[m] = (uint8_t)c0;
+          op[16 + m] = (uint8_t)c1;
         }
-        if (valid && m == 0) g.os[(size_t)orow * (g.inter / 32) + nb] = (uint8_t)(ex + 127);
+        if (m == 0) ts[rl * WN + wn] = (uint8_t)(ex + 127);
+      }
+    __syncthreads();
+    const size_t row_bytes = F::MB == 1 ? (size_t)g.inter / 2 : (size_t)g.inter;
+    constexpr int PARTS = RB / 16;
+    for (int t = threadIdx.x; t < BM * PARTS; t += THREADS) {
+      const int rl = t / PARTS, part = t % PARTS;
+      if (slots[rl] < S)
+        *reinterpret_cast<uint4*>(g.oc + (size_t)(mb * BM + rl) * row_bytes + (size_t)(WN * nt) * BPB + 16 * part) =
+            *reinterpret_cast<const uint4*>(tc + rl * RB + 16 * part);
+    }
+    for (int rl = threadIdx.x; rl < BM; rl += THREADS)
+      if (slots[rl] < S) {
+#pragma unroll
+        for (int w = 0; w < WN; ++w) g.os[(size_t)(mb * BM + rl) * (g.inter / 32) + WN * nt + w] = ts[rl * WN + w];
       }
   } else if constexpr (MODE == DOWN_ROUTED) {
+    // fp32 result rows per slot: tile [BM][16 STRIPS] (row stride padded by
+    // four floats against bank conflicts), columns 16 STRIPS nt onwards
+    constexpr int CW = 16 * STRIPS;
+    constexpr int LD = CW + 4;
+    static_assert(BM * LD * 4 <= NS * Gm::STAGE, "the output tile fits the ring");
+    float* tf = reinterpret_cast<float*>(ring);
+    __syncthreads();  // every wavefront is done reading the ring
 #pragma unroll
     for (int i = 0; i < MF; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int slot = slots[wm * 16 * MF + 16 * i + 4 * q + r];
-        if (slot < S) {
+        const int rl = wm * 16 * MF + 16 * i + 4 * q + r;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) g.d_part[(size_t)slot * g.H + 16 * w_strip<MODE, WN>(g, nt, 4 * wn + j) + m] = sum[i][j][r];
-        }
+        for (int j = 0; j < 4; ++j) tf[rl * LD + 16 * (4 * wn + j) + m] = sum[i][j][r];
       }
+    __syncthreads();
+    constexpr int V = CW / 4;  // float4 per row
+    for (int t = threadIdx.x; t < BM * V; t += THREADS) {
+      const int rl = t / V, c4 = t % V;
+      const int slot = slots[rl];
+      if (slot < S)
+        *reinterpret_cast<float4*>(g.d_part + (size_t)slot * g.H + (size_t)CW * nt + 4 * c4) =
+            *reinterpret_cast<const float4*>(tf + rl * LD + 4 * c4);
+    }
   } else {
     // combine: y = bf16( sum_j w_j d_j (j in order) + s + residual ).  Per
     // row fragment, every load of a batch of four choices (weights, routed
