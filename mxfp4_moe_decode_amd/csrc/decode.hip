@@ -213,8 +213,11 @@ __device__ __forceinline__ uint32_t quant_block8(const uint32_t (&bits)[4], uint
   const int e = block_exponent<F>(am);
   const float inv = block_inv_scale(e);
   uint32_t packed = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) packed |= quant_elem_fast<F>(bits[i], inv) << ((F::MB == 1 ? 4 : 8) * i);
+  if constexpr (F::MB == 1) {
+    packed = quant_quad_fp4(bits[0], bits[1], bits[2], bits[3], inv);
+  } else {
+    packed = quant_pair_fp8(bits[0], bits[1], inv) | (quant_pair_fp8(bits[2], bits[3], inv) << 16);
+  }
   *scale = (uint32_t)(e + 127);
   return packed;
 }

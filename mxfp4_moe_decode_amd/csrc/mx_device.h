@@ -78,6 +78,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two E4M3 codes (element a in the low byte) of v * 2^-e for fp32 bit
+// patterns a, b and inv = block_inv_scale(e), by the hardware conversion:
+// q = v * inv is exact (a power-of-two scaling) and |q| < 2^9; clamped to
+// +-448 (the largest E4M3 magnitude) first, its round-to-nearest-even
+// conversion equals rounding and then saturating, sign of zero included.
+__device__ __forceinline__ uint32_t quant_pair_fp8(uint32_t a, uint32_t b, float inv) {
+  const float qa = __builtin_amdgcn_fmed3f(__uint_as_float(a) * inv, -448.f, 448.f);
+  const float qb = __builtin_amdgcn_fmed3f(__uint_as_float(b) * inv, -448.f, 448.f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(qa, qb, 0, false) & 0xffffu;
+}
+
+// E2M1 codes of v * 2^-e for four fp32 bit patterns (element i in nibble i)
+// by the hardware conversion, with a unit scale: q = v * inv is exact and
+// |q| < 2^3, and the conversion rounds to nearest even and saturates at 6.
+__device__ __forceinline__ uint32_t quant_quad_fp4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3, float inv) {
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, __uint_as_float(b0) * inv, __uint_as_float(b1) * inv,
+                                                        1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, __uint_as_float(b2) * inv, __uint_as_float(b3) * inv, 1.0f, 1);
+  return w & 0xffffu;
+}
+
 // Quantize 32 consecutive values (fp32 bit patterns) of one MX block held by
 // one lane.  FP4: 16 packed bytes (element 2i in the low nibble of byte i);
 // FP8: 32 bytes.  Returns the E8M0 scale code.
@@ -90,20 +111,14 @@ __device__ __forceinline__ uint32_t quant_block32(const uint32_t* bits, uint32_t
   const float inv = block_inv_scale(e);
   if constexpr (F::MB == 1) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) word |= quant_elem_fast<F>(bits[8 * w + i], inv) << (4 * i);
-      out_words[w] = word;
-    }
+    for (int w = 0; w < 4; ++w)
+      out_words[w] = quant_quad_fp4(bits[8 * w], bits[8 * w + 1], bits[8 * w + 2], bits[8 * w + 3], inv) |
+                     (quant_quad_fp4(bits[8 * w + 4], bits[8 * w + 5], bits[8 * w + 6], bits[8 * w + 7], inv) << 16);
   } else {
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) word |= quant_elem_fast<F>(bits[4 * w + i], inv) << (8 * i);
-      out_words[w] = word;
-    }
+    for (int w = 0; w < 8; ++w)
+      out_words[w] = quant_pair_fp8(bits[4 * w], bits[4 * w + 1], inv) |
+                     (quant_pair_fp8(bits[4 * w + 2], bits[4 * w + 3], inv) << 16);
   }
   return (uint32_t)(e + 127);
 }
