@@ -134,3 +134,27 @@ def test_decode_rejects_more_than_16_rows():
     with pytest.raises(binding.MoeError) as ei:
         binding.fused_moe_mxfp4_decode(gl, x)
     assert ei.value.status == -2
+
+
+@pytest.mark.timeout(900)
+def test_decode_sixteen_rows_on_four_experts():
+    """A router bias that sends all 16 rows to the same 4 experts: every
+    workgroup's gate/up units then read all 16 rows of x, so the MXFP4 copy of
+    x it makes once routing is known spans several batches.  Checked against
+    the oracle and bit for bit against the grouped path."""
+    cfg, gl, ol = _layers("decode16")
+    hot = [3, 40, 77, 120]
+    bias = np.zeros(cfg["E"], np.float32)
+    bias[hot] = 64.0
+    gl2 = binding.MoELayer(gl.hidden, gl.inter, gl.num_experts, gl.top_k, gl.shared_inter, gl.router_w,
+                           torch.from_numpy(bias).cuda(), gl.w13, gl.w13_scale, gl.w2, gl.w2_scale,
+                           gl.ws13, gl.ws13_scale, gl.ws2, gl.ws2_scale)
+    ol2 = moe.Layer(ol.H, ol.I, ol.E, ol.k, ol.I_s, ol.router_w, bias, ol.w13_codes, ol.w13_scales,
+                    ol.w2_codes, ol.w2_scales, ol.ws13_codes, ol.ws13_scales, ol.ws2_codes, ol.ws2_scales)
+    x = synth.activations(cfg)
+    y, ids, w = _run(gl2, x)
+    assert all(sorted(r) == hot for r in ids.tolist())
+    _compare(cfg, gl2, ol2, x, y, ids, w)
+    yg = binding.fused_moe_mxfp4_grouped(gl2, _dev(x))
+    torch.cuda.synchronize()
+    assert np.array_equal(_host(yg), y)
