@@ -14,6 +14,7 @@ namespace {
 constexpr int kThreads = kSortChunk;  // one slot per thread
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxE = 256;
+constexpr int kScanBatch = 16;  // chunk counts loaded together by the scan
 
 __global__ void __launch_bounds__(kThreads) sort_rank_kernel(const int32_t* __restrict__ ids, int S,
                                                              int E, int32_t* __restrict__ hist,
@@ -61,47 +62,57 @@ __global__ void __launch_bounds__(256) sort_scan_kernel(int32_t* __restrict__ hi
                                                         int32_t* __restrict__ num_padded) {
   __shared__ int32_t total[kMaxE], padded[kMaxE], poff[kMaxE + 1], uoff[kMaxE + 1];
   const int tid = threadIdx.x;
+  // the chunk counts of an expert are read kScanBatch at a time, all loads of
+  // a batch issued before any is used
   for (int e = tid; e < E; e += blockDim.x) {
     int run = 0;
-    for (int c = 0; c < nchunks; ++c) run += hist[(size_t)c * E + e];
+    for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+      int h[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) h[i] = c0 + i < nchunks ? hist[(size_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) run += h[i];
+    }
     total[e] = run;
     padded[e] = (run + block_m - 1) / block_m * block_m;
   }
   __syncthreads();
-  if (tid == 0) {
+  // exclusive prefixes over the experts: thread e sums the entries below e
+  // (independent LDS reads, so they pipeline); thread E forms the totals
+  for (int e = tid; e <= E; e += blockDim.x) {
     int p = 0, u = 0;
-    for (int e = 0; e < E; ++e) {
-      poff[e] = p;
-      uoff[e] = u;
-      p += padded[e];
-      u += total[e];
+    for (int e2 = 0; e2 < e; ++e2) {
+      p += padded[e2];
+      u += total[e2];
     }
-    poff[E] = p;
-    uoff[E] = u;
-    *num_padded = p;
+    poff[e] = p;
+    uoff[e] = u;
+    if (e == E) *num_padded = p;
   }
   __syncthreads();
   for (int e = tid; e <= E; e += blockDim.x) expert_offsets[e] = uoff[e];
   // per-chunk destination bases (overwrite the histogram in place)
   for (int e = tid; e < E; e += blockDim.x) {
     int run = poff[e];
-    for (int c = 0; c < nchunks; ++c) {
-      const int h = hist[(size_t)c * E + e];
-      hist[(size_t)c * E + e] = run;
-      run += h;
+    for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+      int h[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) h[i] = c0 + i < nchunks ? hist[(size_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        if (c0 + i < nchunks) {
+          hist[(size_t)(c0 + i) * E + e] = run;
+          run += h[i];
+        }
     }
   }
   const int npad = poff[E];
   const int nblk_cap = capacity / block_m;
-  for (int b = tid; b < nblk_cap; b += blockDim.x) {
-    int owner = -1;
-    if (b * block_m < npad) {
-      // experts are few (<= 256): find the owner by scanning the offsets
-      for (int e = 0; e < E; ++e)
-        if (b * block_m >= poff[e] && b * block_m < poff[e] + padded[e]) owner = e;
-    }
-    block_expert[b] = owner;
-  }
+  // block owners: each expert marks its own blocks, blocks past the padded
+  // length get -1
+  for (int e = tid; e < E; e += blockDim.x)
+    for (int b = poff[e] / block_m; b < (poff[e] + padded[e]) / block_m; ++b) block_expert[b] = e;
+  for (int b = npad / block_m + tid; b < nblk_cap; b += blockDim.x) block_expert[b] = -1;
   // pad entries inside segments and everything past the padded length
   for (int e = tid; e < E; e += blockDim.x)
     for (int i = poff[e] + total[e]; i < poff[e] + padded[e]; ++i) sorted_slots[i] = S;

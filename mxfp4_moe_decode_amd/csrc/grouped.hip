@@ -547,7 +547,13 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
   if ((err = launch_align_sort(ids, T, k, E, kBM, sorted, bexp, reinterpret_cast<int32_t*>(at(c.eoff)), npad,
                                at(c.sort_ws), stream)) != hipSuccess)
     return err;
-  if ((err = launch_quant_act(x, T, H, MX_FMT_FP4, xq4, xs4, stream)) != hipSuccess) return err;
+  // MXFP4 x (and, with a shared expert, MXFP8 x) from one read of x
+  if (Is > 0)
+    err = launch_quant_act_dual(x, T, H, xq4, xs4, reinterpret_cast<uint8_t*>(at(c.xq8)),
+                                reinterpret_cast<uint8_t*>(at(c.xs8)), stream);
+  else
+    err = launch_quant_act(x, T, H, MX_FMT_FP4, xq4, xs4, stream);
+  if (err != hipSuccess) return err;
 
   GemmArgs g{};
   g.T = T;
@@ -606,7 +612,6 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
   uint8_t* xs8 = reinterpret_cast<uint8_t*>(at(c.xs8));
   uint8_t* a8 = reinterpret_cast<uint8_t*>(at(c.a8));
   uint8_t* as8 = reinterpret_cast<uint8_t*>(at(c.as8));
-  if ((err = launch_quant_act(x, T, H, MX_FMT_FP8, xq8, xs8, stream)) != hipSuccess) return err;
   constexpr int BM8 = Geo<FP8, 2>::BM;
   // shared gate/up: A = MXFP8 x, B = Ws13
   {

@@ -27,6 +27,10 @@ hipError_t launch_quant_weights(const float* w, int rows, int cols, int fmt, int
 // (FP8), scales [rows, cols/32].
 hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int fmt, uint8_t* codes,
                             uint8_t* scales, hipStream_t stream);
+// Both copies at once: MXFP4 codes [rows, cols/2] and MXFP8 codes [rows, cols],
+// each with scales [rows, cols/32].
+hipError_t launch_quant_act_dual(const uint16_t* x, int rows, int cols, uint8_t* codes4, uint8_t* scales4,
+                                 uint8_t* codes8, uint8_t* scales8, hipStream_t stream);
 hipError_t launch_fill_u32(void* p, size_t words, uint32_t value, hipStream_t stream);
 
 // ------------------------------------------------------------------ router

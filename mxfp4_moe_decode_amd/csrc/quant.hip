@@ -105,6 +105,41 @@ __global__ void __launch_bounds__(kThreads) quant_act_kernel(const uint16_t* __r
   scales[(size_t)r * nb + b] = (uint8_t)s;
 }
 
+// Both MX copies of the activations (MXFP4 and MXFP8) from one read of x:
+// the same block arithmetic as quant_act_kernel for each format.
+__global__ void __launch_bounds__(kThreads) quant_act_dual_kernel(const uint16_t* __restrict__ x, int rows,
+                                                                  int cols, uint8_t* __restrict__ codes4,
+                                                                  uint8_t* __restrict__ scales4,
+                                                                  uint8_t* __restrict__ codes8,
+                                                                  uint8_t* __restrict__ scales8) {
+  const int nb = cols / 32;
+  const size_t blk = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (blk >= (size_t)rows * nb) return;
+  const int r = (int)(blk / nb), b = (int)(blk % nb);
+  const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)r * cols + 32 * b);
+  uint32_t bits[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = src[i];
+    const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bits[8 * i + 2 * j] = p[j] << 16;
+      bits[8 * i + 2 * j + 1] = p[j] & 0xffff0000u;
+    }
+  }
+  uint32_t w4[4], w8[8];
+  const uint32_t s4 = quant_block32<FP4>(bits, w4);
+  const uint32_t s8 = quant_block32<FP8>(bits, w8);
+  const size_t o = (size_t)r * nb + b;
+  *reinterpret_cast<uint4*>(codes4 + o * 16) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+  uint4* d8 = reinterpret_cast<uint4*>(codes8 + o * 32);
+  d8[0] = make_uint4(w8[0], w8[1], w8[2], w8[3]);
+  d8[1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
+  scales4[o] = (uint8_t)s4;
+  scales8[o] = (uint8_t)s8;
+}
+
 __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -151,6 +186,15 @@ hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int fmt, uint
     hipLaunchKernelGGL(quant_act_kernel<FP4>, dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, codes, scales);
   else
     hipLaunchKernelGGL(quant_act_kernel<FP8>, dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act_dual(const uint16_t* x, int rows, int cols, uint8_t* codes4, uint8_t* scales4,
+                                 uint8_t* codes8, uint8_t* scales8, hipStream_t stream) {
+  const size_t nblk = (size_t)rows * (cols / 32);
+  const unsigned grid = (unsigned)((nblk + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(quant_act_dual_kernel, dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, codes4, scales4,
+                     codes8, scales8);
   return hipGetLastError();
 }
 
