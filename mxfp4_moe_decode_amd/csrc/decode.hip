@@ -563,15 +563,15 @@ __device__ __forceinline__ void gu_compute(const DA& A, Smem& sm, const uint8_t*
   if (wave >= A.nc1()) return;
   const int n = sm.ecount[dd];
   const int m = lane & 15, q = lane >> 4;
-  const int tok = m < n ? sm.tl[dd][m] / A.kk() : -1;
+  // rows past the expert's slot count repeat its last token: their products
+  // land in result rows that are never read
+  const int tok = sm.tl[dd][m < n ? m : n - 1] / A.kk();
   const int CT = A.ct1(), t0 = wave * CT;
   v4i a[kMaxCT];
   uint32_t sa[kMaxCT];
 #pragma unroll
   for (int jj = 0; jj < kMaxCT; ++jj) {
-    a[jj] = v4i{0, 0, 0, 0};
-    sa[jj] = 127;
-    if (jj < CT && tok >= 0) {
+    if (jj < CT) {
       const int kt = t0 + jj;
       a[jj] = *reinterpret_cast<const v4i*>(xq4_lds + (size_t)tok * (A.h() / 2) + kt * 64 + 16 * q);
       sa[jj] = xs4_lds[tok * (A.h() / 32) + 4 * kt + q];
@@ -719,14 +719,14 @@ __device__ __forceinline__ v4f down_compute(const uint8_t* w, const uint8_t* ws_
     for (int jj = 0; jj < NB; ++jj) {
       const int kt = b0 + jj;
       if (kt < KT) {
-        v4i a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
-        uint32_t sa = 127;
-        if (m < n) {
-          const uint8_t* ap = codes + (size_t)m * (F::MB == 1 ? K / 2 : K) + kt * 64 * R + 16 * q;
-          a0 = *reinterpret_cast<const v4i*>(ap);
-          if (R == 2) a1 = *reinterpret_cast<const v4i*>(ap + 64);
-          sa = scales[m * (K / 32) + 4 * kt + q];
-        }
+        // rows past n repeat row n - 1: their products land in result rows
+        // that are never stored
+        const int mr = m < n ? m : n - 1;
+        const uint8_t* ap = codes + (size_t)mr * (F::MB == 1 ? K / 2 : K) + kt * 64 * R + 16 * q;
+        const v4i a0 = *reinterpret_cast<const v4i*>(ap);
+        v4i a1 = a0;
+        if constexpr (R == 2) a1 = *reinterpret_cast<const v4i*>(ap + 64);
+        const uint32_t sa = scales[mr * (K / 32) + 4 * kt + q];
         const uint32_t sb = scale_byte(buf.w(jj / 4), kt);
         if constexpr (F::MB == 1)
           acc = mfma_fp4(a0, buf.q[jj], acc, sa, sb);
