@@ -386,14 +386,12 @@ __device__ __forceinline__ void unit_shared_strip(const DA& A, uint32_t tag, Sme
     for (int j = 0; j < kMaxCT; ++j)
       if (j < CT) {
         const int kt = t0 + j;
-        v4i a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
-        uint32_t sa = 127;
-        if (m < A.T) {
-          const uint8_t* ap = x8 + (size_t)m * A.h() + kt * 128 + 16 * q;
-          a0 = *reinterpret_cast<const v4i*>(ap);
-          a1 = *reinterpret_cast<const v4i*>(ap + 64);
-          sa = xs8[m * (A.h() / 32) + 4 * kt + q];
-        }
+        // rows past T repeat row T - 1: their sums are never read
+        const int mr = m < A.T ? m : A.T - 1;
+        const uint8_t* ap = x8 + (size_t)mr * A.h() + kt * 128 + 16 * q;
+        const v4i a0 = *reinterpret_cast<const v4i*>(ap);
+        const v4i a1 = *reinterpret_cast<const v4i*>(ap + 64);
+        const uint32_t sa = xs8[mr * (A.h() / 32) + 4 * kt + q];
         const uint32_t word = pick3(sw[0], sw[1], sw[2], kt / 4 - t0 / 4);
         acc = mfma_fp8(a0, a1, B[j][0], B[j][1], acc, sa, scale_byte(word, kt));
       }
