@@ -7,13 +7,15 @@
 // device's co-resident capacity) runs three lists of work units:
 //
 //   phase A  (workgroup b takes units b, b+G, ...)
-//            x quantization blocks (MXFP4 and, with a shared expert, MXFP8),
 //            router logits (one unit per expert, all rows),
-//            shared-expert gate/up (one unit per 16-column strip: the gate
-//            strip and the matching up strip; the four wavefronts split K);
+//            shared-expert gate/up (one unit per 16-column strip of the gate
+//            or the up half, on an MXFP8 copy of x the workgroup makes in
+//            LDS; the four wavefronts split K);
 //   routing  every workgroup waits for all logits, takes the top k of each
-//            row and builds the same list of the D selected experts, then
-//            stages the MXFP4 copy of x in LDS;
+//            row and builds the same list of the D selected experts; the
+//            MXFP4 copy of x its gate/up units read is in LDS by then (up to
+//            4 rows: all rows, made while waiting for the logits) or is made
+//            now (more rows: only the rows routed to its experts);
 //   phase B  routed gate/up units (selected expert, 16-column strip; the four
 //            wavefronts split K), SwiGLU, fp32 result per (row, choice) slot;
 //   phase C  routed down units (selected expert, 64 output columns, one
