@@ -242,7 +242,10 @@ constexpr int kQBatch = 16;
 constexpr int kEarlyQuantT = 4;
 constexpr int kQGroups = kThreads / 8;
 
-template <class DA>
+// Without a row list (kRows false) task t is block t of x in row-major
+// order, so every offset is linear in t: x elements 32 t, MXFP8 code bytes
+// 32 t, MXFP4 code bytes 16 t, scale t.
+template <bool kRows, class DA>
 __device__ __forceinline__ void x_batch_load(const DA& A, int t0, int tasks, const uint8_t* rows,
                                              uint32_t (&bits)[kQBatch][4]) {
   const int H = A.h(), nb = H / 32, j = threadIdx.x & 7, grp = threadIdx.x / 8;
@@ -251,8 +254,8 @@ __device__ __forceinline__ void x_batch_load(const DA& A, int t0, int tasks, con
     const int task = t0 + p * kQGroups + grp;
     bits[p][0] = bits[p][1] = bits[p][2] = bits[p][3] = 0u;
     if (task < tasks) {
-      const int m = rows ? rows[task / nb] : task / nb;
-      const uint2 v = *reinterpret_cast<const uint2*>(A.x + (size_t)m * H + 32 * (task % nb) + 4 * j);
+      const size_t off = kRows ? (size_t)rows[task / nb] * H + 32 * (task % nb) : 32 * (size_t)task;
+      const uint2 v = *reinterpret_cast<const uint2*>(A.x + off + 4 * j);
       bits[p][0] = v.x << 16;
       bits[p][1] = v.x & 0xffff0000u;
       bits[p][2] = v.y << 16;
@@ -263,7 +266,7 @@ __device__ __forceinline__ void x_batch_load(const DA& A, int t0, int tasks, con
 
 // Quantizes a loaded batch to format F: codes [T][H * bytes per element],
 // scales [T][H/32] (indexed by the real row).
-template <class F, class DA>
+template <class F, bool kRows, class DA>
 __device__ __forceinline__ void x_batch_quant(const DA& A, int t0, int tasks, const uint8_t* rows,
                                               const uint32_t (&bits)[kQBatch][4], uint8_t* codes,
                                               uint8_t* scales) {
@@ -275,12 +278,13 @@ __device__ __forceinline__ void x_batch_quant(const DA& A, int t0, int tasks, co
     uint32_t sc;
     const uint32_t packed = quant_block8<F>(bits[p], &sc);
     if (task < tasks) {
-      const int m = rows ? rows[task / nb] : task / nb, b = task % nb;
+      // block index in row-major order: task itself without a row list
+      const int blk = kRows ? rows[task / nb] * nb + task % nb : task;
       if constexpr (F::MB == 1)
-        *reinterpret_cast<uint16_t*>(codes + (size_t)m * (H / 2) + 16 * b + 2 * j) = (uint16_t)packed;
+        *reinterpret_cast<uint16_t*>(codes + 16 * blk + 2 * j) = (uint16_t)packed;
       else
-        *reinterpret_cast<uint32_t*>(codes + (size_t)m * H + 32 * b + 4 * j) = packed;
-      if (j == 0) scales[m * nb + b] = (uint8_t)sc;
+        *reinterpret_cast<uint32_t*>(codes + 32 * blk + 4 * j) = packed;
+      if (j == 0) scales[blk] = (uint8_t)sc;
     }
   }
 }
@@ -360,7 +364,7 @@ __device__ __forceinline__ void unit_shared_strip(const DA& A, uint32_t tag, Sme
   uint8_t* xs8 = x8 + (size_t)kDecodeMaxT * A.h();
   const int tasks = A.T * (A.h() / 32);
   uint32_t bits[kQBatch][4];
-  x_batch_load(A, 0, tasks, nullptr, bits);
+  x_batch_load<false>(A, 0, tasks, nullptr, bits);
   v4i B[kMaxCT][2];
   uint32_t sw[3];
   if (act) {
@@ -376,9 +380,9 @@ __device__ __forceinline__ void unit_shared_strip(const DA& A, uint32_t tag, Sme
     for (int g = 0; g < 3; ++g) sw[g] = load_stream4(sp + (size_t)min(t0 / 4 + g, KG - 1) * 256);
   }
   for (int b0 = 0; b0 < tasks; b0 += kQBatch * kQGroups) {
-    if (b0 > 0) x_batch_load(A, b0, tasks, nullptr, bits);
-    x_batch_quant<FP8>(A, b0, tasks, nullptr, bits, x8, xs8);
-    if (A.T <= kEarlyQuantT) x_batch_quant<FP4>(A, b0, tasks, nullptr, bits, xq4, xs4);
+    if (b0 > 0) x_batch_load<false>(A, b0, tasks, nullptr, bits);
+    x_batch_quant<FP8, false>(A, b0, tasks, nullptr, bits, x8, xs8);
+    if (A.T <= kEarlyQuantT) x_batch_quant<FP4, false>(A, b0, tasks, nullptr, bits, xq4, xs4);
   }
   trace_at(A, TR_XQ);
   __syncthreads();
@@ -903,8 +907,8 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
     const int tasks = T * (A.h() / 32);
     for (int t0 = 0; t0 < tasks; t0 += kQBatch * kQGroups) {
       uint32_t bits[kQBatch][4];
-      x_batch_load(A, t0, tasks, nullptr, bits);
-      x_batch_quant<FP4>(A, t0, tasks, nullptr, bits, xq4_lds, xs4_lds);
+      x_batch_load<false>(A, t0, tasks, nullptr, bits);
+      x_batch_quant<FP4, false>(A, t0, tasks, nullptr, bits, xq4_lds, xs4_lds);
     }
     trace_at(A, TR_XQ);
   }
@@ -981,8 +985,8 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
     const int q_tasks = __popc(need) * (A.h() / 32);
     for (int t0 = 0; t0 < q_tasks; t0 += kQBatch * kQGroups) {
       uint32_t bits[kQBatch][4];
-      x_batch_load(A, t0, q_tasks, sm.qrows, bits);
-      x_batch_quant<FP4>(A, t0, q_tasks, sm.qrows, bits, xq4_lds, xs4_lds);
+      x_batch_load<true>(A, t0, q_tasks, sm.qrows, bits);
+      x_batch_quant<FP4, true>(A, t0, q_tasks, sm.qrows, bits, xq4_lds, xs4_lds);
     }
     trace_at(A, TR_XQ);
     __syncthreads();  // the x rows are in LDS before any gate/up unit reads them
