@@ -12,9 +12,14 @@ Prints one JSON line.  `value` is the device time per launch over the timed
 region: K launches issued back to back on one stream (as a decode step issues
 its layers), bracketed by a synchronize and HIP events recorded on that
 stream, divided by K; `ms_per_step` is the wall-clock time per step over the
-same region.  The same launches timed one at a time (an event pair around
+same region.  Every rotated layer instance is launched once before the timed
+region (plus the requested warm-up launches), so no timed launch is the first
+on its weights.  The same launches timed one at a time (an event pair around
 each, so every launch starts on an idle GPU) are reported beside it as
-`us_isolated_*`.
+`us_isolated_*`.  Beside the 1-row line: the 16-row workload, the 8-layer
+4-row chain replayed from a captured HIP graph (us per layer), and the
+8192-row grouped path with each launch step timed by events (routed FP4
+GEMMs against the FP4 matrix peak, shared FP8 GEMMs against the FP8 peak).
 """
 
 import argparse
@@ -100,6 +105,10 @@ def time_decode(binding, synth, name, rotate, steps, warmup, pool=64, isolated=T
         if st != 0:
             raise binding.MoeError("fused_moe_mxfp4_decode", st)
 
+    # every rotated instance is touched once before timing (its first launch
+    # pays first-touch costs the steady state does not), then `warmup` more
+    for i in range(rotate):
+        launch(i)
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
@@ -151,31 +160,107 @@ def prefill_flops(T, H, I, E, k, Is):
     return routed, shared, router
 
 
+FP8_PEAK_TFLOPS = 5000.0   # MI355X dense MXFP8 matrix peak (published)
+FP32_PEAK_TFLOPS = 157.3   # MI355X fp32 vector peak (published)
+
+
 def time_grouped(binding, synth, steps=10, warmup=3):
-    """Whole-layer time of the grouped path on the 8192-row prefill workload."""
+    """The grouped path on the 8192-row prefill workload: whole-layer time,
+    and each launch step timed with HIP events recorded between the steps."""
     import torch
     cfg, layers = build_layers(binding, synth, "prefill", 1)
     L = layers[0]
     x = torch.from_numpy(synth.activations(cfg).view(np.int16)).cuda().view(torch.bfloat16)
     y = torch.empty_like(x)
     ws = binding.grouped_workspace(L, cfg["T"])
-    stream = torch.cuda.current_stream()
     for _ in range(warmup):
         binding.fused_moe_mxfp4_grouped(L, x, out=y, workspace=ws)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in ev:
-        a.record(stream)
-        binding.fused_moe_mxfp4_grouped(L, x, out=y, workspace=ws)
-        b.record(stream)
+    runs = []
+    for _ in range(steps):
+        _, ev = binding.fused_moe_mxfp4_grouped_timed(L, x, out=y, workspace=ws)
+        runs.append(ev)
     torch.cuda.synchronize()
-    us = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+    step_us = np.array([[ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(len(ev) - 1)] for ev in runs])
+    us = np.array([ev[0].elapsed_time(ev[-1]) * 1e3 for ev in runs])
     routed, shared, router = prefill_flops(cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["k"], cfg["I_s"])
     del layers, L, ws
     torch.cuda.empty_cache()
+    st = dict(zip(binding.GROUPED_STEPS, step_us.mean(axis=0)))
+    gu, dn = st["routed_gate_up"], st["routed_down"]
+    sgu, sdn = st["shared_gate_up"], st["shared_down_combine"]
+    # routed: gate/up is 2/3 of the FLOPs, down 1/3 (2 I H and I H per slot)
     return {"us_mean": float(us.mean()), "us_median": float(np.median(us)),
-            "tflops_all": (routed + shared + router) / (us.mean() * 1e-6) / 1e12,
+            "step_us": {k: round(float(v), 2) for k, v in st.items()},
+            "routed_fp4": {"us": round(gu + dn, 2), "tflops": routed / ((gu + dn) * 1e-6) / 1e12,
+                           "gate_up_tflops": routed * 2 / 3 / (gu * 1e-6) / 1e12,
+                           "down_tflops": routed / 3 / (dn * 1e-6) / 1e12},
+            "shared_fp8": {"us": round(sgu + sdn, 2), "tflops": shared / ((sgu + sdn) * 1e-6) / 1e12},
+            "router_fp32": {"us": round(st["router"], 2), "tflops": router / (st["router"] * 1e-6) / 1e12},
             "gflop_routed": routed / 1e9, "gflop_shared": shared / 1e9, "gflop_router": router / 1e9}
+
+
+def time_chain(binding, synth, replays=20):
+    """The 8-layer decode chain (4 rows, Zipf-biased routers, residual):
+    8 fused launches, each reading the previous layer's output, captured once
+    into a HIP graph and replayed.  Each replay starts on a new input row set
+    (copied into the graph's input buffer before its start event)."""
+    import torch
+    cfg = synth.workload("chain8")
+    nl, T = cfg["layers"], cfg["T"]
+    layers = [binding.MoELayer.from_fp32(
+        cfg["H"], cfg["I"], cfg["E"], cfg["k"], cfg["I_s"], synth.router_weights(cfg, li),
+        synth.router_bias(cfg, li), lambda e, li=li: synth.device_expert_w13(cfg, li, e),
+        lambda e, li=li: synth.device_expert_w2(cfg, li, e),
+        synth.device_shared_w13(cfg, li), synth.device_shared_w2(cfg, li)) for li in range(nl)]
+    xs = [torch.from_numpy(synth.activations(cfg, index=j).view(np.int16)).cuda().view(torch.bfloat16)
+          for j in range(replays + 1)]
+    ws = binding.decode_workspace(layers[0])
+    bufs = [torch.empty_like(xs[0]) for _ in range(nl + 1)]
+    ids = [torch.empty(T, cfg["k"], dtype=torch.int32, device="cuda") for _ in range(nl)]
+    wts = [torch.empty(T, cfg["k"], dtype=torch.float32, device="cuda") for _ in range(nl)]
+    lib = binding.load()
+
+    def chain():
+        sp = binding._stream()
+        for li in range(nl):
+            st = lib.fused_moe_mxfp4_decode(layers[li].c, binding._ptr(bufs[li]), T, binding._ptr(bufs[li]),
+                                            binding._ptr(bufs[li + 1]), binding._ptr(ws), ws.numel(),
+                                            binding._ptr(ids[li]), binding._ptr(wts[li]), sp)
+            if st != 0:
+                raise binding.MoeError("fused_moe_mxfp4_decode", st)
+
+    bufs[0].copy_(xs[-1])
+    chain()  # eager once: first touch of every layer
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chain()
+    graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]
+    D = np.zeros((replays, nl))
+    for r in range(replays):
+        bufs[0].copy_(xs[r])
+        ev[r][0].record(stream)
+        graph.replay()
+        ev[r][1].record(stream)
+        torch.cuda.synchronize()
+        D[r] = [len(np.unique(i.cpu().numpy())) for i in ids]
+    us = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+    if binding.moe_decode_status(ws) != 0:
+        raise RuntimeError("a device-side wait timed out during the chain benchmark")
+    nbytes = np.array([[layer_bytes(cfg["H"], cfg["I"], cfg["E"], cfg["I_s"], d, T, residual=True) for d in row]
+                       for row in D])
+    del layers, graph
+    torch.cuda.empty_cache()
+    per_layer = float(np.median(us)) / nl
+    gbs = float(nbytes.sum(axis=1).mean()) / (np.median(us) * 1e-6) / 1e9
+    return {"us_per_layer": per_layer, "us_replay_median": float(np.median(us)),
+            "us_replay_p10": float(np.percentile(us, 10)), "us_replay_p90": float(np.percentile(us, 90)),
+            "distinct_experts_per_layer": [round(float(v), 2) for v in D.mean(axis=0)],
+            "bytes_per_layer_mean": float(nbytes.mean()), "gbs": gbs}
 
 
 def cpu_baseline(synth, seconds=15.0):
@@ -241,6 +326,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-16", action="store_true", help="skip the 16-row measurement")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 8192-row grouped measurement")
+    ap.add_argument("--no-chain", action="store_true", help="skip the 8-layer graph-replayed chain")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-isolated", action="store_true",
                     help="skip the one-launch-at-a-time timing (profiler runs: only back-to-back launches)")
@@ -271,11 +357,17 @@ def main():
         print(f"[bench] 16 rows: {r16['us_launch']:.2f} us per launch back to back, {r16['gbs']:.0f} GB/s, "
               f"D={r16['distinct_experts_mean']:.1f}; isolated {r16['us_isolated_mean']:.2f} us",
               file=sys.stderr, flush=True)
+    rc = None
+    if not args.no_chain:
+        rc = time_chain(binding, synth)
+        print(f"[bench] 8-layer chain, 4 rows, graph replay: {rc['us_per_layer']:.2f} us per layer, "
+              f"{rc['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
     rp = None
     if not args.no_prefill:
         rp = time_grouped(binding, synth)
-        print(f"[bench] prefill 8192 rows (grouped path): {rp['us_mean']:.1f} us per layer, "
-              f"{rp['tflops_all']:.1f} TFLOP/s over all layer FLOPs", file=sys.stderr, flush=True)
+        print(f"[bench] prefill 8192 rows (grouped path): {rp['us_mean']:.1f} us per layer; routed FP4 GEMMs "
+              f"{rp['routed_fp4']['us']:.1f} us ({rp['routed_fp4']['tflops']:.0f} TFLOP/s), shared FP8 "
+              f"{rp['shared_fp8']['us']:.1f} us", file=sys.stderr, flush=True)
     if args.copy_mib:
         src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -320,16 +412,35 @@ def main():
                          "us_isolated_mean": round(r16["us_isolated_mean"], 3),
                          "algorithmic_bytes_per_launch": int(r16["bytes_mean"]),
                          "ms_per_step": round(r16["wall_ms_per_step"], 5)}
+    if rc:
+        out["chain8"] = {
+            "workload": "8 distinct layers (hidden 3072, 128 experts top-4, I 1024, MXFP8 shared 1024), 4 rows, "
+                        "Zipf(1.2)-biased routers, fused residual; one launch per layer, 8 launches captured "
+                        "in a HIP graph and replayed",
+            "us_per_layer": round(rc["us_per_layer"], 3), "us_replay_median": round(rc["us_replay_median"], 2),
+            "us_replay_p10": round(rc["us_replay_p10"], 2), "us_replay_p90": round(rc["us_replay_p90"], 2),
+            "distinct_experts_per_layer": rc["distinct_experts_per_layer"],
+            "algorithmic_bytes_per_layer": int(rc["bytes_per_layer_mean"]),
+            "gbs": round(rc["gbs"], 1), "frac": round(rc["gbs"] / HBM_PEAK_GBS, 4)}
     if rp:
         out["prefill8192"] = {
             "workload": "8192 bf16 rows through the same layer on the grouped path (router, sort, MX quant, "
                         "grouped FP4 GEMMs, MXFP8 shared expert, combine)",
             "us_mean": round(rp["us_mean"], 2), "us_median": round(rp["us_median"], 2),
+            "step_us": rp["step_us"],
             "gflop": {"routed_fp4": round(rp["gflop_routed"], 1), "shared_fp8": round(rp["gflop_shared"], 1),
                       "router_fp32": round(rp["gflop_router"], 2)},
-            "tflops_all_flops": round(rp["tflops_all"], 1),
-            "fp4_peak_tflops": FP4_PEAK_TFLOPS,
-            "frac_of_fp4_peak_whole_layer": round(rp["tflops_all"] / FP4_PEAK_TFLOPS, 4)}
+            "routed_fp4_gemms": {"us": rp["routed_fp4"]["us"], "tflops": round(rp["routed_fp4"]["tflops"], 1),
+                                 "peak_tflops": FP4_PEAK_TFLOPS,
+                                 "frac": round(rp["routed_fp4"]["tflops"] / FP4_PEAK_TFLOPS, 4),
+                                 "gate_up_frac": round(rp["routed_fp4"]["gate_up_tflops"] / FP4_PEAK_TFLOPS, 4),
+                                 "down_frac": round(rp["routed_fp4"]["down_tflops"] / FP4_PEAK_TFLOPS, 4)},
+            "shared_fp8_gemms": {"us": rp["shared_fp8"]["us"], "tflops": round(rp["shared_fp8"]["tflops"], 1),
+                                 "peak_tflops": FP8_PEAK_TFLOPS,
+                                 "frac": round(rp["shared_fp8"]["tflops"] / FP8_PEAK_TFLOPS, 4)},
+            "router_fp32": {"us": rp["router_fp32"]["us"], "tflops": round(rp["router_fp32"]["tflops"], 2),
+                            "peak_tflops": FP32_PEAK_TFLOPS,
+                            "frac": round(rp["router_fp32"]["tflops"] / FP32_PEAK_TFLOPS, 4)}}
     out["cpu_baseline"] = cpu
     print(json.dumps(out))
 

@@ -99,7 +99,11 @@ moe_status mx_quantize_weights(const float* w, int rows, int cols, int fmt, int 
  *   x      [rows][cols] bf16, 16-byte aligned, cols % 32 == 0
  *   codes  [rows][cols/2] packed E2M1 (element 2i in the low nibble of byte i)
  *   scales [rows][cols/32] E8M0
- * Bit-exact: the conversion is integer arithmetic on the bf16 patterns.
+ * Exact: each element is multiplied by 2^-e (a power of two, exact in fp32)
+ * and converted by gfx950's scaled fp32 -> E2M1 instruction with a unit scale,
+ * which rounds to nearest even and saturates; the block exponent comes from the
+ * exponent bits of the block maximum.  Codes equal the specification's for
+ * every finite bf16 input.
  */
 moe_status mxfp4_quant_act(const uint16_t* x, int rows, int cols, uint8_t* codes,
                            uint8_t* scales, hipStream_t stream);
@@ -147,6 +151,11 @@ moe_status moe_router_topk(const moe_layer_t* layer, const uint16_t* x, int T, f
 /*
  * Token sort by expert: a stable counting sort of the slots s = t*k + j by
  * topk_ids[t][j], each expert's segment padded to a multiple of block_m.
+ * This is the step that turns routed tokens into per-expert row blocks for a
+ * grouped fused-MoE GEMM (the AITER MXFP4 fused MoE the article "MiniMax-M3.1
+ * on AMD Instinct GPUs: Day-0 support and optimization" runs outside mono
+ * decode, section "Serving with vLLM / What we Optimized"; the pages do not
+ * spell the sort out, so the padded counting sort is this library's reading).
  *   sorted_slots   moe_align_sort_capacity(T, k, E, block_m) int32: slots grouped
  *                  by expert (experts ascending, slots ascending inside), each
  *                  segment padded with T*k; entries past num_padded are T*k
@@ -166,7 +175,12 @@ moe_status moe_align_sort(const int32_t* topk_ids, int T, int k, int E, int bloc
  * Workspace for the fused calls.  path 0: fused_moe_mxfp4_decode (T <= 16),
  * path 1: fused_moe_mxfp4_grouped (any T).  Returns 0 for invalid arguments.
  * A decode workspace must be zero-filled once (moe_workspace_init) before its
- * first use; every decode call leaves it zero-filled again on exit.
+ * first use.  Each decode call tags the words it hands between workgroups
+ * with a 32-bit call counter kept in the workspace; the call that would make
+ * the counter wrap clears every tagged word itself, so a workspace serves any
+ * number of calls without re-initialization.  After moe_decode_status reports
+ * MOE_ERR_TIMEOUT the workspace must be zero-filled again: until then every
+ * decode call on it writes NaN (bf16 0x7FC0) to y and computes nothing.
  */
 size_t moe_workspace_bytes(const moe_layer_t* layer, int T, int path);
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
@@ -212,8 +226,24 @@ moe_status fused_moe_mxfp4_grouped(const moe_layer_t* layer, const uint16_t* x, 
                                    hipStream_t stream);
 
 /*
+ * Diagnostic: fused_moe_mxfp4_grouped with an event recorded on `stream`
+ * before each of its launch steps and one at the end, so that a caller can
+ * time them (hipEventElapsedTime).  events[0..7], caller-created, non-NULL:
+ *   0 router and top-k, 1 token sort, 2 MX quantization of x, 3 routed
+ *   gate/up GEMM, 4 routed down GEMM, 5 shared gate/up GEMM (the combine
+ *   kernel when there is no shared expert), 6 shared down GEMM with the
+ *   combine (nothing without a shared expert), 7 end.
+ * Results and errors as for fused_moe_mxfp4_grouped.
+ */
+moe_status fused_moe_mxfp4_grouped_timed(const moe_layer_t* layer, const uint16_t* x, int T,
+                                         const uint16_t* residual, uint16_t* y, void* ws, size_t ws_bytes,
+                                         const hipEvent_t* events, hipStream_t stream);
+
+/*
  * Diagnostic (synchronizes the device): MOE_OK if no fused decode call on this
- * workspace has given up a device-side wait, MOE_ERR_TIMEOUT otherwise.
+ * workspace has given up a device-side wait, MOE_ERR_TIMEOUT otherwise.  A
+ * call whose wait gives up writes NaN to the output columns it combines after
+ * that point; later calls write NaN everywhere (see moe_workspace_bytes).
  */
 moe_status moe_decode_status(const void* ws, size_t ws_bytes);
 

@@ -9,9 +9,7 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# MXMOE_LIB selects another build of the library (e.g. for A/B measurements);
-# by default the in-tree build is loaded.
-LIB_PATH = os.environ.get("MXMOE_LIB") or os.path.join(_HERE, "libmxmoe.so")
+LIB_PATH = os.path.join(_HERE, "libmxmoe.so")
 
 MX_FMT = {"fp4": 0, "fp8": 1}
 MX_LAYOUT = {"rowmajor": 0, "tiled": 1}
@@ -22,7 +20,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARGUMENT", -2: "MOE_ERR_UNSUPPORTED"
 EXPORTS = [
     "mx_codes_bytes", "mx_scales_bytes", "mx_quantize_weights", "mxfp4_quant_act",
     "moe_router_topk", "moe_align_sort_capacity", "moe_align_sort_workspace_bytes", "moe_align_sort",
-    "moe_workspace_bytes", "moe_workspace_init", "fused_moe_mxfp4_decode", "fused_moe_mxfp4_grouped",
+    "moe_workspace_bytes", "moe_workspace_init", "fused_moe_mxfp4_decode", "fused_moe_mxfp4_grouped", "fused_moe_mxfp4_grouped_timed",
     "moe_decode_status", "moe_decode_trace", "moe_status_string",
 ]
 
@@ -72,6 +70,7 @@ def load():
         "moe_workspace_init": (S, [P, Z, P]),
         "fused_moe_mxfp4_decode": (S, [LP, P, I, P, P, P, Z, P, P, P]),
         "fused_moe_mxfp4_grouped": (S, [LP, P, I, P, P, P, Z, P]),
+        "fused_moe_mxfp4_grouped_timed": (S, [LP, P, I, P, P, P, Z, P, P]),
         "moe_decode_status": (S, [P, Z]),
         "moe_decode_trace": (I, [LP, P, Z, P, Z]),
         "moe_status_string": (ctypes.c_char_p, [S]),
@@ -293,6 +292,73 @@ def fused_moe_mxfp4_grouped(layer, x, residual=None, out=None, workspace=None):
     _check("fused_moe_mxfp4_grouped", load().fused_moe_mxfp4_grouped(
         layer.c, _ptr(x), T, _ptr(residual), _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
     return out
+
+
+# Steps of at most this many rows run as one fused launch; wider ones take the
+# grouped path (the article "MiniMax-M3.1 on AMD Instinct GPUs: Day-0 support
+# and optimization", section "Performance, mono decode on vs off": beyond 16
+# tokens the dispatcher leaves the step on the original path).
+DECODE_MAX_ROWS = 16
+
+
+class MoEForward:
+    """One MoE layer call for any number of rows: the fused single-launch
+    decode for T <= 16 (falling back to the grouped path when the library
+    reports the shape as unsupported by it), the grouped path otherwise.  Keeps
+    the decode workspace (zero-filled once) and a grouped workspace grown on
+    demand."""
+
+    def __init__(self, layer, device="cuda"):
+        self.layer, self.device = layer, torch.device(device)
+        self.decode_ws = None
+        self.grouped_ws = None
+        self.last_path = None
+
+    def _grouped(self, x, residual, out):
+        n = moe_workspace_bytes(self.layer, x.shape[0], 1)
+        if n == 0:
+            raise MoeError("moe_workspace_bytes", -2)
+        if self.grouped_ws is None or self.grouped_ws.numel() < n:
+            self.grouped_ws = torch.empty(n, dtype=torch.uint8, device=self.device)
+        self.last_path = "grouped"
+        return fused_moe_mxfp4_grouped(self.layer, x, residual, out, self.grouped_ws)
+
+    def __call__(self, x, residual=None, out=None):
+        if x.shape[0] <= DECODE_MAX_ROWS:
+            if self.decode_ws is None:
+                self.decode_ws = decode_workspace(self.layer, self.device)
+            try:
+                y = fused_moe_mxfp4_decode(self.layer, x, residual, out, self.decode_ws)
+                self.last_path = "decode"
+                return y
+            except MoeError as err:
+                if err.status != -2:  # MOE_ERR_UNSUPPORTED: shape beyond the fused kernel
+                    raise
+        return self._grouped(x, residual, out)
+
+
+GROUPED_STEPS = ("router", "sort", "x_quant", "routed_gate_up", "routed_down", "shared_gate_up",
+                 "shared_down_combine")
+
+
+def fused_moe_mxfp4_grouped_timed(layer, x, residual=None, out=None, workspace=None):
+    """fused_moe_mxfp4_grouped with HIP events around each launch step.
+    Returns (out, events); after a synchronize, events[i].elapsed_time(
+    events[i + 1]) is step GROUPED_STEPS[i] in ms."""
+    _need_cuda(x, residual, out, workspace)
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = grouped_workspace(layer, T, x.device)
+    stream = torch.cuda.current_stream()
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(len(GROUPED_STEPS) + 1)]
+    for e in events:  # creates the HIP events
+        e.record(stream)
+    handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    _check("fused_moe_mxfp4_grouped_timed", load().fused_moe_mxfp4_grouped_timed(
+        layer.c, _ptr(x), T, _ptr(residual), _ptr(out), _ptr(workspace), workspace.numel(), handles, _stream()))
+    return out, events
 
 
 def moe_decode_status(workspace):

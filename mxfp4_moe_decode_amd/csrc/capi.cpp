@@ -134,9 +134,9 @@ moe_status fused_moe_mxfp4_decode(const moe_layer_t* layer, const uint16_t* x, i
   return from_hip(launch_decode(*layer, x, T, residual, y, ws, topk_ids_out, topk_w_out, stream));
 }
 
-moe_status fused_moe_mxfp4_grouped(const moe_layer_t* layer, const uint16_t* x, int T,
-                                   const uint16_t* residual, uint16_t* y, void* ws, size_t ws_bytes,
-                                   hipStream_t stream) {
+namespace {
+moe_status grouped_call(const moe_layer_t* layer, const uint16_t* x, int T, const uint16_t* residual, uint16_t* y,
+                        void* ws, size_t ws_bytes, hipStream_t stream, const hipEvent_t* events) {
   const moe_status st = check_layer(layer);
   if (st != MOE_OK) return st;
   if (!x || !y || !ws || T <= 0) return MOE_ERR_INVALID_ARGUMENT;
@@ -146,7 +146,23 @@ moe_status fused_moe_mxfp4_grouped(const moe_layer_t* layer, const uint16_t* x, 
   const size_t need = grouped_ws_bytes(*layer, T);
   if (need == 0) return MOE_ERR_UNSUPPORTED;
   if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  return from_hip(launch_grouped(*layer, x, T, residual, y, ws, stream));
+  return from_hip(launch_grouped(*layer, x, T, residual, y, ws, stream, events));
+}
+}  // namespace
+
+moe_status fused_moe_mxfp4_grouped(const moe_layer_t* layer, const uint16_t* x, int T,
+                                   const uint16_t* residual, uint16_t* y, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  return grouped_call(layer, x, T, residual, y, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status fused_moe_mxfp4_grouped_timed(const moe_layer_t* layer, const uint16_t* x, int T,
+                                         const uint16_t* residual, uint16_t* y, void* ws, size_t ws_bytes,
+                                         const hipEvent_t* events, hipStream_t stream) {
+  if (!events) return MOE_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i <= kGroupedSteps; ++i)
+    if (!events[i]) return MOE_ERR_INVALID_ARGUMENT;
+  return grouped_call(layer, x, T, residual, y, ws, ws_bytes, stream, events);
 }
 
 moe_status moe_decode_status(const void* ws, size_t ws_bytes) {

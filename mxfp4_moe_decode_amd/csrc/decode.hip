@@ -41,6 +41,8 @@
 // SwiGLU and re-quantization (MXFP4 routed, MXFP8 shared) follow per 32-column
 // block; the combine adds sum_j w_j d_j in j order, then s, then the residual,
 // and rounds once to bf16.  Output row t therefore depends on x[t] only.
+#include <atomic>
+
 #include "internal.h"
 #include "mx_device.h"
 
@@ -57,6 +59,7 @@ constexpr int kBufWords = 6;   // scale words one prefetch buffer holds per lane
 constexpr int kBufs = 3;       // register buffers of the unit pipeline
 constexpr int kDownBatch = 8;  // routed (MXFP4) down tiles per register batch; MXFP8: half
 constexpr uint64_t kSpinTicks = 100000000ull;  // ~1 s of the 100 MHz constant clock
+constexpr uint16_t kBf16NaN = 0x7fc0;
 
 // Every counter sits on a 256-byte line of its own: device-scope atomics on
 // one line are serialized by the memory side.
@@ -93,6 +96,8 @@ struct DecodeArgs {
   uint64_t* a_r;  // tagged [T*k][I]
   uint64_t* a_s;  // tagged [T][2 I_s]
   uint64_t *d_part, *s_part;  // tagged [T*k][H], [T][H]
+  uint64_t* tagged;           // every tagged word above: one contiguous range
+  uint32_t n_tagged;
   uint64_t* trace;
 };
 
@@ -136,7 +141,7 @@ struct Smem {
   uint8_t qrows[kDecodeMaxT];                   // rows of x quantized for this workgroup's gate/up units
   int D;
   int flag;
-  int staged;                                   // expert whose intermediate is in LDS (-1 shared, -2 none)
+  int last;                                     // this workgroup is the call's last to finish
 };
 
 // ------------------------------------------------------------------ synchronisation
@@ -748,7 +753,9 @@ __device__ __forceinline__ v4f down_compute(const uint8_t* w, const uint8_t* ws_
 
 // Combine of output columns 64 hg .. +64 for every row: reads the tagged down
 // outputs of the group until all are this call's, then
-// y = bf16( sum_j w_j d_j (j in order) + s + residual ).
+// y = bf16( sum_j w_j d_j (j in order) + s + residual ).  If any wait of the
+// call has given up by then (the status word, read with the last polls), the
+// group's output is NaN instead.
 template <class DA>
 __device__ __forceinline__ void combine(const DA& A, uint32_t tag, const Smem& sm, int hg) {
   const int H = A.h(), k = A.kk();
@@ -756,8 +763,10 @@ __device__ __forceinline__ void combine(const DA& A, uint32_t tag, const Smem& s
   float d[kPer][kMaxK], s[kPer];
   const uint64_t t0 = wall_clock64();
   bool ok;
+  uint32_t status;
   do {
     ok = true;
+    status = ld_dev(ctr(A.sync, S_STATUS));  // read with the polls: no extra round trip
 #pragma unroll
     for (int p = 0; p < kPer; ++p) {
       const int idx = threadIdx.x + p * kThreads;
@@ -789,7 +798,8 @@ __device__ __forceinline__ void combine(const DA& A, uint32_t tag, const Smem& s
         if (j < k) acc = fmaf(sm.w[t * k + j], d[p][j], acc);
       if (A.is()) acc = acc + s[p];
       if (A.residual) acc = acc + bf16_to_f32(A.residual[(size_t)t * H + h]);
-      A.y[(size_t)t * H + h] = f32_to_bf16(acc);
+      // a wait of this call that gave up (status set) leaves NaN, not stale data
+      A.y[(size_t)t * H + h] = (ok && status == 0u) ? f32_to_bf16(acc) : kBf16NaN;
     }
   }
 }
@@ -827,10 +837,13 @@ __device__ __forceinline__ void run_entry(const DA& A, uint32_t tag, Smem& sm, c
     const int K = A.i();
     uint8_t* codes = stage;
     uint8_t* scales = stage + kDecodeMaxT * (K / 2);
-    if (sm.staged != e) {
+    // The staged intermediate is the previous entry's when that entry was a
+    // routed down unit of the same expert.  Every thread derives this from
+    // the sequence itself, so the whole workgroup takes the same branch.
+    const int pu = u - 1;
+    if (!(j > S.nb && pu >= S.ns && (pu - S.ns) / S.nhg == dd)) {
       stage_routed(A, tag, K, n, sm.tl[dd], codes, scales);
       __syncthreads();
-      if (threadIdx.x == 0) sm.staged = e;
       if (j == S.nb) trace_at(A, TR_C_STAGED);
     }
     const int KG = (A.kt2() + 3) / 4;
@@ -846,10 +859,11 @@ __device__ __forceinline__ void run_entry(const DA& A, uint32_t tag, Smem& sm, c
     const int K = A.is();
     uint8_t* codes = stage;
     uint8_t* scales = stage + kDecodeMaxT * K;
-    if (sm.staged != -1) {
+    // shared down units come first in the sequence: a previous down entry
+    // was a shared one and has staged the intermediate already
+    if (j == S.nb) {
       stage_shared(A, tag, K, codes, scales);
       __syncthreads();
-      if (threadIdx.x == 0) sm.staged = -1;
     }
     const int KG = (A.kts() + 3) / 4;
     const uint8_t* w = A.ws2 + (size_t)hs * A.kts() * 2048 + lane * 16;
@@ -863,21 +877,11 @@ __device__ __forceinline__ void run_entry(const DA& A, uint32_t tag, Smem& sm, c
 }
 
 // ------------------------------------------------------------------ kernel
+// The layer itself: phases A, B, C and the combines of this workgroup.
 template <class DA>
-__global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
-  const uint64_t t_entry = wall_clock64();
-  __shared__ Smem sm;
-  extern __shared__ __align__(16) unsigned char dyn[];
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+__device__ __forceinline__ void decode_body(const DA& A, uint32_t tag, Smem& sm, unsigned char* dyn, uint64_t* tr,
+                                            int lane, int wave) {
   const int G = A.G, T = A.T, E = A.e();
-  const uint32_t tag = ld_dev(ctr(A.sync, S_EPOCH)) + 1u;
-  uint64_t* tr = A.trace + (size_t)blockIdx.x * kTraceWords;
-  if (threadIdx.x == 0) {
-    tr[TR_START] = t_entry;
-    for (int i = 1; i < kTraceWords - 1; ++i) tr[i] = 0;
-    wait_vm<0>();
-    tr[TR_TAG] = wall_clock64() + (tag == 0u ? 1u : 0u);
-  }
 
   // dynamic LDS: logits, the MXFP4 x, then the MXFP8 x of a shared strip
   // (phase A) or the staged down-unit intermediate (later)
@@ -890,7 +894,6 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
   // phase A: router units, then shared gate/up strips, strided over the grid.
   // With few rows a strip leaves the MXFP4 copy of x in LDS and the other
   // workgroups make it after their units.
-  if (threadIdx.x == 0) sm.staged = -2;
   const int n_ss = A.is() ? 2 * A.is() / 16 : 0;
   const bool early_x4 = T <= kEarlyQuantT;
   bool have_x4 = false;
@@ -1011,8 +1014,42 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
 
   // combines: workgroup b takes column groups b, b + G, ...
   for (int hg = blockIdx.x; hg < S.nhg; hg += G) combine(A, tag, sm, hg);
+}
 
-  // exit: the last workgroup resets the launch-wide counters
+// A call on a workspace whose status word is set (an earlier call gave up a
+// wait, so its tagged words cannot be trusted) computes nothing: its output
+// is the bf16 NaN pattern, until the workspace is zero-filled again.
+template <class DA>
+__device__ __forceinline__ void poison_output(const DA& A) {
+  const int nhg = A.h() / 64;
+  for (int hg = blockIdx.x; hg < nhg; hg += A.G)
+    for (int idx = threadIdx.x; idx < A.T * 64; idx += kThreads)
+      A.y[(size_t)(idx >> 6) * A.h() + 64 * hg + (idx & 63)] = kBf16NaN;
+}
+
+template <class DA>
+__global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
+  const uint64_t t_entry = wall_clock64();
+  __shared__ Smem sm;
+  extern __shared__ __align__(16) unsigned char dyn[];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int G = A.G;
+  const uint32_t tag = ld_dev(ctr(A.sync, S_EPOCH)) + 1u;
+  const uint32_t status = ld_dev(ctr(A.sync, S_STATUS));
+  uint64_t* tr = A.trace + (size_t)blockIdx.x * kTraceWords;
+  if (threadIdx.x == 0) {
+    tr[TR_START] = t_entry;
+    for (int i = 1; i < kTraceWords - 1; ++i) tr[i] = 0;
+    wait_vm<0>();
+    tr[TR_TAG] = wall_clock64() + (tag == 0u ? 1u : 0u);
+  }
+  if (status == 0u)
+    decode_body(A, tag, sm, dyn, tr, lane, wave);
+  else
+    poison_output(A);
+
+  // exit: the last workgroup to finish advances the epoch (the next call's
+  // tag is one more) and resets the arrival counter
   __syncthreads();
   if (threadIdx.x == 0) {
     tr[TR_C] = wall_clock64();
@@ -1021,8 +1058,22 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
     wait_vm<0>();
     const uint32_t old = __hip_atomic_fetch_add(ctr(A.sync, S_DONE), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     compiler_fence();
-    if (old + 1 == (uint32_t)G) {
-      st_dev(ctr(A.sync, S_EPOCH), tag);  // the next call's tag is one more
+    sm.last = old + 1 == (uint32_t)G;
+  }
+  __syncthreads();
+  if (sm.last) {  // uniform
+    // After 2^32 - 1 calls the tag would wrap to 0, the tag of zero-filled
+    // words, and later tags would match words written 2^32 calls earlier.
+    // Instead every tagged word is cleared and the epoch restarts at 0.
+    const bool wrap = tag == 0xffffffffu;
+    if (wrap) {
+      for (uint32_t i = threadIdx.x; i < A.n_tagged; i += kThreads) st_dev(&A.tagged[i], (uint64_t)0);
+      compiler_fence();
+      wait_vm<0>();
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+      st_dev(ctr(A.sync, S_EPOCH), wrap ? 0u : tag);
       compiler_fence();
       wait_vm<0>();
       st_dev(ctr(A.sync, S_DONE), 0u);
@@ -1068,13 +1119,17 @@ size_t dyn_lds_bytes(const moe_layer_t& L) {
   return logits + xq + (st > x8 ? st : x8);
 }
 
+// Grid of the persistent launch: as many workgroups as the device keeps
+// resident at once (one per CU), since every workgroup must run concurrently.
+// Kept per device in a lock-free table of (dynamic LDS bytes << 32 | grid);
+// two threads that race on a device's first call compute the same entry.
 template <class DA>
 int grid_size(size_t lds) {
-  static int cached_dev = -1, cached_grid = 0;
-  static size_t cached_lds = 0;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (dev == cached_dev && lds == cached_lds) return cached_grid;
+  static std::atomic<uint64_t> cache[kMaxDevices];
+  const int dev = current_device();
+  if (dev < 0) return 0;
+  const uint64_t c = cache[dev].load(std::memory_order_relaxed);
+  if (c != 0 && (c >> 32) == lds) return (int)(uint32_t)c;
   int cus = 0, occ = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (lds + sizeof(Smem) > 64 * 1024 &&
@@ -1083,12 +1138,10 @@ int grid_size(size_t lds) {
     return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fused_decode_kernel<DA>, kThreads, lds) != hipSuccess)
     return 0;
-  if (occ > 1) occ = 1;
-  cached_dev = dev;
-  cached_lds = lds;
-  cached_grid = occ * cus;
-  if (cached_grid > kDecodeMaxGrid) cached_grid = kDecodeMaxGrid;
-  return cached_grid;
+  int grid = (occ > 1 ? 1 : occ) * cus;
+  if (grid > kDecodeMaxGrid) grid = kDecodeMaxGrid;
+  if (grid > 0) cache[dev].store(((uint64_t)lds << 32) | (uint32_t)grid, std::memory_order_relaxed);
+  return grid;
 }
 
 template <class DA>
@@ -1163,6 +1216,8 @@ hipError_t launch_decode(const moe_layer_t& L, const uint16_t* x, int T, const u
   A.d_part = reinterpret_cast<uint64_t*>(base + c.d_part);
   A.s_part = reinterpret_cast<uint64_t*>(base + c.s_part);
   A.trace = reinterpret_cast<uint64_t*>(base + c.trace);
+  A.tagged = A.logits;
+  A.n_tagged = (uint32_t)((c.trace - c.logits) / 8);
   if (A.H == 3072 && A.I == 1024 && A.Is == 1024 && A.E == 128 && A.k == 4)
     return launch_instance<MiniMaxShape>(A, lds, stream);
   return launch_instance<AnyShape>(A, lds, stream);

@@ -30,6 +30,8 @@
 // next K-tile are loaded while the current one is multiplied.  Workgroups are
 // numbered so that each XCD receives a contiguous run of tiles: the tiles of
 // one expert's blocks then share that XCD's L2.
+#include <atomic>
+
 #include "internal.h"
 #include "mx_device.h"
 
@@ -187,7 +189,9 @@ __device__ __forceinline__ void wait_ktiles(int ahead) {
 // Main loop.  The operands of K-tile kt travel global -> LDS with direct
 // (LDS-destination) 16-byte loads into slot kt % NS of a ring, NS - 1 K-tiles
 // ahead of the matrix instructions; each wavefront moves TPW of the tile's
-// 1 KiB blocks.  Block scales of the whole K range sit in LDS from the start.
+// 1 KiB blocks and its share of the K-tile's block scales (4-byte direct
+// loads of the activation scales, the weight-scale words of the K-tile's
+// group of four).
 template <class F, int MODE, int WN>
 __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  // 2 x WN wavefronts
   using Gm = Geo<F, WN>;
@@ -509,12 +513,18 @@ template <class F, int MODE, int WN>
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
   using Gm = Geo<F, WN>;
   const size_t lds = (size_t)Gm::NS * Gm::STAGE + (size_t)Gm::BM * 4;
-  static size_t lds_set = 0;  // largest dynamic LDS size enabled so far for this kernel
-  if (lds > 64 * 1024 && lds > lds_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_kernel<F, MODE, WN>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return hipErrorInvalidValue;
-    lds_set = lds;
+  // the kernel's dynamic LDS limit is raised once per device (a lock-free
+  // flag per device; racing first calls both set the same attribute)
+  static std::atomic<bool> lds_set[kMaxDevices];
+  if (lds > 64 * 1024) {
+    const int dev = current_device();
+    if (dev < 0) return hipErrorInvalidDevice;
+    if (!lds_set[dev].load(std::memory_order_relaxed)) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_kernel<F, MODE, WN>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return hipErrorInvalidValue;
+      lds_set[dev].store(true, std::memory_order_relaxed);
+    }
   }
   hipLaunchKernelGGL((grouped_gemm_kernel<F, MODE, WN>), dim3(grid8(g.MB * g.NT)), dim3(Gm::THREADS), lds, stream,
                      g);
@@ -526,7 +536,9 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
 size_t grouped_ws_bytes(const moe_layer_t& L, int T) { return gcarve(L, T).total; }
 
 hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const uint16_t* residual,
-                          uint16_t* y, void* ws, hipStream_t stream) {
+                          uint16_t* y, void* ws, hipStream_t stream, const hipEvent_t* ev) {
+  // ev (optional): kGroupedSteps + 1 events, recorded before each step and at the end
+  auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
   const GCarve c = gcarve(L, T);
   char* base = reinterpret_cast<char*>(ws);
   auto at = [&](size_t off) { return base + off; };
@@ -542,11 +554,14 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
   uint8_t* as4 = reinterpret_cast<uint8_t*>(at(c.as4));
   float* d_part = reinterpret_cast<float*>(at(c.d_part));
   hipError_t err;
+  if ((err = mark(0)) != hipSuccess) return err;
   if ((err = launch_router_topk(L, x, T, router_tiled(T) ? reinterpret_cast<float*>(at(c.logits)) : nullptr, ids, w,
                                stream)) != hipSuccess) return err;
+  if ((err = mark(1)) != hipSuccess) return err;
   if ((err = launch_align_sort(ids, T, k, E, kBM, sorted, bexp, reinterpret_cast<int32_t*>(at(c.eoff)), npad,
                                at(c.sort_ws), stream)) != hipSuccess)
     return err;
+  if ((err = mark(2)) != hipSuccess) return err;
   // MXFP4 x (and, with a shared expert, MXFP8 x) from one read of x
   if (Is > 0)
     err = launch_quant_act_dual(x, T, H, xq4, xs4, reinterpret_cast<uint8_t*>(at(c.xq8)),
@@ -554,6 +569,7 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
   else
     err = launch_quant_act(x, T, H, MX_FMT_FP4, xq4, xs4, stream);
   if (err != hipSuccess) return err;
+  if ((err = mark(3)) != hipSuccess) return err;
 
   GemmArgs g{};
   g.T = T;
@@ -583,6 +599,7 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
     r.os = as4;
     if ((err = launch_gemm<FP4, GU_ROUTED, 2>(r, stream)) != hipSuccess) return err;
   }
+  if ((err = mark(4)) != hipSuccess) return err;
   // routed down: A = intermediate in sorted order, B = W2[e], out d_part[slot]
   {
     GemmArgs r = g;
@@ -602,11 +619,14 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
     r.d_part = d_part;
     if ((err = launch_gemm<FP4, DOWN_ROUTED, 2>(r, stream)) != hipSuccess) return err;
   }
+  if ((err = mark(5)) != hipSuccess) return err;
   if (Is == 0) {
     const size_t n = (size_t)T * H;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
                        T, k, H, w, d_part, residual, y);
-    return hipGetLastError();
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = mark(6)) != hipSuccess) return err;
+    return mark(7);
   }
   uint8_t* xq8 = reinterpret_cast<uint8_t*>(at(c.xq8));
   uint8_t* xs8 = reinterpret_cast<uint8_t*>(at(c.xs8));
@@ -632,6 +652,7 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
     r.os = as8;
     if ((err = launch_gemm<FP8, GU_SHARED, 2>(r, stream)) != hipSuccess) return err;
   }
+  if ((err = mark(6)) != hipSuccess) return err;
   // shared down + combine
   {
     GemmArgs r = g;
@@ -652,7 +673,7 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
     r.y = y;
     if ((err = launch_gemm<FP8, DOWN_SHARED, 2>(r, stream)) != hipSuccess) return err;
   }
-  return hipSuccess;
+  return mark(7);
 }
 
 }  // namespace mxmoe

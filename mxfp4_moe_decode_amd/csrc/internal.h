@@ -20,6 +20,16 @@ inline size_t tiled_scales_bytes(int rows, int cols) {
 
 __host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Per-device host tables (launch geometry, the no-allocation scratch) hold
+// this many devices.
+constexpr int kMaxDevices = 64;
+// The current HIP device, or -1 if it cannot be queried or is beyond the tables.
+inline int current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  return dev;
+}
+
 // ------------------------------------------------------------------ quantization
 hipError_t launch_quant_weights(const float* w, int rows, int cols, int fmt, int layout,
                                 uint8_t* codes, uint8_t* scales, hipStream_t stream);
@@ -68,7 +78,11 @@ constexpr size_t kDecodeGridOffset = 2 * 256;  // word holding the grid size of 
 
 // ------------------------------------------------------------------ grouped path
 size_t grouped_ws_bytes(const moe_layer_t& L, int T);
+// Launch steps of the grouped path: router, sort, x quantization, routed
+// gate/up, routed down, shared gate/up (without a shared expert: the
+// combine), shared down with the combine.
+constexpr int kGroupedSteps = 7;
 hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const uint16_t* residual,
-                          uint16_t* y, void* ws, hipStream_t stream);
+                          uint16_t* y, void* ws, hipStream_t stream, const hipEvent_t* ev = nullptr);
 
 }  // namespace mxmoe

@@ -1,6 +1,7 @@
-// Device helpers shared by the gfx950 kernels: MX element conversion in
-// integer arithmetic, scaled FP4/FP8 matrix-core wrappers, the router's
-// fixed-order dot product and wavefront reductions.
+// Device helpers shared by the gfx950 kernels: MX block quantization (block
+// exponent from the exponent bits, elements by the hardware conversions or the
+// branch-free software rounding), scaled FP4/FP8 matrix-core wrappers, the
+// router's fixed-order dot product and wavefront reductions.
 #pragma once
 
 #include <hip/hip_runtime.h>

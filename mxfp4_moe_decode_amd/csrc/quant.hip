@@ -1,7 +1,8 @@
 // MX quantization kernels: static weight quantization (fp32 -> MXFP4 / MXFP8,
 // row-major or tiled) and dynamic MXFP4 activation quantization (bf16 -> MXFP4).
-// One thread per 32-element block; the conversion is the integer routine in
-// mx_device.h, so results are bit-exact.
+// One thread per 32-element block.  Each element is scaled by 2^-e (exact)
+// and converted by gfx950's rounding fp32 -> E2M1 / E4M3 instructions
+// (quant_block32 in mx_device.h), so the codes are the specification's.
 #include "internal.h"
 #include "mx_device.h"
 

@@ -15,6 +15,13 @@ intermediate sizes are not on the pages and are taken as 3072 / 1024):
 * ``chain8``   T=4,    8 layers with distinct weights, Zipf(s=1.2) router bias,
                residual add between layers
 * ``prefill``  T=8192, same layer as ``decode1``
+* ``tp4``      T=16, the per-GPU share of the layer under 4-way tensor
+               parallelism over the intermediate dimension: H=3072, E=128,
+               k=4, I=256, shared I_s=256
+* ``wide``     T=16, H=3072, 256 experts top-8, I=256, shared I_s=256
+* ``odd``      T=16, H=1280, 16 experts top-3, I=384, shared I_s=640: K-tile
+               counts 10 / 3 / 5, so the dot products split into 2 / 1 / 1
+               K-chunks and the scale groups end part-filled
 
 Draws: expert and shared weights fp32 N(0, 0.02); router weights fp32 N(0, 0.02)
 (``decode16``: uniform); activations N(0, 1) stored as bf16 (round to nearest
@@ -42,6 +49,12 @@ WORKLOADS = {
                    zipf=1.2, residual=True),
     "prefill": dict(T=8192, H=3072, E=128, k=4, I=1024, I_s=1024, router="normal", layers=1,
                     zipf=None, residual=False),
+    "tp4": dict(T=16, H=3072, E=128, k=4, I=256, I_s=256, router="normal", layers=1,
+                zipf=None, residual=False),
+    "wide": dict(T=16, H=3072, E=256, k=8, I=256, I_s=256, router="normal", layers=1,
+                 zipf=None, residual=False),
+    "odd": dict(T=16, H=1280, E=16, k=3, I=384, I_s=640, router="normal", layers=1,
+                zipf=None, residual=False),
 }
 _WID = {name: i + 1 for i, name in enumerate(WORKLOADS)}
 _TAG = {"router": 1, "w13": 2, "w2": 3, "ws13": 4, "ws2": 5, "bias": 6, "x": 7}

@@ -120,8 +120,11 @@ class Layer:
 
     def __init__(self, H, I, E, k, I_s, router_w, router_bias,
                  w13_codes, w13_scales, w2_codes, w2_scales,
-                 ws13_codes=None, ws13_scales=None, ws2_codes=None, ws2_scales=None):
+                 ws13_codes=None, ws13_scales=None, ws2_codes=None, ws2_scales=None, shared_folded=False):
         self.H, self.I, self.E, self.k, self.I_s = H, I, E, k, I_s
+        # shared_folded: expert E of the (E + 1)-expert table is the shared
+        # expert in MXFP4, selected for every token with weight 1 (I_s is 0)
+        self.shared_folded = shared_folded
         self.router_w = np.asarray(router_w, np.float64)
         self.router_bias = None if router_bias is None else np.asarray(router_bias, np.float64)
         self.w13_codes, self.w13_scales = w13_codes, w13_scales
@@ -151,6 +154,34 @@ def quantize_layer(H, I, E, k, I_s, router_w, router_bias, w13, w2, ws13=None, w
     return Layer(H, I, E, k, I_s, router_w, router_bias, c13, s13, c2, s2, **sc)
 
 
+class _Appended:
+    """Sequence view: ``base`` (indexed by expert) with one more entry at E."""
+
+    def __init__(self, base, E, extra):
+        self.base, self.E, self.extra = base, E, extra
+
+    def __getitem__(self, e):
+        return self.extra if int(e) == self.E else self.base[e]
+
+
+def fold_shared_expert(layer):
+    """The layer with its MXFP8 shared expert re-quantized to MXFP4 and folded
+    into the routed expert table as expert E, which every token selects with
+    weight 1 (the AITER fused MoE "with the shared expert optionally folded
+    into the expert table", article "MiniMax-M3.1 on AMD Instinct GPUs: Day-0
+    support and optimization", section "Serving with vLLM / What we
+    Optimized"; re-quantization to MXFP4 as in vLLM PR #64273, section
+    "Purpose").  Requires I_s == I (the table's experts share one shape)."""
+    if layer.I_s != layer.I:
+        raise ValueError("folding needs the shared expert's intermediate size to equal the routed one")
+    c13, s13 = mx.requant_fp8_to_fp4(layer.ws13_codes, layer.ws13_scales)
+    c2, s2 = mx.requant_fp8_to_fp4(layer.ws2_codes, layer.ws2_scales)
+    E = layer.E
+    return Layer(layer.H, layer.I, E, layer.k, 0, layer.router_w, layer.router_bias,
+                 _Appended(layer.w13_codes, E, c13), _Appended(layer.w13_scales, E, s13),
+                 _Appended(layer.w2_codes, E, c2), _Appended(layer.w2_scales, E, s2), shared_folded=True)
+
+
 # ---------------------------------------------------------------------------
 # Expert FFN (SwiGLU) on MX operands
 # ---------------------------------------------------------------------------
@@ -167,7 +198,9 @@ def mx_ffn(x, w13_codes, w13_scales, w2_codes, w2_scales, fmt):
         xq = MX(x); g, u = xq . W13 gate / up rows (fp64, then fp32)
         a  = fp32(silu(g) * u); aq = MX(a); d = aq . W2 rows (fp64)
 
-    Returns d [n, H] fp64 and the intermediate codes for inspection."""
+    Returns d [n, H] fp64 and, for inspection, the intermediates: the
+    dequantized operands (xq, w13, aq, w2), g, u, a and the intermediate's
+    codes and scales."""
     I = w13_codes.shape[0] // 2
     xc, xs = mx.mx_quantize(x, fmt)
     xq = mx.mx_dequantize(xc, xs, fmt)
@@ -179,22 +212,25 @@ def mx_ffn(x, w13_codes, w13_scales, w2_codes, w2_scales, fmt):
     aq = mx.mx_dequantize(ac, as_, fmt)
     w2 = mx.mx_dequantize(w2_codes, w2_scales, fmt)
     d = aq @ w2.T
-    return d, {"x_codes": xc, "x_scales": xs, "g": g, "u": u, "a": a,
-               "a_codes": ac, "a_scales": as_}
+    return d, {"x_codes": xc, "x_scales": xs, "g": g, "u": u, "a": a, "a_codes": ac, "a_scales": as_,
+               "xq": xq, "w13": w13, "aq": aq, "w2": w2, "fmt": fmt}
 
 
 # ---------------------------------------------------------------------------
 # The layer
 # ---------------------------------------------------------------------------
 
-def moe_layer(x_bits, layer, residual_bits=None, ids=None):
+def moe_layer(x_bits, layer, residual_bits=None, ids=None, on_ffn=None):
     """One MoE layer on bf16 rows ``x_bits`` [T, H] (uint16 patterns).
 
     ``ids`` may override the routing choice (used only where the top-k is a
     near-tie and another choice is equally valid); the weights are then the
-    softmax over the given experts' logits.  Returns a dict with ``y_bits``
-    (bf16 output patterns), ``y`` (fp64 before rounding), ``logits``,
-    ``ids``, ``weights``, ``d`` [T, k, H], ``s`` [T, H]."""
+    softmax over the given experts' logits, in the given order.  ``on_ffn``,
+    if given, is called after each expert FFN as on_ffn(kind, e, rows, info)
+    with kind "routed" (rows: the (t, j) pairs of expert e) or "shared" (e and
+    rows None) and mx_ffn's intermediates; it changes nothing.  Returns a dict
+    with ``y_bits`` (bf16 output patterns), ``y`` (fp64 before rounding),
+    ``logits``, ``ids``, ``weights``, ``d`` [T, k, H], ``s`` [T, H]."""
     x = mx.bf16_bits_to_f64(x_bits)
     T, H = x.shape
     k = layer.k
@@ -212,14 +248,26 @@ def moe_layer(x_bits, layer, residual_bits=None, ids=None):
     for e in sorted(set(int(v) for v in ids.reshape(-1))):
         rows = [(t, j) for t in range(T) for j in range(k) if ids[t, j] == e]
         xt = np.stack([x[t] for t, _ in rows])
-        de, _ = mx_ffn(xt, layer.w13_codes[e], layer.w13_scales[e],
-                       layer.w2_codes[e], layer.w2_scales[e], "fp4")
+        de, info = mx_ffn(xt, layer.w13_codes[e], layer.w13_scales[e],
+                          layer.w2_codes[e], layer.w2_scales[e], "fp4")
+        if on_ffn is not None:
+            on_ffn("routed", e, rows, info)
         for r, (t, j) in enumerate(rows):
             d[t, j] = de[r]
     s = np.zeros((T, H))
     if layer.I_s > 0:
-        s, _ = mx_ffn(x, layer.ws13_codes, layer.ws13_scales,
-                      layer.ws2_codes, layer.ws2_scales, "fp8")
+        s, info = mx_ffn(x, layer.ws13_codes, layer.ws13_scales,
+                         layer.ws2_codes, layer.ws2_scales, "fp8")
+        if on_ffn is not None:
+            on_ffn("shared", None, None, info)
+    elif layer.shared_folded:
+        # expert E, selected by every token with weight 1: its output is added
+        # like the shared expert's, after the routed experts
+        E = layer.E
+        s, info = mx_ffn(x, layer.w13_codes[E], layer.w13_scales[E],
+                         layer.w2_codes[E], layer.w2_scales[E], "fp4")
+        if on_ffn is not None:
+            on_ffn("shared", E, None, info)
     y = np.einsum("tj,tjh->th", w, d) + s
     if residual_bits is not None:
         y = y + mx.bf16_bits_to_f64(residual_bits)

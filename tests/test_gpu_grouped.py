@@ -5,8 +5,11 @@
 * against the fused decode kernel, bit for bit, at the full MiniMax-shaped
   sizes for 1..16 rows (both paths promise the same arithmetic), with and
   without the residual;
-* at the 8192-row prefill size: sampled rows against the oracle, and against
-  the decode kernel run on those rows alone (bit for bit).
+* at the 8192-row prefill size: every row bit for bit against the decode
+  kernel, and the rows at 128-row block boundaries and segment tails of
+  twelve experts against the oracle;
+* at the TP4 per-GPU shape, with 256 experts top-8, and at a shape whose K
+  splits into 2 / 1 / 1 chunks (test_gpu_shapes.py).
 """
 
 import numpy as np
@@ -14,7 +17,7 @@ import pytest
 import torch
 
 from mxfp4_moe_decode_amd import binding, synth
-from oracle import moe
+from oracle import moe, mx
 from tests import helpers
 
 pytestmark = pytest.mark.gpu
@@ -59,21 +62,8 @@ def _decode(gl, x_bits, residual_bits=None, ws=None):
             np.concatenate([o[2] for o in out]))
 
 
-def _oracle_compare(cfg, gl, ol, x_bits, y, residual_bits=None, layer=0):
-    """Oracle comparison; rows whose routing is a near tie are recomputed with
-    the GPU router's (valid) choice."""
-    ref = moe.moe_layer(x_bits, ol, residual_bits)
-    ids_g, _, logits = binding.moe_router_topk(gl, _dev(x_bits), want_logits=True)
-    ids_g = ids_g.cpu().numpy()
-    if not np.array_equal(ids_g, ref["ids"]):
-        logits = logits.cpu().numpy()
-        bound = helpers.logit_bound(x_bits, synth.router_weights(cfg, layer), ref["logits"])
-        helpers.check_logits(logits, ref["logits"], bound)
-        helpers.check_topk(ids_g, logits, ref["logits"], bound, cfg["k"])
-        ref = moe.moe_layer(x_bits, ol, residual_bits, ids=ids_g)
-    err, within = helpers.check_layer_output(y, ref)
-    print(f"[grouped] {cfg['name']} T={x_bits.shape[0]}: max row err {err:.3e}, within 1 ulp {within:.4f}",
-          flush=True)
+def _oracle_compare(cfg, gl, ol, x_bits, y, residual_bits=None, layer=0, label=""):
+    helpers.compare_with_oracle(cfg, gl, ol, x_bits, y, residual_bits=residual_bits, layer=layer, label=label)
 
 
 @pytest.mark.parametrize("T", [1, 4, 37, 1000])
@@ -113,18 +103,46 @@ def test_grouped_equals_decode_ragged_with_residual():
     assert np.array_equal(yg, yd)
 
 
+def _boundary_rows(ids, experts, block_m=128):
+    """Rows whose slots sit at the first and last position of each 128-row
+    block of the given experts' segments, and at each segment's ragged tail
+    (the sorted order is by slot, i.e. by row, inside a segment)."""
+    rows = set()
+    T, k = ids.shape
+    for e in experts:
+        seg = (np.flatnonzero(ids.reshape(-1) == e) // k).tolist()
+        n = len(seg)
+        for p in range(0, n, block_m):
+            rows.add(seg[p])
+            rows.add(seg[min(p + block_m - 1, n - 1)])
+        rows.add(seg[n - 1])
+        if n >= 2:
+            rows.add(seg[n - 2])
+    return sorted(rows)
+
+
 @pytest.mark.timeout(1200)
-def test_grouped_prefill_8192_sampled_rows():
-    """Full prefill size: 8192 rows, about 256 slots per expert.  Sampled
-    rows (first, last, and spread ones) against the oracle and against the
-    decode kernel run on those rows alone."""
+def test_grouped_prefill_8192_every_row():
+    """Full prefill size: 8192 rows, about 256 slots per expert.  Every row
+    equals the fused decode kernel run on it (512 calls of 16 rows, bit for
+    bit: both promise the same arithmetic).  Rows at the first and last
+    position of the 128-row blocks of twelve experts' segments and at their
+    ragged tails are compared with the oracle."""
     cfg, gl, ol = _layers("prefill")
     x = synth.activations(cfg)
     assert x.shape == (8192, 3072)
     y = _grouped(gl, x)
-    rows = np.array([0, 1, 2047, 4444, 8190, 8191])
-    yd, _, _ = _decode(gl, x[rows])
-    assert np.array_equal(y[rows], yd)
-    _oracle_compare(cfg, gl, ol, x[rows], y[rows])
-    # every row is finite bf16 (no NaN/Inf pattern: exponent field not all ones)
-    assert not np.any((y & 0x7f80) == 0x7f80)
+    assert not np.any((y & 0x7f80) == 0x7f80)  # finite bf16 everywhere
+    ws = binding.decode_workspace(gl)
+    yd, _, _ = _decode(gl, x, ws=ws)
+    mismatch = np.flatnonzero(np.any(y != yd, axis=1))
+    assert mismatch.size == 0, f"{mismatch.size} rows differ from the decode kernel, first {mismatch[:8]}"
+    logits = moe.router_logits(mx.bf16_bits_to_f64(x), ol.router_w, ol.router_bias)
+    ids, _ = moe.select_topk(logits, cfg["k"])
+    experts = [0, 11, 23, 37, 50, 63, 64, 77, 90, 101, 115, 127]
+    rows = _boundary_rows(ids, experts)
+    assert len(rows) >= 64, len(rows)
+    print(f"[grouped] oracle on {len(rows)} boundary rows", flush=True)
+    xr = x[rows]
+    helpers.prefetch(ol, np.unique(ids[rows]))
+    _oracle_compare(cfg, gl, ol, xr, y[rows], label="block boundaries")

@@ -7,6 +7,7 @@ import torch
 
 from mxfp4_moe_decode_amd import binding, synth
 from oracle import mx
+from tests import layout
 
 pytestmark = pytest.mark.gpu
 
@@ -66,7 +67,7 @@ def test_weight_quant_tiled_matches_oracle_layout(fmt, shape):
     w = (rng.standard_normal(shape) * 0.02).astype(np.float32)
     codes, scales = binding.mx_quantize_weights(torch.from_numpy(w).cuda(), fmt, "tiled")
     rc, rs = mx.mx_quantize(w.astype(np.float64), fmt)
-    tc, ts = mx.tile_weight(rc, rs, fmt)
+    tc, ts = layout.tile_weight(rc, rs, fmt)
     assert np.array_equal(codes.cpu().numpy(), tc)
     assert np.array_equal(scales.cpu().numpy(), ts)
 

@@ -208,3 +208,82 @@ def test_router_logits_are_fp32_rounded_exact_products():
         for e in range(3):
             exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(xf[t], wr[e]))
             assert l[t, e] == float(np.float32(float(exact)))
+
+
+def test_ids_override_with_the_topk_itself_changes_nothing():
+    layer, rng = _random_layer(I_s=64)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((6, 256)).astype(np.float32))
+    out = moe.moe_layer(x, layer)
+    again = moe.moe_layer(x, layer, ids=out["ids"])
+    assert np.array_equal(again["y_bits"], out["y_bits"])
+    np.testing.assert_allclose(again["weights"], out["weights"], rtol=1e-15)
+
+
+def test_ids_override_hand_worked():
+    # The hand layer's logits are (1, -1).  Forcing the second expert alone:
+    # weight 1 and d = 1.5 (its hand-worked output, see the two-expert case),
+    # not the top choice's -0.5.  Forcing both in swapped order: the weights
+    # follow the order given, softmax of (-1, 1), and y is unchanged.
+    layer = _hand_layer(k=1)
+    x = _bf16([_row(1.0, 32)])
+    out = moe.moe_layer(x, layer, ids=np.array([[1]]))
+    assert out["weights"][0, 0] == 1.0
+    assert np.all(out["y"] == 1.5)
+    layer2 = _hand_layer(k=2)
+    out2 = moe.moe_layer(x, layer2, ids=np.array([[1, 0]]))
+    w0 = 1.0 / (1.0 + math.exp(-2.0))
+    np.testing.assert_allclose(out2["weights"][0], [1.0 - w0, w0], rtol=1e-14)
+    np.testing.assert_allclose(out2["y"], (1.0 - w0) * 1.5 + w0 * -0.5, rtol=1e-14)
+
+
+def test_ids_override_any_order_of_all_experts_is_dense_mixture():
+    # k = E with every row's experts given in a shuffled order: the weights
+    # are the softmax of the logits in that order, so the layer is still the
+    # dense softmax mixture.
+    layer, rng = _random_layer(E=4, k=4)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((5, 256)).astype(np.float32))
+    ids = np.stack([rng.permutation(4) for _ in range(5)]).astype(np.int32)
+    out = moe.moe_layer(x, layer, ids=ids)
+    xf = mx.bf16_bits_to_f64(x)
+    logits = (xf @ layer.router_w.T).astype(np.float32).astype(np.float64)
+    p = scipy.special.softmax(logits, axis=1)
+    np.testing.assert_allclose(out["weights"], np.take_along_axis(p, ids, axis=1), rtol=1e-12)
+    dense = np.zeros_like(xf)
+    for e in range(4):
+        d, _ = moe.mx_ffn(xf, layer.w13_codes[e], layer.w13_scales[e], layer.w2_codes[e], layer.w2_scales[e], "fp4")
+        dense += p[:, e:e + 1] * d
+    np.testing.assert_allclose(out["y"], dense, rtol=1e-12, atol=1e-12)
+
+
+def test_folded_shared_expert_hand_worked():
+    # The hand layer with its shared expert (gate 1.5, up 2, down 0.25; all on
+    # the E2M1 grid, so the MXFP8 -> MXFP4 weight re-quantization is exact)
+    # folded in as expert 2 with weight 1.  Its activations are now MXFP4:
+    # xq = 1; g = 1.5, u = 2 -> a = silu(1.5) * 2 = 2.4527235 -> block exponent
+    # -1, 4.905 -> nearest 4 -> aq = 2.0 (MXFP8 gave 2.5); s = 2.0 * 0.25 = 0.5.
+    # Routed part -0.5 as before, residual 1: y = 1.0.
+    layer = moe.fold_shared_expert(_hand_layer(k=1, with_shared=True, I_s=32))
+    assert layer.shared_folded and layer.I_s == 0 and layer.E == 2
+    x = _bf16([_row(1.0, 32)])
+    r = _bf16([np.full(32, 1.0, np.float32)])
+    out = moe.moe_layer(x, layer, residual_bits=r)
+    assert out["ids"].tolist() == [[0]]
+    assert np.all(out["s"] == 0.5)
+    assert np.all(out["y"] == 1.0)
+
+
+def test_folded_layer_routes_over_the_original_experts_only():
+    # The folded expert is not a router candidate: ids stay in 0..E-1 and the
+    # routed part is unchanged; only the always-on part differs.
+    layer, rng = _random_layer(I=128, I_s=128)
+    folded = moe.fold_shared_expert(layer)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((6, 256)).astype(np.float32))
+    a = moe.moe_layer(x, layer)
+    b = moe.moe_layer(x, folded)
+    assert np.array_equal(a["ids"], b["ids"]) and np.array_equal(a["d"], b["d"])
+    assert b["ids"].max() < layer.E
+    # the folded part is the MXFP4 FFN of the re-quantized shared weights
+    c13, s13 = mx.requant_fp8_to_fp4(layer.ws13_codes, layer.ws13_scales)
+    c2, s2 = mx.requant_fp8_to_fp4(layer.ws2_codes, layer.ws2_scales)
+    s_ref, _ = moe.mx_ffn(mx.bf16_bits_to_f64(x), c13, s13, c2, s2, "fp4")
+    assert np.array_equal(b["s"], s_ref)

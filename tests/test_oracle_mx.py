@@ -9,6 +9,7 @@ import pytest
 import torch
 
 from oracle import mx
+from tests import layout
 from tests.conftest import read_golden
 
 
@@ -215,7 +216,7 @@ def test_tiled_layout_is_a_bijection_with_hand_checked_entries(fmt):
     maxc = 16 if fmt == "fp4" else 256
     codes = rng.integers(0, maxc, (N, K)).astype(np.uint8)
     scales = rng.integers(100, 150, (N, K // 32)).astype(np.uint8)
-    tc, ts = mx.tile_weight(codes, scales, fmt)
+    tc, ts = layout.tile_weight(codes, scales, fmt)
     TB = 1024 if fmt == "fp4" else 2048
     assert tc.size == N // 16 * (K // 128) * TB
     assert ts.size == N // 16 * 2 * 256
@@ -232,3 +233,62 @@ def test_tiled_layout_is_a_bijection_with_hand_checked_entries(fmt):
     assert ts[((1 * 2 + 1) * 64 + 4 + 48) * 4 + 0] == scales[20, 19]
     # padding (K-tiles 5..7) holds 127
     assert ts[((0 * 2 + 1) * 64 + 0) * 4 + 1] == 127
+
+
+def test_requant_fp8_to_fp4_hand_worked():
+    # One MXFP8 block, scale 2^-7: element 0 = E4M3 0x7A (320) -> 2.5, element
+    # 1 = E4M3 0xE2 (-40) -> -0.3125.  MXFP4: block max 2.5 -> exponent
+    # floor(log2 2.5) - 2 = -1; 2.5 * 2 = 5 lies halfway between 4 (code 6) and
+    # 6 (code 7) -> even code 6, value 4 * 2^-1 = 2.0 (the loss); -0.3125 * 2 =
+    # -0.625 -> nearest 0.5 -> code 0x9, value -0.25.
+    c8 = np.zeros((1, 32), np.uint8)
+    c8[0, 0], c8[0, 1] = 0x7A, 0xE2
+    s8 = np.array([[127 - 7]], np.uint8)
+    c4, s4 = mx.requant_fp8_to_fp4(c8, s8)
+    assert s4.tolist() == [[126]]
+    assert c4[0, 0] == 6 and c4[0, 1] == 0x9 and not c4[0, 2:].any()
+    v = mx.mx_dequantize(c4, s4, "fp4")
+    assert v[0, 0] == 2.0 and v[0, 1] == -0.25
+
+
+def test_requant_fp8_to_fp4_brute_force_every_e4m3_code():
+    # Block: element 0 carries every finite E4M3 code in turn, element 1 is
+    # fixed at +448 (the E4M3 maximum), so the MXFP4 block exponent is
+    # floor(log2(448 * X)) - 2 = 6 + (s - 127) for scale code s.  Each code's
+    # requantized value must be the E2M1 grid point nearest to its exact value
+    # (found by exhaustive search over the 8 magnitudes, ties to the even code).
+    grid = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    for s in (120, 127, 131):
+        codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+        c8 = np.zeros((codes.size, 32), np.uint8)
+        c8[:, 0] = codes
+        c8[:, 1] = 0x7E  # 448
+        s8 = np.full((codes.size, 1), s, np.uint8)
+        c4, s4 = mx.requant_fp8_to_fp4(c8, s8)
+        e = 6 + (s - 127)
+        assert np.all(s4 == e + 127)
+        for i, c in enumerate(codes.tolist()):
+            v = mx.e4m3_value(c) * 2.0 ** (s - 127) / 2.0 ** e
+            mag = abs(v)
+            dist = [abs(mag - g) for g in grid]
+            best = min(dist)
+            cands = [j for j in range(8) if dist[j] == best]
+            j = cands[0] if len(cands) == 1 else [j for j in cands if j % 2 == 0][0]
+            if mag > 6:
+                j = 7
+            want = j | (8 if (c & 0x80) else 0)
+            assert c4[i, 0] == want, (s, hex(c), v, c4[i, 0], want)
+        # the fixed 448 element: 448 * X / 2^e = 7 -> saturates to 6 (code 7)
+        assert np.all(c4[:, 1] == 7)
+
+
+def test_requant_fp8_to_fp4_lossless_on_the_fp4_grid():
+    # Values that are E2M1 values times a common power of two survive the
+    # round trip fp32 -> MXFP8 -> MXFP4 unchanged.
+    rng = np.random.default_rng(5)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    w = rng.choice(grid, size=(16, 128)) * rng.choice([-1.0, 1.0], size=(16, 128)) * 2.0 ** -9
+    w[:, ::32] = 6 * 2.0 ** -9  # every block reaches the top binade
+    c8, s8 = mx.mx_quantize(w, "fp8")
+    c4, s4 = mx.requant_fp8_to_fp4(c8, s8)
+    assert np.array_equal(mx.mx_dequantize(c4, s4, "fp4"), w)
