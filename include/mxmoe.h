@@ -213,6 +213,28 @@ moe_status fused_moe_mxfp4_decode(const moe_layer_t* layer, const uint16_t* x, i
                                   int32_t* topk_ids_out, float* topk_w_out, hipStream_t stream);
 
 /*
+ * fused_moe_mxfp4_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is the library's own: a
+ * static device array of 8 MiB per GPU, held until the process ends, whose
+ * address is looked up once per device.  The first call on a device also
+ * zero-fills it, with a kernel on `stream` ahead of the layer's launch.  This
+ * call allocates nothing and calls no allocating routine.
+ *   arguments, results and arithmetic as for fused_moe_mxfp4_decode.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (different streams, or concurrent host threads with their first
+ * calls) race on it and must not be made.  The array keeps the last call's
+ * contents; the call-tag protocol of the decode workspace makes that safe for
+ * the next call.  A layer whose decode workspace (moe_workspace_bytes with
+ * path 0) exceeds 8 MiB gives MOE_ERR_WORKSPACE_TOO_SMALL.  A timed-out wait
+ * poisons the array for the rest of the process (outputs NaN, see
+ * moe_workspace_bytes); moe_decode_status cannot inspect it.
+ */
+moe_status fused_moe_mxfp4_decode_noalloc(const moe_layer_t* layer, const uint16_t* x, int T,
+                                          const uint16_t* residual, uint16_t* y, int32_t* topk_ids_out,
+                                          float* topk_w_out, hipStream_t stream);
+
+/*
  * The layer for any number of rows (prefill and steps wider than 16 rows,
  * which the pages keep on the standard path: article section "Performance,
  * mono decode on vs off").  Several launches: router + top-k, token sort,

@@ -20,7 +20,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARGUMENT", -2: "MOE_ERR_UNSUPPORTED"
 EXPORTS = [
     "mx_codes_bytes", "mx_scales_bytes", "mx_quantize_weights", "mxfp4_quant_act",
     "moe_router_topk", "moe_align_sort_capacity", "moe_align_sort_workspace_bytes", "moe_align_sort",
-    "moe_workspace_bytes", "moe_workspace_init", "fused_moe_mxfp4_decode", "fused_moe_mxfp4_grouped", "fused_moe_mxfp4_grouped_timed",
+    "moe_workspace_bytes", "moe_workspace_init", "fused_moe_mxfp4_decode", "fused_moe_mxfp4_decode_noalloc",
+    "fused_moe_mxfp4_grouped", "fused_moe_mxfp4_grouped_timed",
     "moe_decode_status", "moe_decode_trace", "moe_status_string",
 ]
 
@@ -69,6 +70,7 @@ def load():
         "moe_workspace_bytes": (Z, [LP, I, I]),
         "moe_workspace_init": (S, [P, Z, P]),
         "fused_moe_mxfp4_decode": (S, [LP, P, I, P, P, P, Z, P, P, P]),
+        "fused_moe_mxfp4_decode_noalloc": (S, [LP, P, I, P, P, P, P, P]),
         "fused_moe_mxfp4_grouped": (S, [LP, P, I, P, P, P, Z, P]),
         "fused_moe_mxfp4_grouped_timed": (S, [LP, P, I, P, P, P, Z, P, P]),
         "moe_decode_status": (S, [P, Z]),
@@ -272,6 +274,22 @@ def fused_moe_mxfp4_decode(layer, x, residual=None, out=None, workspace=None, re
     _check("fused_moe_mxfp4_decode", load().fused_moe_mxfp4_decode(
         layer.c, _ptr(x), T, _ptr(residual), _ptr(out), _ptr(workspace), workspace.numel(),
         _ptr(ids), _ptr(w), _stream()))
+    return (out, ids, w) if return_routing else out
+
+
+def fused_moe_mxfp4_decode_noalloc(layer, x, residual=None, out=None, return_routing=False):
+    """fused_moe_mxfp4_decode on the library's own per-device workspace (no
+    workspace argument; see mxmoe.h for the sharing rules)."""
+    _need_cuda(x, residual, out)
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    ids = w = None
+    if return_routing:
+        ids = torch.empty(T, layer.top_k, dtype=torch.int32, device=x.device)
+        w = torch.empty(T, layer.top_k, dtype=torch.float32, device=x.device)
+    _check("fused_moe_mxfp4_decode_noalloc", load().fused_moe_mxfp4_decode_noalloc(
+        layer.c, _ptr(x), T, _ptr(residual), _ptr(out), _ptr(ids), _ptr(w), _stream()))
     return (out, ids, w) if return_routing else out
 
 

@@ -134,6 +134,21 @@ moe_status fused_moe_mxfp4_decode(const moe_layer_t* layer, const uint16_t* x, i
   return from_hip(launch_decode(*layer, x, T, residual, y, ws, topk_ids_out, topk_w_out, stream));
 }
 
+moe_status fused_moe_mxfp4_decode_noalloc(const moe_layer_t* layer, const uint16_t* x, int T,
+                                          const uint16_t* residual, uint16_t* y, int32_t* topk_ids_out,
+                                          float* topk_w_out, hipStream_t stream) {
+  const moe_status st = check_layer(layer);
+  if (st != MOE_OK) return st;
+  if (!x || !y || T <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (T > kDecodeMaxT || !decode_supported(*layer)) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<const void*>(y) == static_cast<const void*>(x)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(y, 4) || !aligned(residual, 4)) return MOE_ERR_INVALID_ARGUMENT;
+  if (decode_ws_bytes(*layer) > kNoAllocScratchBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = noalloc_scratch(stream);
+  if (!ws) return MOE_ERR_HIP;
+  return from_hip(launch_decode(*layer, x, T, residual, y, ws, topk_ids_out, topk_w_out, stream));
+}
+
 namespace {
 moe_status grouped_call(const moe_layer_t* layer, const uint16_t* x, int T, const uint16_t* residual, uint16_t* y,
                         void* ws, size_t ws_bytes, hipStream_t stream, const hipEvent_t* events) {

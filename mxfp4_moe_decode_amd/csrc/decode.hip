@@ -42,6 +42,7 @@
 // block; the combine adds sum_j w_j d_j in j order, then s, then the residual,
 // and rounds once to bf16.  Output row t therefore depends on x[t] only.
 #include <atomic>
+#include <mutex>
 
 #include "internal.h"
 #include "mx_device.h"
@@ -1221,6 +1222,36 @@ hipError_t launch_decode(const moe_layer_t& L, const uint16_t* x, int T, const u
   if (A.H == 3072 && A.I == 1024 && A.Is == 1024 && A.E == 128 && A.k == 4)
     return launch_instance<MiniMaxShape>(A, lds, stream);
   return launch_instance<AnyShape>(A, lds, stream);
+}
+
+// ------------------------------------------------------------------ no-allocation variant
+// The workspace of fused_moe_mxfp4_decode_noalloc: a file-scope device array,
+// one copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it only stands for the symbol): each
+// device's address comes from hipGetSymbolAddress, taken once per device with
+// that device current, and only that address is used.
+namespace {
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;                       // guards the first call on each device
+std::atomic<void*> g_scratch_ptr[kMaxDevices];  // this device's copy of `scratch`, once set up
+}  // namespace
+
+void* noalloc_scratch(hipStream_t stream) {
+  const int dev = current_device();
+  if (dev < 0) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+  // The decode protocol needs zero-filled words before its first call; the
+  // fill is a kernel on the caller's stream, ordered before that call.
+  if (launch_fill_u32(ptr, kNoAllocScratchBytes / 4, 0u, stream) != hipSuccess) return nullptr;
+  g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  return ptr;
 }
 
 }  // namespace mxmoe

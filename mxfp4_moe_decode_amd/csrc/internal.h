@@ -75,6 +75,11 @@ constexpr size_t kDecodeStatusOffset = 0;
 size_t decode_sync_bytes(const moe_layer_t& L);
 size_t decode_trace_offset(const moe_layer_t& L);
 constexpr size_t kDecodeGridOffset = 2 * 256;  // word holding the grid size of the last call
+// No-allocation decode: the library's own per-device workspace (a file-scope
+// device array of this many bytes).  Returns its address on the current
+// device, zero-filling it on `stream` the first time; nullptr on failure.
+constexpr size_t kNoAllocScratchBytes = 8u << 20;
+void* noalloc_scratch(hipStream_t stream);
 
 // ------------------------------------------------------------------ grouped path
 size_t grouped_ws_bytes(const moe_layer_t& L, int T);
