@@ -39,11 +39,12 @@ HBM_PEAK_GBS = 8000.0
 FP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 matrix peak (published)
 
 
-def layer_bytes(H, I, E, Is, D, T, residual=False):
+def layer_bytes(H, I, E, Is, D, T, residual=False, folded=False):
     """Algorithmic HBM bytes of one layer call: router weights, D routed
-    experts (W13 + W2 codes and scales), the shared expert, x, y (+ residual)."""
+    experts (W13 + W2 codes and scales), the shared expert (MXFP8; folded: one
+    more MXFP4 expert of the table), x, y (+ residual)."""
     routed = 3 * I * H * 17 // 32
-    shared = 3 * Is * H * 33 // 32
+    shared = routed if folded else 3 * Is * H * 33 // 32
     return E * H * 4 + D * routed + shared + (3 if residual else 2) * T * H * 2
 
 
@@ -69,7 +70,7 @@ def load_traffic(workload):
     return entry.get("bytes_per_launch")
 
 
-def build_layers(binding, synth, name, count):
+def build_layers(binding, synth, name, count, fold=False):
     import torch
     cfg = synth.workload(name)
     layers = []
@@ -78,14 +79,14 @@ def build_layers(binding, synth, name, count):
             cfg["H"], cfg["I"], cfg["E"], cfg["k"], cfg["I_s"], synth.router_weights(cfg, li),
             synth.router_bias(cfg, li), lambda e, li=li: synth.device_expert_w13(cfg, li, e),
             lambda e, li=li: synth.device_expert_w2(cfg, li, e),
-            synth.device_shared_w13(cfg, li), synth.device_shared_w2(cfg, li)))
+            synth.device_shared_w13(cfg, li), synth.device_shared_w2(cfg, li), fold_shared=fold))
     torch.cuda.synchronize()
     return cfg, layers
 
 
-def time_decode(binding, synth, name, rotate, steps, warmup, pool=64, isolated=True):
+def time_decode(binding, synth, name, rotate, steps, warmup, pool=64, isolated=True, fold=False):
     import torch
-    cfg, layers = build_layers(binding, synth, name, rotate)
+    cfg, layers = build_layers(binding, synth, name, rotate, fold)
     T = cfg["T"]
     xs = [torch.from_numpy(synth.activations(cfg, T=T, index=j).view(np.int16)).cuda().view(torch.bfloat16)
           for j in range(pool)]
@@ -139,7 +140,7 @@ def time_decode(binding, synth, name, rotate, steps, warmup, pool=64, isolated=T
         raise RuntimeError("a device-side wait timed out during the benchmark")
     ids_np = ids.cpu().numpy()
     D = np.array([len(np.unique(ids_np[i])) for i in range(steps)])
-    nbytes = np.array([layer_bytes(cfg["H"], cfg["I"], cfg["E"], cfg["I_s"], d, T) for d in D])
+    nbytes = np.array([layer_bytes(cfg["H"], cfg["I"], cfg["E"], cfg["I_s"], d, T, folded=fold) for d in D])
     del layers
     torch.cuda.empty_cache()
     return {
@@ -327,6 +328,8 @@ def main():
     ap.add_argument("--no-16", action="store_true", help="skip the 16-row measurement")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 8192-row grouped measurement")
     ap.add_argument("--no-chain", action="store_true", help="skip the 8-layer graph-replayed chain")
+    ap.add_argument("--no-folded", action="store_true",
+                    help="skip the layers with the shared expert folded into the table as an MXFP4 expert")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-isolated", action="store_true",
                     help="skip the one-launch-at-a-time timing (profiler runs: only back-to-back launches)")
@@ -357,6 +360,15 @@ def main():
         print(f"[bench] 16 rows: {r16['us_launch']:.2f} us per launch back to back, {r16['gbs']:.0f} GB/s, "
               f"D={r16['distinct_experts_mean']:.1f}; isolated {r16['us_isolated_mean']:.2f} us",
               file=sys.stderr, flush=True)
+    rf = {}
+    if not args.no_folded:
+        for name, label in (("decode1", "1 row"), ("decode16", "16 rows")):
+            if name == "decode16" and args.no_16:
+                continue
+            rf[name] = time_decode(binding, synth, name, max(4, args.rotate // 2), args.steps, args.warmup,
+                                   isolated=False, fold=True)
+            print(f"[bench] {label}, shared expert folded (MXFP4 expert 128): {rf[name]['us_launch']:.2f} us per "
+                  f"launch, {rf[name]['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
     rc = None
     if not args.no_chain:
         rc = time_chain(binding, synth)
@@ -412,6 +424,15 @@ def main():
                          "us_isolated_mean": round(r16["us_isolated_mean"], 3),
                          "algorithmic_bytes_per_launch": int(r16["bytes_mean"]),
                          "ms_per_step": round(r16["wall_ms_per_step"], 5)}
+    if rf:
+        out["folded_shared"] = {
+            "workload": "the same layers with the MXFP8 shared expert re-quantized to MXFP4 and folded into the "
+                        "expert table as expert 128 (every row selects it with weight 1)",
+            **{("rows1" if n == "decode1" else "rows16"): {
+                "us_per_launch": round(r["us_launch"], 3), "gbs": round(r["gbs"], 1),
+                "frac": round(r["gbs"] / HBM_PEAK_GBS, 4), "distinct_routed_experts_mean":
+                round(r["distinct_experts_mean"], 2), "algorithmic_bytes_per_launch": int(r["bytes_mean"])}
+               for n, r in rf.items()}}
     if rc:
         out["chain8"] = {
             "workload": "8 distinct layers (hidden 3072, 128 experts top-4, I 1024, MXFP8 shared 1024), 4 rows, "

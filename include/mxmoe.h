@@ -94,6 +94,45 @@ moe_status mx_quantize_weights(const float* w, int rows, int cols, int fmt, int 
                                uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
 /*
+ * Re-quantization of an MXFP8 matrix to MXFP4 along the same 32-element
+ * blocks: each element's exact value (E4M3 value times its E8M0 scale) goes
+ * through the MX conversion again with the E2M1 element type.  This is how
+ * the MXFP8 shared expert becomes the MXFP4 expert folded into the table (vLLM
+ * PR #64273, section "Purpose": the shared-expert re-quantization is lossy).
+ * Run once at load time.
+ *   codes8, scales8  MXFP8 matrix [rows][cols] in `layout` (16- / 4-byte aligned)
+ *   codes4, scales4  MXFP4 output in the same layout: mx_codes_bytes(rows, cols,
+ *                    MX_FMT_FP4, layout) and mx_scales_bytes(rows, cols, layout)
+ * Values must be finite in fp32 (scale code and element value together below
+ * 2^128).  Shape requirements as for mx_quantize_weights.
+ */
+moe_status mx_requant_fp8_to_fp4(const uint8_t* codes8, const uint8_t* scales8, int rows, int cols, int layout,
+                                 uint8_t* codes4, uint8_t* scales4, hipStream_t stream);
+
+/*
+ * NVFP4 -> MXFP4 re-quantization: the load-time conversion of the NVFP4
+ * routed experts to the MXFP4 datapath (article "MiniMax-M3.1 on AMD Instinct
+ * GPUs: Day-0 support and optimization", TL;DR and section "Day 0 support for
+ * AMD Instinct GPUs"; vLLM PR #64273 squash commit, "Re-quantize the NVFP4
+ * routed experts to MXFP8 (or MXFP4) at load").  The pages name NVFP4 without
+ * defining it; the public definition is used: E2M1 elements in blocks of 16
+ * consecutive elements along a row, each block with an E4M3 scale, and an fp32
+ * second-level scale.  Values v = E2M1(c) * E4M3(s_block) * s_global, the
+ * last product rounded once to fp32; these go through the MX conversion with
+ * the E2M1 element type (32-element blocks, E8M0 scales).
+ *   codes          [rows][cols/2] packed E2M1 (element 2i in the low nibble), 16-byte aligned
+ *   block_scales   [rows][cols/16] E4M3
+ *   global_scales  fp32, device memory: row r uses global_scales[r / rows_per_scale]
+ *                  (rows_per_scale = rows for one per-tensor scale; I for a
+ *                  gate/up matrix whose two halves carry their own)
+ *   codes4, scales4 MXFP4 output in `layout` (sizes as mx_codes_bytes / mx_scales_bytes)
+ * Requires cols % 32 == 0 (row-major) or rows % 16 == 0 and cols % 128 == 0 (tiled).
+ */
+moe_status mx_requant_nvfp4_to_fp4(const uint8_t* codes, const uint8_t* block_scales, const float* global_scales,
+                                   int rows_per_scale, int rows, int cols, int layout, uint8_t* codes4,
+                                   uint8_t* scales4, hipStream_t stream);
+
+/*
  * Dynamic MXFP4 quantization of bf16 activations (model card "Model
  * Overview": "Routed-expert activation quantization: OCP MXFP4, Dynamic").
  *   x      [rows][cols] bf16, 16-byte aligned, cols % 32 == 0
@@ -112,6 +151,19 @@ moe_status mxfp4_quant_act(const uint16_t* x, int rows, int cols, uint8_t* codes
  * One MoE layer's weights (device pointers, caller-owned, tiled layout).
  * Routed expert e's matrices start at e * mx_codes_bytes(rows, cols, FP4, TILED)
  * bytes from w13 / w2 (scales likewise with mx_scales_bytes).
+ *
+ * shared_folded = 1: the shared expert is folded into the expert table (the
+ * AITER fused MoE "with the shared expert optionally folded into the expert
+ * table", article "MiniMax-M3.1 on AMD Instinct GPUs: Day-0 support and
+ * optimization", section "Serving with vLLM / What we Optimized"; MXFP4
+ * shared experts, model card section "Experimental MXFP4 shared experts").
+ * w13 / w2 then hold E + 1 experts; expert E (index num_experts) is the shared
+ * expert in MXFP4 (mx_requant_fp8_to_fp4 makes it from the MXFP8 one) and is
+ * selected for every token with weight 1, after the k routed choices:
+ *   y[t] = bf16( sum_{j<k} w[t,j] d[t,j] + d_shared[t] (+ residual[t]) ).
+ * The router still chooses among experts 0..E-1.  Requires shared_inter = 0
+ * (the ws* pointers are ignored), top_k <= 7 and num_experts <= 255.
+ * shared_folded = 0: an MXFP8 shared expert as given by shared_inter / ws*.
  */
 typedef struct {
   int32_t hidden;        /* H: multiple of 128 */
@@ -129,6 +181,7 @@ typedef struct {
   const uint8_t* ws13_scale;
   const uint8_t* ws2;         /* tiled FP8 [H][I_s], NULL if I_s == 0 */
   const uint8_t* ws2_scale;
+  int32_t shared_folded;      /* 0 or 1, see above */
 } moe_layer_t;
 
 /*

@@ -18,7 +18,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARGUMENT", -2: "MOE_ERR_UNSUPPORTED"
           -3: "MOE_ERR_WORKSPACE_TOO_SMALL", -4: "MOE_ERR_HIP", -5: "MOE_ERR_TIMEOUT"}
 
 EXPORTS = [
-    "mx_codes_bytes", "mx_scales_bytes", "mx_quantize_weights", "mxfp4_quant_act",
+    "mx_codes_bytes", "mx_scales_bytes", "mx_quantize_weights", "mx_requant_fp8_to_fp4", "mx_requant_nvfp4_to_fp4",
+    "mxfp4_quant_act",
     "moe_router_topk", "moe_align_sort_capacity", "moe_align_sort_workspace_bytes", "moe_align_sort",
     "moe_workspace_bytes", "moe_workspace_init", "fused_moe_mxfp4_decode", "fused_moe_mxfp4_decode_noalloc",
     "fused_moe_mxfp4_grouped", "fused_moe_mxfp4_grouped_timed",
@@ -42,6 +43,7 @@ class MoeLayerC(ctypes.Structure):
         ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
         ("ws13", ctypes.c_void_p), ("ws13_scale", ctypes.c_void_p),
         ("ws2", ctypes.c_void_p), ("ws2_scale", ctypes.c_void_p),
+        ("shared_folded", ctypes.c_int32),
     ]
 
 
@@ -62,6 +64,8 @@ def load():
         "mx_codes_bytes": (Z, [I, I, I, I]),
         "mx_scales_bytes": (Z, [I, I, I]),
         "mx_quantize_weights": (S, [P, I, I, I, I, P, P, P]),
+        "mx_requant_fp8_to_fp4": (S, [P, P, I, I, I, P, P, P]),
+        "mx_requant_nvfp4_to_fp4": (S, [P, P, P, I, I, I, I, P, P, P]),
         "mxfp4_quant_act": (S, [P, I, I, P, P, P]),
         "moe_router_topk": (S, [LP, P, I, P, P, P, P]),
         "moe_align_sort_capacity": (Z, [I, I, I, I]),
@@ -143,6 +147,46 @@ def mx_quantize_weights(w, fmt="fp4", layout="tiled", codes=None, scales=None):
     return codes, scales
 
 
+def mx_requant_fp8_to_fp4(codes8, scales8, rows, cols, layout="tiled", codes4=None, scales4=None):
+    """MXFP8 matrix (codes, scales uint8 CUDA tensors) re-quantized to MXFP4
+    along the same blocks.  Returns (codes4, scales4)."""
+    _need_cuda(codes8, scales8)
+    nc, ns = mx_codes_bytes(rows, cols, "fp4", layout), mx_scales_bytes(rows, cols, layout)
+    if nc == 0 or ns == 0:
+        raise ValueError(f"unsupported shape {(rows, cols)} for layout {layout}")
+    if codes4 is None:
+        codes4 = torch.empty(nc, dtype=torch.uint8, device=codes8.device)
+    if scales4 is None:
+        scales4 = torch.empty(ns, dtype=torch.uint8, device=codes8.device)
+    _check("mx_requant_fp8_to_fp4", load().mx_requant_fp8_to_fp4(
+        _ptr(codes8), _ptr(scales8), rows, cols, MX_LAYOUT[layout], _ptr(codes4), _ptr(scales4), _stream()))
+    if layout == "rowmajor":
+        codes4, scales4 = codes4.view(rows, cols // 2), scales4.view(rows, cols // 32)
+    return codes4, scales4
+
+
+def mx_requant_nvfp4_to_fp4(codes, block_scales, global_scales, rows_per_scale, layout="tiled",
+                            codes4=None, scales4=None):
+    """NVFP4 matrix (packed codes [rows, cols/2], E4M3 block scales [rows,
+    cols/16] uint8, fp32 global scales, CUDA tensors) re-quantized to MXFP4.
+    Returns (codes4, scales4)."""
+    _need_cuda(codes, block_scales, global_scales)
+    rows, cols = codes.shape[0], codes.shape[1] * 2
+    nc, ns = mx_codes_bytes(rows, cols, "fp4", layout), mx_scales_bytes(rows, cols, layout)
+    if nc == 0 or ns == 0:
+        raise ValueError(f"unsupported shape {(rows, cols)} for layout {layout}")
+    if codes4 is None:
+        codes4 = torch.empty(nc, dtype=torch.uint8, device=codes.device)
+    if scales4 is None:
+        scales4 = torch.empty(ns, dtype=torch.uint8, device=codes.device)
+    _check("mx_requant_nvfp4_to_fp4", load().mx_requant_nvfp4_to_fp4(
+        _ptr(codes), _ptr(block_scales), _ptr(global_scales), rows_per_scale, rows, cols, MX_LAYOUT[layout],
+        _ptr(codes4), _ptr(scales4), _stream()))
+    if layout == "rowmajor":
+        codes4, scales4 = codes4.view(rows, cols // 2), scales4.view(rows, cols // 32)
+    return codes4, scales4
+
+
 def mxfp4_quant_act(x):
     """Dynamic MXFP4 quantization of bf16 [rows, cols]: (codes [rows, cols/2],
     scales [rows, cols/32]) uint8."""
@@ -162,9 +206,11 @@ class MoELayer:
     """Device weights of one layer in the library's tiled MX layout."""
 
     def __init__(self, hidden, inter, num_experts, top_k, shared_inter, router_w, router_bias,
-                 w13, w13_scale, w2, w2_scale, ws13=None, ws13_scale=None, ws2=None, ws2_scale=None):
+                 w13, w13_scale, w2, w2_scale, ws13=None, ws13_scale=None, ws2=None, ws2_scale=None,
+                 shared_folded=False):
         self.hidden, self.inter, self.num_experts, self.top_k, self.shared_inter = (
             hidden, inter, num_experts, top_k, shared_inter)
+        self.shared_folded = bool(shared_folded)
         self.router_w, self.router_bias = router_w, router_bias
         self.w13, self.w13_scale, self.w2, self.w2_scale = w13, w13_scale, w2, w2_scale
         self.ws13, self.ws13_scale, self.ws2, self.ws2_scale = ws13, ws13_scale, ws2, ws2_scale
@@ -174,7 +220,7 @@ class MoELayer:
                             ws13.data_ptr() if ws13 is not None else None,
                             ws13_scale.data_ptr() if ws13_scale is not None else None,
                             ws2.data_ptr() if ws2 is not None else None,
-                            ws2_scale.data_ptr() if ws2_scale is not None else None)
+                            ws2_scale.data_ptr() if ws2_scale is not None else None, int(self.shared_folded))
 
     @property
     def c(self):
@@ -182,34 +228,54 @@ class MoELayer:
 
     @classmethod
     def from_fp32(cls, hidden, inter, num_experts, top_k, shared_inter, router_w, router_bias,
-                  expert_w13, expert_w2, shared_w13=None, shared_w2=None, device="cuda"):
+                  expert_w13, expert_w2, shared_w13=None, shared_w2=None, device="cuda", fold_shared=False):
         """Quantize fp32 weights on the device.  ``expert_w13(e)`` /
         ``expert_w2(e)`` return the fp32 [2I, H] / [H, I] matrices of expert e
         (host arrays or device tensors); ``router_w`` [E, H]; ``router_bias``
-        [E] or None; shared weights [2I_s, H] / [H, I_s] or None."""
+        [E] or None; shared weights [2I_s, H] / [H, I_s] or None.  With
+        ``fold_shared`` the shared expert is quantized to MXFP8, re-quantized
+        to MXFP4 and stored as expert E of an (E + 1)-expert table."""
         H, I, E, Is = hidden, inter, num_experts, shared_inter
         dev = torch.device(device)
+        if fold_shared and Is != I:
+            raise ValueError("folding needs the shared intermediate size to equal the routed one")
+        n_tab = E + 1 if fold_shared else E
 
         def dev_f32(a):
             return torch.as_tensor(a, dtype=torch.float32).to(dev).contiguous()
 
         c13, s13 = mx_codes_bytes(2 * I, H, "fp4"), mx_scales_bytes(2 * I, H)
         c2, s2 = mx_codes_bytes(H, I, "fp4"), mx_scales_bytes(H, I)
-        w13 = torch.empty(E * c13, dtype=torch.uint8, device=dev)
-        w13s = torch.empty(E * s13, dtype=torch.uint8, device=dev)
-        w2 = torch.empty(E * c2, dtype=torch.uint8, device=dev)
-        w2s = torch.empty(E * s2, dtype=torch.uint8, device=dev)
+        w13 = torch.empty(n_tab * c13, dtype=torch.uint8, device=dev)
+        w13s = torch.empty(n_tab * s13, dtype=torch.uint8, device=dev)
+        w2 = torch.empty(n_tab * c2, dtype=torch.uint8, device=dev)
+        w2s = torch.empty(n_tab * s2, dtype=torch.uint8, device=dev)
         for e in range(E):
             mx_quantize_weights(dev_f32(expert_w13(e)), "fp4", "tiled",
                                 w13[e * c13:(e + 1) * c13], w13s[e * s13:(e + 1) * s13])
             mx_quantize_weights(dev_f32(expert_w2(e)), "fp4", "tiled",
                                 w2[e * c2:(e + 1) * c2], w2s[e * s2:(e + 1) * s2])
         sh = {}
-        if Is > 0:
-            sh["ws13"], sh["ws13_scale"] = mx_quantize_weights(dev_f32(shared_w13), "fp8", "tiled")
-            sh["ws2"], sh["ws2_scale"] = mx_quantize_weights(dev_f32(shared_w2), "fp8", "tiled")
         rb = None if router_bias is None else dev_f32(router_bias)
+        if Is > 0:
+            q13, q13s = mx_quantize_weights(dev_f32(shared_w13), "fp8", "tiled")
+            q2, q2s = mx_quantize_weights(dev_f32(shared_w2), "fp8", "tiled")
+            if fold_shared:
+                mx_requant_fp8_to_fp4(q13, q13s, 2 * I, H, "tiled", w13[E * c13:], w13s[E * s13:])
+                mx_requant_fp8_to_fp4(q2, q2s, H, I, "tiled", w2[E * c2:], w2s[E * s2:])
+                return cls(H, I, E, top_k, 0, dev_f32(router_w), rb, w13, w13s, w2, w2s, shared_folded=True)
+            sh = dict(ws13=q13, ws13_scale=q13s, ws2=q2, ws2_scale=q2s)
         return cls(H, I, E, top_k, Is, dev_f32(router_w), rb, w13, w13s, w2, w2s, **sh)
+
+    def folded_from(self, fp4_13, fp4_13s, fp4_2, fp4_2s):
+        """A folded-shared copy of this layer sharing its routed weights:
+        the routed tables are copied into (E + 1)-expert tables and expert E
+        is set from the given MXFP4 tiled shared-expert matrices."""
+        E = self.num_experts
+        cat = lambda a, b: torch.cat([a, b.reshape(-1)]).contiguous()
+        return MoELayer(self.hidden, self.inter, E, self.top_k, 0, self.router_w, self.router_bias,
+                        cat(self.w13, fp4_13), cat(self.w13_scale, fp4_13s), cat(self.w2, fp4_2),
+                        cat(self.w2_scale, fp4_2s), shared_folded=True)
 
 
 # --------------------------------------------------------------------------- router / sort

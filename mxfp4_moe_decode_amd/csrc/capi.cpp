@@ -24,6 +24,8 @@ moe_status check_layer(const moe_layer_t* L) {
   if (!aligned(L->router_w, 16) || !aligned(L->router_bias, 4)) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(L->w13, 16) || !aligned(L->w2, 16) || !aligned(L->w13_scale, 4) || !aligned(L->w2_scale, 4))
     return MOE_ERR_INVALID_ARGUMENT;
+  if (L->shared_folded != 0 && L->shared_folded != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (L->shared_folded && (Is != 0 || k > 7 || E > 255)) return MOE_ERR_INVALID_ARGUMENT;
   if (Is > 0) {
     if (!L->ws13 || !L->ws13_scale || !L->ws2 || !L->ws2_scale) return MOE_ERR_INVALID_ARGUMENT;
     if (!aligned(L->ws13, 16) || !aligned(L->ws2, 16) || !aligned(L->ws13_scale, 4) ||
@@ -66,6 +68,26 @@ moe_status mx_quantize_weights(const float* w, int rows, int cols, int fmt, int 
   return from_hip(launch_quant_weights(w, rows, cols, fmt, layout, codes, scales, stream));
 }
 
+moe_status mx_requant_fp8_to_fp4(const uint8_t* codes8, const uint8_t* scales8, int rows, int cols, int layout,
+                                 uint8_t* codes4, uint8_t* scales4, hipStream_t stream) {
+  if (!codes8 || !scales8 || !codes4 || !scales4) return MOE_ERR_INVALID_ARGUMENT;
+  if (!valid_layout(layout) || !valid_shape(rows, cols, layout)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(codes8, 16) || !aligned(codes4, 16) || !aligned(scales4, 4)) return MOE_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_requant_fp8_fp4(codes8, scales8, rows, cols, layout, codes4, scales4, stream));
+}
+
+moe_status mx_requant_nvfp4_to_fp4(const uint8_t* codes, const uint8_t* block_scales, const float* global_scales,
+                                   int rows_per_scale, int rows, int cols, int layout, uint8_t* codes4,
+                                   uint8_t* scales4, hipStream_t stream) {
+  if (!codes || !block_scales || !global_scales || !codes4 || !scales4) return MOE_ERR_INVALID_ARGUMENT;
+  if (!valid_layout(layout) || !valid_shape(rows, cols, layout)) return MOE_ERR_INVALID_ARGUMENT;
+  if (rows_per_scale <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(codes, 16) || !aligned(global_scales, 4) || !aligned(codes4, 16) || !aligned(scales4, 4))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_requant_nvfp4(codes, block_scales, global_scales, rows_per_scale, rows, cols, layout, codes4,
+                                       scales4, stream));
+}
+
 moe_status mxfp4_quant_act(const uint16_t* x, int rows, int cols, uint8_t* codes, uint8_t* scales,
                            hipStream_t stream) {
   if (!x || !codes || !scales) return MOE_ERR_INVALID_ARGUMENT;
@@ -80,7 +102,7 @@ moe_status moe_router_topk(const moe_layer_t* layer, const uint16_t* x, int T, f
   if (st != MOE_OK) return st;
   if (T <= 0 || !x || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16)) return MOE_ERR_INVALID_ARGUMENT;
-  return from_hip(launch_router_topk(*layer, x, T, logits, topk_ids, topk_w, stream));
+  return from_hip(launch_router_topk(*layer, x, T, logits, topk_ids, topk_w, layer->top_k, -1, stream));
 }
 
 size_t moe_align_sort_capacity(int T, int k, int E, int block_m) {

@@ -81,6 +81,7 @@ enum {
 
 struct DecodeArgs {
   int T, H, I, E, k, Is, G;
+  int fold;           // the shared expert is expert E of the table (1) or MXFP8 (0)
   int KT1, CT1, NC1;  // K = H: tiles of 128, tiles per chunk, chunks
   int KT2, CT2;       // K = I
   int KTs, CTs;       // K = I_s
@@ -104,15 +105,20 @@ struct DecodeArgs {
 
 // The shape as the kernel sees it: compile-time constants where the launch
 // picked a specialization for the layer's shape (H_, I_, IS_, E_, K_ non-zero,
-// IS_ = -1 for no shared expert), the run-time fields otherwise.
+// IS_ = -1 for no MXFP8 shared expert; FOLD_ 0 or 1, -1 for run time), the
+// run-time fields otherwise.  kr() is the router's k; kk() the slots per row:
+// the k routed choices and, with the shared expert folded into the table, one
+// more slot (expert E, weight 1).
 constexpr int n_chunks_of(int tiles) { return tiles % 4 == 0 ? 4 : (tiles % 2 == 0 ? 2 : 1); }
-template <int H_, int I_, int IS_, int E_, int K_>
+template <int H_, int I_, int IS_, int E_, int K_, int FOLD_>
 struct DArgs : DecodeArgs {
   __device__ __forceinline__ int h() const { return H_ ? H_ : H; }
   __device__ __forceinline__ int i() const { return I_ ? I_ : I; }
   __device__ __forceinline__ int is() const { return IS_ ? (IS_ < 0 ? 0 : IS_) : Is; }
   __device__ __forceinline__ int e() const { return E_ ? E_ : E; }
-  __device__ __forceinline__ int kk() const { return K_ ? K_ : k; }
+  __device__ __forceinline__ int kr() const { return K_ ? K_ : k; }
+  __device__ __forceinline__ int fd() const { return FOLD_ >= 0 ? FOLD_ : fold; }
+  __device__ __forceinline__ int kk() const { return kr() + fd(); }
   __device__ __forceinline__ int kt1() const { return h() / 128; }
   __device__ __forceinline__ int nc1() const { return n_chunks_of(kt1()); }
   __device__ __forceinline__ int ct1() const { return kt1() / nc1(); }
@@ -934,22 +940,31 @@ __device__ __forceinline__ void decode_body(const DA& A, uint32_t tag, Smem& sm,
     } while (keep_polling(ok, t0, A.sync));
   }
   trace_at(A, TR_LOGITS);
+  // the k routed choices of row t go to slots t*kk .. t*kk + k - 1
   if (T <= kWaves) {  // a wavefront per row
     const int row = wave < T ? wave : 0;
-    row_topk64(logits_lds + row * E, wave < T, E, A.kk(), lane, sm.ids + row * A.kk(), sm.w + row * A.kk());
+    row_topk64(logits_lds + row * E, wave < T, E, A.kr(), lane, sm.ids + row * A.kk(), sm.w + row * A.kk());
   } else {  // 16 lanes per row, 16 rows
     const int row = threadIdx.x / 16;
-    rows_topk16(logits_lds + (row < T ? row : 0) * E, row < T, E, A.kk(), threadIdx.x & 15,
+    rows_topk16(logits_lds + (row < T ? row : 0) * E, row < T, E, A.kr(), threadIdx.x & 15,
                 sm.ids + (row < T ? row : 0) * A.kk(), sm.w + (row < T ? row : 0) * A.kk());
+  }
+  if (A.fd() && threadIdx.x >= kThreads - kDecodeMaxT) {  // the folded shared expert: last slot of each row
+    const int t = threadIdx.x - (kThreads - kDecodeMaxT);
+    if (t < T) {
+      sm.ids[t * A.kk() + A.kr()] = E;
+      sm.w[t * A.kk() + A.kr()] = 1.0f;
+    }
   }
   __syncthreads();
   trace_at(A, TR_TOPK);
   build_expert_list(A, sm, lane, wave);
   trace_at(A, TR_ELIST);
-  if (blockIdx.x == 0) {
-    for (int i = threadIdx.x; i < T * A.kk(); i += kThreads) {
-      if (A.ids_out) A.ids_out[i] = sm.ids[i];
-      if (A.w_out) A.w_out[i] = sm.w[i];
+  if (blockIdx.x == 0) {  // the routing outputs: the k routed choices per row
+    for (int i = threadIdx.x; i < T * A.kr(); i += kThreads) {
+      const int sl = (i / A.kr()) * A.kk() + i % A.kr();
+      if (A.ids_out) A.ids_out[i] = sm.ids[sl];
+      if (A.w_out) A.w_out[i] = sm.w[sl];
     }
   }
   __syncthreads();
@@ -1089,7 +1104,7 @@ struct Carve {
 };
 
 Carve carve(const moe_layer_t& L) {
-  const size_t T = kDecodeMaxT, H = L.hidden, I = L.inter, E = L.num_experts, k = L.top_k,
+  const size_t T = kDecodeMaxT, H = L.hidden, I = L.inter, E = L.num_experts, k = layer_slots(L),
                Is = L.shared_inter;
   Carve c{};
   size_t o = 0;
@@ -1157,8 +1172,9 @@ hipError_t launch_instance(const DecodeArgs& args, size_t lds, hipStream_t strea
 
 // The MiniMax-M3.1 layer shape (hidden 3072, 128 experts top-4, intermediate
 // 1024, shared intermediate 1024) has its own compiled instance.
-using MiniMaxShape = DArgs<3072, 1024, 1024, 128, 4>;
-using AnyShape = DArgs<0, 0, 0, 0, 0>;
+using MiniMaxShape = DArgs<3072, 1024, 1024, 128, 4, 0>;
+using MiniMaxFolded = DArgs<3072, 1024, -1, 128, 4, 1>;  // shared expert folded in as expert 128
+using AnyShape = DArgs<0, 0, 0, 0, 0, -1>;
 
 int n_chunks(int tiles) { return tiles % 4 == 0 ? 4 : (tiles % 2 == 0 ? 2 : 1); }
 
@@ -1185,6 +1201,7 @@ hipError_t launch_decode(const moe_layer_t& L, const uint16_t* x, int T, const u
   A.I = L.inter;
   A.E = L.num_experts;
   A.k = L.top_k;
+  A.fold = L.shared_folded ? 1 : 0;
   A.Is = L.shared_inter;
   A.KT1 = A.H / 128;
   A.NC1 = n_chunks(A.KT1);
@@ -1219,8 +1236,10 @@ hipError_t launch_decode(const moe_layer_t& L, const uint16_t* x, int T, const u
   A.trace = reinterpret_cast<uint64_t*>(base + c.trace);
   A.tagged = A.logits;
   A.n_tagged = (uint32_t)((c.trace - c.logits) / 8);
-  if (A.H == 3072 && A.I == 1024 && A.Is == 1024 && A.E == 128 && A.k == 4)
-    return launch_instance<MiniMaxShape>(A, lds, stream);
+  if (A.H == 3072 && A.I == 1024 && A.E == 128 && A.k == 4) {
+    if (A.Is == 1024 && !A.fold) return launch_instance<MiniMaxShape>(A, lds, stream);
+    if (A.Is == 0 && A.fold) return launch_instance<MiniMaxFolded>(A, lds, stream);
+  }
   return launch_instance<AnyShape>(A, lds, stream);
 }
 

@@ -478,7 +478,9 @@ struct GCarve {
 };
 
 GCarve gcarve(const moe_layer_t& L, int T) {
-  const size_t H = L.hidden, I = L.inter, E = L.num_experts, k = L.top_k, Is = L.shared_inter;
+  // slots per row and experts in the table (with the folded shared expert: one more of each)
+  const size_t H = L.hidden, I = L.inter, E = L.num_experts + (L.shared_folded ? 1 : 0), k = layer_slots(L),
+               Is = L.shared_inter;
   const size_t S = (size_t)T * k;
   GCarve c{};
   c.cap = S + (S < E ? S : E) * (kBM - 1);
@@ -542,7 +544,10 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
   const GCarve c = gcarve(L, T);
   char* base = reinterpret_cast<char*>(ws);
   auto at = [&](size_t off) { return base + off; };
-  const int H = L.hidden, I = L.inter, E = L.num_experts, k = L.top_k, Is = L.shared_inter;
+  // k: slots per row, E: experts in the table; with the shared expert folded
+  // in, slot k_routed of every row holds expert num_experts with weight 1
+  const int H = L.hidden, I = L.inter, Is = L.shared_inter, k = layer_slots(L);
+  const int E = L.num_experts + (L.shared_folded ? 1 : 0);
   int32_t* ids = reinterpret_cast<int32_t*>(at(c.ids));
   float* w = reinterpret_cast<float*>(at(c.w));
   int32_t* sorted = reinterpret_cast<int32_t*>(at(c.sorted));
@@ -556,7 +561,8 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
   hipError_t err;
   if ((err = mark(0)) != hipSuccess) return err;
   if ((err = launch_router_topk(L, x, T, router_tiled(T) ? reinterpret_cast<float*>(at(c.logits)) : nullptr, ids, w,
-                               stream)) != hipSuccess) return err;
+                               k, L.shared_folded ? L.num_experts : -1, stream)) != hipSuccess)
+    return err;
   if ((err = mark(1)) != hipSuccess) return err;
   if ((err = launch_align_sort(ids, T, k, E, kBM, sorted, bexp, reinterpret_cast<int32_t*>(at(c.eoff)), npad,
                                at(c.sort_ws), stream)) != hipSuccess)

@@ -42,14 +42,29 @@ hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int fmt, uint
 hipError_t launch_quant_act_dual(const uint16_t* x, int rows, int cols, uint8_t* codes4, uint8_t* scales4,
                                  uint8_t* codes8, uint8_t* scales8, hipStream_t stream);
 hipError_t launch_fill_u32(void* p, size_t words, uint32_t value, hipStream_t stream);
+// MXFP8 -> MXFP4 along the same blocks, either layout.
+hipError_t launch_requant_fp8_fp4(const uint8_t* codes8, const uint8_t* scales8, int rows, int cols, int layout,
+                                  uint8_t* codes4, uint8_t* scales4, hipStream_t stream);
+
+// NVFP4 (row-major codes, E4M3 block scales per 16, fp32 scale per row group)
+// -> MXFP4 in either layout.
+hipError_t launch_requant_nvfp4(const uint8_t* codes, const uint8_t* block_scales, const float* global_scales,
+                                int rows_per_scale, int rows, int cols, int layout, uint8_t* codes4,
+                                uint8_t* scales4, hipStream_t stream);
+
+// Slots per row of a layer call: the k routed choices, plus the folded shared
+// expert when there is one.
+inline int layer_slots(const moe_layer_t& L) { return L.top_k + (L.shared_folded ? 1 : 0); }
 
 // ------------------------------------------------------------------ router
 // From this many rows on, a call that keeps the logits takes the tiled logits
 // kernel and a separate top-k pass (same arithmetic, identical results).
 constexpr int kRouterTiledMinT = 64;
 bool router_tiled(int T);
+// ids / w rows are `ld` apart (>= k); with fold_e >= 0 entry k of every row
+// is set to (fold_e, 1.0): the folded shared expert's slot.
 hipError_t launch_router_topk(const moe_layer_t& L, const uint16_t* x, int T, float* logits,
-                              int32_t* ids, float* w, hipStream_t stream);
+                              int32_t* ids, float* w, int ld, int fold_e, hipStream_t stream);
 
 // ------------------------------------------------------------------ align / sort
 constexpr int kSortChunk = 1024;

@@ -53,6 +53,113 @@ __device__ __forceinline__ void store_block(uint8_t* codes, uint8_t* scales, int
   }
 }
 
+// Codes and scale of MXFP8 block (r, b) of a [rows][cols] matrix in either
+// layout (the inverse of store_block<FP8, Tiled>).
+template <bool Tiled>
+__device__ __forceinline__ uint32_t load_block_fp8(const uint8_t* codes, const uint8_t* scales, int r, int b,
+                                                   int cols, uint32_t (&words)[8]) {
+  const int KT = cols / 128;
+  if constexpr (!Tiled) {
+    const uint4* src = reinterpret_cast<const uint4*>(codes + (size_t)r * cols + 32 * b);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4 v = src[h];
+      words[4 * h] = v.x;
+      words[4 * h + 1] = v.y;
+      words[4 * h + 2] = v.z;
+      words[4 * h + 3] = v.w;
+    }
+    return scales[(size_t)r * (cols / 32) + b];
+  } else {
+    const int nt = r / 16, kt = b / 4, q = b % 4;
+    const uint8_t* tile = codes + ((size_t)nt * KT + kt) * 2048;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k0 = 32 * q + 16 * h;
+      const int c = k0 / 64, qq = (k0 % 64) / 16;
+      const uint4 v = *reinterpret_cast<const uint4*>(tile + 1024 * c + 16 * ((r % 16) + 16 * qq));
+      words[4 * h] = v.x;
+      words[4 * h + 1] = v.y;
+      words[4 * h + 2] = v.z;
+      words[4 * h + 3] = v.w;
+    }
+    const int KG = (KT + 3) / 4;
+    return scales[(((size_t)nt * KG + kt / 4) * 64 + (r % 16) + 16 * q) * 4 + kt % 4];
+  }
+}
+
+// Exact fp32 value of E4M3 code c times 2^(s - 127): the code is M * 2^(E - 10)
+// with M = 8 + m, E = e for a normal (e >= 1) and M = m, E = 1 for a subnormal;
+// M has at most four significant bits, so the product is exact whenever it is
+// finite in fp32 (down to 2^-136, inside fp32's subnormal range).
+__device__ __forceinline__ uint32_t e4m3_scaled_bits(uint32_t c, uint32_t s) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float M = (float)(e ? 8u + m : m);
+  const float v = ldexpf(M, (int)(e ? e : 1u) - 10 + (int)s - 127);
+  return __float_as_uint(v) | ((c & 0x80u) << 24);
+}
+
+// MXFP8 -> MXFP4 re-quantization along the same 32-element blocks: every
+// element's exact value goes through the MX conversion again with the E2M1
+// element type.  One thread per block.
+template <bool Tiled>
+__global__ void __launch_bounds__(kThreads) requant_fp8_fp4_kernel(const uint8_t* __restrict__ codes8,
+                                                                   const uint8_t* __restrict__ scales8, int rows,
+                                                                   int cols, uint8_t* __restrict__ codes4,
+                                                                   uint8_t* __restrict__ scales4) {
+  const int nb = cols / 32;
+  const size_t blk = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (blk >= (size_t)rows * nb) return;
+  const int r = (int)(blk / nb), b = (int)(blk % nb);
+  uint32_t w8[8];
+  const uint32_t s = load_block_fp8<Tiled>(codes8, scales8, r, b, cols, w8);
+  uint32_t bits[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) bits[i] = e4m3_scaled_bits((w8[i / 4] >> (8 * (i % 4))) & 0xffu, s);
+  uint32_t words[8];
+  const uint32_t s4 = quant_block32<FP4>(bits, words);
+  store_block<FP4, Tiled>(codes4, scales4, r, b, cols, words, s4);
+}
+
+// NVFP4 -> MXFP4 re-quantization.  NVFP4 (the public format: E2M1 elements,
+// an E4M3 scale per 16 consecutive elements, an fp32 scale per tensor or row
+// group): v = E2M1(c) * E4M3(s_block) * s_global, where the first product is
+// exact in fp32 and the second is rounded once (round to nearest even).  The
+// fp32 values then go through the MX conversion with the E2M1 element type,
+// 32 elements per block.  One thread per 32-element block: the row-major codes
+// [rows][cols/2] (element 2i in the low nibble of byte i), block scales
+// [rows][cols/16], scale group r / rows_per_scale.
+template <bool Tiled>
+__global__ void __launch_bounds__(kThreads) requant_nvfp4_kernel(const uint8_t* __restrict__ codes,
+                                                                 const uint8_t* __restrict__ block_scales,
+                                                                 const float* __restrict__ global_scales,
+                                                                 int rows_per_scale, int rows, int cols,
+                                                                 uint8_t* __restrict__ codes4,
+                                                                 uint8_t* __restrict__ scales4) {
+  const int nb = cols / 32;
+  const size_t blk = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (blk >= (size_t)rows * nb) return;
+  const int r = (int)(blk / nb), b = (int)(blk % nb);
+  const uint4 v = *reinterpret_cast<const uint4*>(codes + (size_t)r * (cols / 2) + 16 * b);
+  const uint32_t packed[4] = {v.x, v.y, v.z, v.w};
+  const uint8_t* bs = block_scales + (size_t)r * (cols / 16) + 2 * b;
+  const float s[2] = {__uint_as_float(e4m3_scaled_bits(bs[0], 127u)), __uint_as_float(e4m3_scaled_bits(bs[1], 127u))};
+  const float g = global_scales[r / rows_per_scale];
+  uint32_t bits[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    // E2M1 magnitude code m = 2e + f: M * 2^(max(e, 1) - 2) with M = 2 + f for
+    // e >= 1 and M = f for e = 0 (0, 0.5, 1, 1.5, 2, 3, 4, 6)
+    const uint32_t c = (packed[i / 8] >> (4 * (i % 8))) & 0xfu;
+    const uint32_t e = (c >> 1) & 3u, f = c & 1u;
+    const float a = ldexpf((float)(e ? 2u + f : f) * s[i / 16], (int)(e ? e : 1u) - 2);  // exact
+    bits[i] = __float_as_uint(a * g) ^ ((c & 8u) << 28);
+  }
+  uint32_t words[8];
+  const uint32_t s4 = quant_block32<FP4>(bits, words);
+  store_block<FP4, Tiled>(codes4, scales4, r, b, cols, words, s4);
+}
+
 template <class F, bool Tiled>
 __global__ void __launch_bounds__(kThreads) quant_weights_kernel(const float* __restrict__ w,
                                                                  int rows, int cols,
@@ -147,6 +254,39 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
 }
 
 }  // namespace
+
+hipError_t launch_requant_fp8_fp4(const uint8_t* codes8, const uint8_t* scales8, int rows, int cols, int layout,
+                                  uint8_t* codes4, uint8_t* scales4, hipStream_t stream) {
+  const size_t nblk = (size_t)rows * (cols / 32);
+  const unsigned grid = (unsigned)((nblk + kThreads - 1) / kThreads);
+  if (layout == MX_LAYOUT_TILED) {
+    hipError_t err = launch_fill_u32(scales4, tiled_scales_bytes(rows, cols) / 4, 0x7f7f7f7fu, stream);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(requant_fp8_fp4_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, codes8, scales8, rows,
+                       cols, codes4, scales4);
+  } else {
+    hipLaunchKernelGGL(requant_fp8_fp4_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, codes8, scales8, rows,
+                       cols, codes4, scales4);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_requant_nvfp4(const uint8_t* codes, const uint8_t* block_scales, const float* global_scales,
+                                int rows_per_scale, int rows, int cols, int layout, uint8_t* codes4,
+                                uint8_t* scales4, hipStream_t stream) {
+  const size_t nblk = (size_t)rows * (cols / 32);
+  const unsigned grid = (unsigned)((nblk + kThreads - 1) / kThreads);
+  if (layout == MX_LAYOUT_TILED) {
+    hipError_t err = launch_fill_u32(scales4, tiled_scales_bytes(rows, cols) / 4, 0x7f7f7f7fu, stream);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(requant_nvfp4_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, codes, block_scales,
+                       global_scales, rows_per_scale, rows, cols, codes4, scales4);
+  } else {
+    hipLaunchKernelGGL(requant_nvfp4_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, codes, block_scales,
+                       global_scales, rows_per_scale, rows, cols, codes4, scales4);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_u32(void* p, size_t words, uint32_t value, hipStream_t stream) {
   if (words == 0) return hipSuccess;

@@ -17,7 +17,7 @@ constexpr int kRouterRows = 8;  // rows a workgroup keeps in LDS
 __global__ void __launch_bounds__(kThreads) router_topk_kernel(
     const uint16_t* __restrict__ x, int T, int H, int E, int k, int rows_per_wg,
     const float* __restrict__ wr, const float* __restrict__ bias, float* __restrict__ logits_out,
-    int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, int ld, int fold_e) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                               // [rows][H]
   float* ls = reinterpret_cast<float*>(smem + align_up((size_t)rows_per_wg * H * 2, 16));  // [rows][E]
@@ -82,8 +82,12 @@ __global__ void __launch_bounds__(kThreads) router_topk_kernel(
     const int r = r0 + (int)threadIdx.x / 16;
     const bool act = r < nrows;
     const int rr = act ? r : 0;
-    rows_topk16(ls + rr * E, act, E, k, threadIdx.x & 15, ids_out + (size_t)(t0 + rr) * k,
-                w_out + (size_t)(t0 + rr) * k);
+    rows_topk16(ls + rr * E, act, E, k, threadIdx.x & 15, ids_out + (size_t)(t0 + rr) * ld,
+                w_out + (size_t)(t0 + rr) * ld);
+    if (act && fold_e >= 0 && (threadIdx.x & 15) == 0) {
+      ids_out[(size_t)(t0 + rr) * ld + k] = fold_e;
+      w_out[(size_t)(t0 + rr) * ld + k] = 1.0f;
+    }
   }
 }
 
@@ -179,12 +183,16 @@ __global__ void __launch_bounds__(kThreads, 2) router_logits_tiled_kernel(
 // Top k of each row of a logits matrix: 16 lanes per row.
 __global__ void __launch_bounds__(kThreads) topk_rows_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                              int32_t* __restrict__ ids_out,
-                                                             float* __restrict__ w_out) {
+                                                             float* __restrict__ w_out, int ld, int fold_e) {
   const int r = blockIdx.x * (kThreads / 16) + (int)threadIdx.x / 16;
   const bool act = r < T;
   const int rr = act ? r : T - 1;
-  rows_topk16(logits + (size_t)rr * E, act, E, k, threadIdx.x & 15, ids_out + (size_t)rr * k,
-              w_out + (size_t)rr * k);
+  rows_topk16(logits + (size_t)rr * E, act, E, k, threadIdx.x & 15, ids_out + (size_t)rr * ld,
+              w_out + (size_t)rr * ld);
+  if (act && fold_e >= 0 && (threadIdx.x & 15) == 0) {
+    ids_out[(size_t)rr * ld + k] = fold_e;
+    w_out[(size_t)rr * ld + k] = 1.0f;
+  }
 }
 
 }  // namespace
@@ -192,7 +200,7 @@ __global__ void __launch_bounds__(kThreads) topk_rows_kernel(const float* __rest
 bool router_tiled(int T) { return T >= kRouterTiledMinT; }
 
 hipError_t launch_router_topk(const moe_layer_t& L, const uint16_t* x, int T, float* logits,
-                              int32_t* ids, float* w, hipStream_t stream) {
+                              int32_t* ids, float* w, int ld, int fold_e, hipStream_t stream) {
   const int H = L.hidden, E = L.num_experts;
   if (logits && router_tiled(T)) {
     const int n_rblk = (T + kTileRows - 1) / kTileRows;
@@ -203,7 +211,7 @@ hipError_t launch_router_topk(const moe_layer_t& L, const uint16_t* x, int T, fl
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)((T + 15) / 16)), dim3(kThreads), 0, stream, logits, T, E,
-                       L.top_k, ids, w);
+                       L.top_k, ids, w, ld, fold_e);
     return hipGetLastError();
   }
   int rows = 65536 / H;
@@ -211,7 +219,7 @@ hipError_t launch_router_topk(const moe_layer_t& L, const uint16_t* x, int T, fl
   const size_t lds = align_up((size_t)rows * H * 2, 16) + (size_t)rows * E * 4;
   const unsigned grid = (unsigned)((T + rows - 1) / rows);
   hipLaunchKernelGGL(router_topk_kernel, dim3(grid), dim3(kThreads), lds, stream, x, T, H, E,
-                     L.top_k, rows, L.router_w, L.router_bias, logits, ids, w);
+                     L.top_k, rows, L.router_w, L.router_bias, logits, ids, w, ld, fold_e);
   return hipGetLastError();
 }
 

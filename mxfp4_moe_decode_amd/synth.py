@@ -57,7 +57,7 @@ WORKLOADS = {
                 zipf=None, residual=False),
 }
 _WID = {name: i + 1 for i, name in enumerate(WORKLOADS)}
-_TAG = {"router": 1, "w13": 2, "w2": 3, "ws13": 4, "ws2": 5, "bias": 6, "x": 7}
+_TAG = {"router": 1, "w13": 2, "w2": 3, "ws13": 4, "ws2": 5, "bias": 6, "x": 7, "nvfp4": 8}
 WEIGHT_STD = 0.02
 
 
@@ -165,3 +165,16 @@ def device_shared_w13(cfg, layer=0, device="cuda"):
 
 def device_shared_w2(cfg, layer=0, device="cuda"):
     return _device_normal(cfg, layer, "ws2", 0, (cfg["H"], cfg["I_s"]), device)
+
+
+def nvfp4_matrix(cfg, layer, index, rows, cols, n_global=1):
+    """A synthetic NVFP4 matrix (the checkpoint format of the routed experts):
+    E2M1 codes uniform over all 16 codes, unpacked [rows, cols]; E4M3 block
+    scale codes [rows, cols/16] uniform over 0x40..0x7E (values 2 .. 448);
+    ``n_global`` fp32 second-level scales log-uniform around 2e-5, so that the
+    values have the spread of N(0, 0.02) weights (block maxima ~1e-2 .. 6e-2)."""
+    g = _rng(cfg, layer, "nvfp4", index)
+    codes = g.integers(0, 16, size=(rows, cols)).astype(np.uint8)
+    bscales = g.integers(0x40, 0x7F, size=(rows, cols // 16)).astype(np.uint8)
+    gscale = (2e-5 * np.exp(g.uniform(-0.5, 0.5, size=n_global))).astype(np.float32)
+    return codes, bscales, gscale

@@ -168,6 +168,36 @@ def requant_fp8_to_fp4(codes8, scales8):
     return mx_quantize(mx_dequantize(codes8, scales8, "fp8"), "fp4")
 
 
+def nvfp4_dequantize(codes, block_scales, global_scales, rows_per_scale):
+    """Values of an NVFP4 matrix, the format of the checkpoint's routed experts
+    (article "MiniMax-M3.1 on AMD Instinct GPUs: Day-0 support and
+    optimization", section "MiniMax-M3.1 at a glance").  The pages name the
+    format without defining it; the definition used is the public NVFP4 one:
+    E2M1 elements (unpacked ``codes`` [rows, cols]) in blocks of 16
+    consecutive elements along a row, each block with an unsigned E4M3 scale
+    (``block_scales`` [rows, cols/16] codes), and a second-level fp32 scale per
+    group of ``rows_per_scale`` rows (``global_scales``):
+        v = E2M1(c) * E4M3(s_block) * s_global.
+    E2M1 times E4M3 is exact (at most 6 significant bits); the product with
+    the fp32 global scale is rounded once to fp32, the precision a loader
+    holds weights in.  Returns fp64 values (each an fp32 number)."""
+    codes = np.asarray(codes)
+    rows, cols = codes.shape
+    bs = np.repeat(e4m3_value(block_scales), 16, axis=-1)
+    g = np.repeat(np.asarray(global_scales, np.float64), rows_per_scale)[:rows, None]
+    return to_f32(e2m1_value(codes) * bs * g)
+
+
+def requant_nvfp4_to_mxfp4(codes, block_scales, global_scales, rows_per_scale):
+    """NVFP4 -> MXFP4: the MX conversion (E2M1 elements, 32-element blocks,
+    E8M0 scales) of the NVFP4 matrix's fp32 values (the load-time conversion of
+    the NVFP4 routed experts to the MXFP4 datapath: article above, TL;DR and
+    section "Day 0 support for AMD Instinct GPUs"; vLLM PR #64273, squash
+    commit notes "Re-quantize the NVFP4 routed experts to MXFP8 (or MXFP4) at
+    load").  Returns (codes, scales) of the MXFP4 matrix."""
+    return mx_quantize(nvfp4_dequantize(codes, block_scales, global_scales, rows_per_scale), "fp4")
+
+
 def pack_fp4(codes):
     """Two E2M1 codes per byte along the last axis: element 2i in the low
     nibble of byte i, element 2i+1 in the high nibble."""

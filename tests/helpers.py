@@ -52,8 +52,10 @@ class LazyExperts:
 def prefetch(ol, experts, threads=16):
     """Quantize the given experts of an oracle layer ahead of use, several at
     a time (numpy releases the GIL in the heavy array work)."""
-    todo = sorted({int(e) for e in experts})
-    w13, w2 = ol.w13_codes.lazy, ol.w2_codes.lazy
+    todo = sorted({int(e) for e in experts if int(e) < ol.E})  # a folded expert E is held already
+    base13 = getattr(ol.w13_codes, "base", ol.w13_codes)
+    base2 = getattr(ol.w2_codes, "base", ol.w2_codes)
+    w13, w2 = base13.lazy, base2.lazy
     host13 = {e: w13.make(e) for e in todo if e not in w13.cache}
     host2 = {e: w2.make(e) for e in todo if e not in w2.cache}
 

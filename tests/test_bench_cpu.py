@@ -34,3 +34,11 @@ def test_prefill_flops():
     assert shared == 2 * 8192 * (2 * 1024 * 3072 + 3072 * 1024)
     assert router == 2 * 8192 * 128 * 3072
     assert round(routed / 1e9, 1) == 618.5 and round(shared / 1e9, 1) == 154.6 and round(router / 1e9, 2) == 6.44
+
+
+def test_folded_layer_bytes():
+    """Folded: the MXFP8 shared expert's 9,732,096 B become one more MXFP4
+    expert of 5,013,504 B."""
+    H, I, E, Is = 3072, 1024, 128, 1024
+    assert bench.layer_bytes(H, I, E, Is, 4, 1, folded=True) == 31_371_264 - 9_732_096 + 5_013_504
+    assert bench.layer_bytes(H, I, E, Is, 4, 1, folded=True) == E * H * 4 + 5 * _expert_bytes(H, I) + 2 * H * 2

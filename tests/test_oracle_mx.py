@@ -292,3 +292,76 @@ def test_requant_fp8_to_fp4_lossless_on_the_fp4_grid():
     c8, s8 = mx.mx_quantize(w, "fp8")
     c4, s4 = mx.requant_fp8_to_fp4(c8, s8)
     assert np.array_equal(mx.mx_dequantize(c4, s4, "fp4"), w)
+
+
+def _e4m3_code(v):
+    """E4M3 code of an exactly representable positive value (test helper)."""
+    vals = mx.e4m3_value(np.arange(0x7F))
+    return int(np.flatnonzero(vals == v)[0])
+
+
+def test_nvfp4_requant_hand_worked():
+    # Block scale 1.5 (E4M3), global 0.5: E2M1 6 -> 6 * 1.5 * 0.5 = 4.5 and
+    # E2M1 -1 -> -0.75.  MXFP4 of the 32-block: max 4.5 -> exponent
+    # floor(log2 4.5) - 2 = 0; 4.5 -> nearest of 4 / 6 is 4 (code 6): lossy;
+    # -0.75 halfway between 0.5 (code 1) and 1 (code 2) -> even code 2 -> -1.
+    c = np.zeros((1, 32), np.uint8)
+    c[0, 0], c[0, 17] = 7, 0xA  # +6 in the first 16-block, -1 in the second
+    bs = np.array([[_e4m3_code(1.5), _e4m3_code(1.5)]], np.uint8)
+    v = mx.nvfp4_dequantize(c, bs, [0.5], 1)
+    assert v[0, 0] == 4.5 and v[0, 17] == -0.75
+    c4, s4 = mx.requant_nvfp4_to_mxfp4(c, bs, [0.5], 1)
+    assert s4.tolist() == [[127]]
+    assert c4[0, 0] == 6 and c4[0, 17] == 0xA and not np.delete(c4[0], [0, 17]).any()
+
+
+def test_nvfp4_requant_is_lossless_for_power_of_two_scales():
+    # Block scales that are powers of two, equal over each pair of 16-blocks,
+    # and a power-of-two global scale: every 32-block is E2M1 codes times a
+    # common power of two, so MXFP4 holds it exactly (with a top-binade element
+    # the MX exponent is that power and the codes are unchanged).
+    rng = np.random.default_rng(1)
+    rows, cols = 8, 128
+    c = rng.integers(0, 16, size=(rows, cols)).astype(np.uint8)
+    c[:, ::32] = 6  # magnitude 4: top binade of E2M1
+    k = rng.integers(-6, 6, size=(rows, cols // 32))
+    bs = np.repeat(np.vectorize(lambda e: _e4m3_code(2.0 ** e))(k), 2, axis=1).astype(np.uint8)
+    g = [2.0 ** -3, 2.0 ** 2]
+    c4, s4 = mx.requant_nvfp4_to_mxfp4(c, bs, g, rows // 2)
+    assert np.array_equal(c4, c)
+    gexp = np.repeat(np.log2(g), rows // 2)[:, None]
+    assert np.array_equal(s4.astype(np.int64), (127 + k + gexp).astype(np.int64))
+    assert np.array_equal(mx.mx_dequantize(c4, s4, "fp4"), mx.nvfp4_dequantize(c, bs, g, rows // 2))
+
+
+def test_nvfp4_requant_brute_force_every_element_and_block_scale():
+    # Every E2M1 code next to a fixed +6 element, under every finite positive
+    # E4M3 block scale and a non-power-of-two global scale: the MXFP4 code is
+    # the grid point nearest to the exact scaled value (exhaustive search,
+    # ties to the even code, saturation), and the block exponent is
+    # floor(log2(6 * s_block * g)) - 2.
+    grid = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    g = 0.3
+    scales = np.array([b for b in range(1, 0x7F)], np.uint8)
+    for s in scales.tolist():
+        c = np.zeros((16, 32), np.uint8)
+        c[:, 0] = np.arange(16)
+        c[:, 1] = 7
+        bs = np.full((16, 2), s, np.uint8)
+        v = mx.nvfp4_dequantize(c, bs, [g], 16)
+        c4, s4 = mx.requant_nvfp4_to_mxfp4(c, bs, [g], 16)
+        amax = float(np.float32(6 * mx.e4m3_value(s)) * np.float32(g))
+        e = math.floor(math.log2(amax)) - 2
+        if amax == 0 or e < -127:
+            continue
+        assert np.all(s4 == e + 127), s
+        for i in range(16):
+            q = abs(v[i, 0]) / 2.0 ** e
+            dist = [abs(q - p) for p in grid]
+            best = min(dist)
+            cands = [j for j in range(8) if dist[j] == best]
+            j = cands[0] if len(cands) == 1 else [j for j in cands if j % 2 == 0][0]
+            if q > 6:
+                j = 7
+            want = j | (8 if (i & 8) else 0)
+            assert c4[i, 0] == want, (s, i, q, c4[i, 0], want)
