@@ -427,6 +427,15 @@ __device__ __forceinline__ void unit_shared_strip(const DA& A, uint32_t tag, Sme
   __syncthreads();  // sm.red and x8 are reused
 }
 
+// Gate/up unit i of the folded shared expert (expert E of the table, every
+// row in slot k of its row), run in phase A since every row selects it: the
+// workgroup makes the MXFP4 copy of all rows of x (its first loads issued
+// ahead of the weight tiles), then the unit computes like a routed one and
+// stores the SwiGLU values of slots t*kk + k as tagged words.
+template <class DA>
+__device__ __forceinline__ void unit_fold_gu(const DA& A, uint32_t tag, Smem& sm, int i, uint8_t* xq4, uint8_t* xs4,
+                                             bool& have_x4, int lane, int wave);
+
 // Chunk sums of a routed gate/up unit in sm.red, added in chunk order, then
 // SwiGLU: thread (row, column) for row < n; returns false for idle threads.
 __device__ __forceinline__ bool gu_finish(const Smem& sm, int nc, int n, int* row, int* col, float* a) {
@@ -483,6 +492,7 @@ __device__ __forceinline__ void build_expert_list(const DA& A, Smem& sm, int lan
 struct Seq {
   int b0, nb, c0, nc;
   int D, nhg, ns;  // selected experts, 64-column groups, shared down units (nhg or 0)
+  int fold;        // the last selected expert is the folded shared expert (gate/up done in phase A)
 };
 
 struct Buf {
@@ -507,16 +517,15 @@ struct Buf {
 // The scale words are gathered in scalars and stored to buf once, on a single
 // path: stores to different members on different paths get merged into one
 // store through a pointer, which keeps buf in scratch memory.
+// The weight tiles and scale words of a gate/up unit (expert e, 16-column
+// strip i of the gate half and of the up half; this wavefront's K-chunk).
+// The scale words come back in n0..n5 (the caller stores them to buf on its
+// single store path); false for a wavefront without a K-chunk.
 template <class DA>
-__device__ __forceinline__ void issue(const DA& A, const Smem& sm, const Seq& S, int j, int lane, int wave,
-                                      Buf& buf) {
-  if (j >= S.nb + S.nc) return;
-  uint32_t n0 = 0, n1 = 0, n2 = 0, n3 = 0, n4 = 0, n5 = 0;
-  if (j < S.nb) {
-    if (wave >= A.nc1()) return;
-    const int u = S.b0 + j;
-    const int per = A.i() / 16;
-    const int e = sm.elist[u / per], i = u % per;
+__device__ __forceinline__ bool issue_gu(const DA& A, int e, int i, int lane, int wave, Buf& buf, uint32_t& n0,
+                                         uint32_t& n1, uint32_t& n2, uint32_t& n3, uint32_t& n4, uint32_t& n5) {
+  if (wave >= A.nc1()) return false;
+  {
     const int CT = A.ct1(), KG = (A.kt1() + 3) / 4, t0 = wave * CT;
     const uint8_t* base = A.w13 + (size_t)e * ((size_t)A.i() * A.h());
     const uint8_t* sbase = A.w13s + (size_t)e * ((size_t)(2 * A.i() / 16) * KG * 256);
@@ -537,6 +546,29 @@ __device__ __forceinline__ void issue(const DA& A, const Smem& sm, const Seq& S,
     n3 = load_stream4(sp1 + (size_t)min(t0 / 4, KG - 1) * 256);
     n4 = load_stream4(sp1 + (size_t)min(t0 / 4 + 1, KG - 1) * 256);
     n5 = load_stream4(sp1 + (size_t)min(t0 / 4 + 2, KG - 1) * 256);
+  }
+  return true;
+}
+
+// Expert (index into the selected-expert list) of routed down unit ur: with
+// the shared expert folded in (the list's last entry) its units come first.
+__device__ __forceinline__ int down_expert(const Seq& S, int ur) {
+  const int q = ur / S.nhg;
+  return S.fold ? (q == 0 ? S.D - 1 : q - 1) : q;
+}
+
+// Requests the weight tiles and scale words of sequence entry j into buf.
+// The scale words are gathered in scalars and stored to buf once, on a single
+// path: stores to different members on different paths get merged into one
+// store through a pointer, which keeps buf in scratch memory.
+template <class DA>
+__device__ __forceinline__ void issue(const DA& A, const Smem& sm, const Seq& S, int j, int lane, int wave,
+                                      Buf& buf) {
+  if (j >= S.nb + S.nc) return;
+  uint32_t n0 = 0, n1 = 0, n2 = 0, n3 = 0, n4 = 0, n5 = 0;
+  if (j < S.nb) {
+    const int u = S.b0 + j, per = A.i() / 16;
+    if (!issue_gu(A, sm.elist[u / per], u % per, lane, wave, buf, n0, n1, n2, n3, n4, n5)) return;
   } else {
     // down units: both kinds load 1 KB weight blocks at a 1 KB stride (a
     // routed FP4 tile is one block, a shared FP8 tile two) and two scale words
@@ -545,7 +577,7 @@ __device__ __forceinline__ void issue(const DA& A, const Smem& sm, const Seq& S,
     int nq, KG;
     if (u >= S.ns) {
       const int ur = u - S.ns;
-      const int e = sm.elist[ur / S.nhg], hs = 4 * (ur % S.nhg) + wave;
+      const int e = sm.elist[down_expert(S, ur)], hs = 4 * (ur % S.nhg) + wave;
       KG = (A.kt2() + 3) / 4;
       nq = min(A.kt2(), kDownBatch);
       wb = A.w2 + (size_t)e * ((size_t)A.h() * A.i() / 2) + (size_t)hs * A.kt2() * 1024 + lane * 16;
@@ -573,15 +605,23 @@ __device__ __forceinline__ void issue(const DA& A, const Smem& sm, const Seq& S,
 
 // Routed gate/up: MFMA chain of this wave's K-chunk for both strips into
 // sm.red (A operand: the MXFP4 x rows of the routed slots, from LDS).
+// Row m of the unit's A operand is x row tok (from the unit's slot list, or
+// the row itself for the folded shared expert's units, which take every row).
 template <class DA>
 __device__ __forceinline__ void gu_compute(const DA& A, Smem& sm, const uint8_t* xq4_lds,
                                            const uint8_t* xs4_lds, int dd, const Buf& buf, int lane, int wave) {
   if (wave >= A.nc1()) return;
-  const int n = sm.ecount[dd];
-  const int m = lane & 15, q = lane >> 4;
-  // rows past the expert's slot count repeat its last token: their products
-  // land in result rows that are never read
-  const int tok = sm.tl[dd][m < n ? m : n - 1] / A.kk();
+  const int m = lane & 15;
+  int tok;
+  if (dd >= 0) {
+    const int n = sm.ecount[dd];
+    // rows past the expert's slot count repeat its last token: their
+    // products land in result rows that are never read
+    tok = sm.tl[dd][m < n ? m : n - 1] / A.kk();
+  } else {
+    tok = m < A.T ? m : A.T - 1;
+  }
+  const int q = lane >> 4;
   const int CT = A.ct1(), t0 = wave * CT;
   v4i a[kMaxCT];
   uint32_t sa[kMaxCT];
@@ -606,6 +646,41 @@ __device__ __forceinline__ void gu_compute(const DA& A, Smem& sm, const uint8_t*
 #pragma unroll
     for (int r = 0; r < 4; ++r) sm.red[wave][s][4 * q + r][m] = acc[r];
   }
+}
+
+template <class DA>
+__device__ __forceinline__ void unit_fold_gu(const DA& A, uint32_t tag, Smem& sm, int i, uint8_t* xq4, uint8_t* xs4,
+                                             bool& have_x4, int lane, int wave) {
+  const int tasks = A.T * (A.h() / 32);
+  uint32_t bits[kQBatch][4];
+  const bool quant = !have_x4;  // uniform
+  if (quant) x_batch_load<false>(A, 0, tasks, nullptr, bits);
+  Buf buf;
+  uint32_t n0 = 0, n1 = 0, n2 = 0, n3 = 0, n4 = 0, n5 = 0;
+  issue_gu(A, A.e(), i, lane, wave, buf, n0, n1, n2, n3, n4, n5);
+  buf.w0 = n0;
+  buf.w1 = n1;
+  buf.w2 = n2;
+  buf.w3 = n3;
+  buf.w4 = n4;
+  buf.w5 = n5;
+  if (quant) {
+    for (int b0 = 0; b0 < tasks; b0 += kQBatch * kQGroups) {
+      if (b0 > 0) x_batch_load<false>(A, b0, tasks, nullptr, bits);
+      x_batch_quant<FP4, false>(A, b0, tasks, nullptr, bits, xq4, xs4);
+    }
+    have_x4 = true;
+    trace_at(A, TR_XQ);
+  }
+  __syncthreads();  // the x rows are in LDS
+  gu_compute(A, sm, xq4, xs4, -1, buf, lane, wave);
+  trace_at(A, TR_S_MMA);
+  __syncthreads();
+  int row, col;
+  float a;
+  if (gu_finish(sm, A.nc1(), A.T, &row, &col, &a))
+    st_dev(&A.a_r[(size_t)(row * A.kk() + A.kr()) * A.i() + 16 * i + col], tagged(tag, a));
+  __syncthreads();  // sm.red is rewritten by the next unit
 }
 
 // Staging of a down unit's intermediate rows into LDS as MX blocks: codes
@@ -834,7 +909,7 @@ __device__ __forceinline__ void run_entry(const DA& A, uint32_t tag, Smem& sm, c
   }
   const int u = S.c0 + j - S.nb;  // shared down units first, then routed
   const bool routed = u >= S.ns;
-  const int dd = routed ? (u - S.ns) / S.nhg : -1;
+  const int dd = routed ? down_expert(S, u - S.ns) : -1;
   const int hg = routed ? (u - S.ns) % S.nhg : u;  // 64-column group
   const int hs = 4 * hg + wave;
   const int m = lane & 15, q = lane >> 4;
@@ -848,7 +923,7 @@ __device__ __forceinline__ void run_entry(const DA& A, uint32_t tag, Smem& sm, c
     // routed down unit of the same expert.  Every thread derives this from
     // the sequence itself, so the whole workgroup takes the same branch.
     const int pu = u - 1;
-    if (!(j > S.nb && pu >= S.ns && (pu - S.ns) / S.nhg == dd)) {
+    if (!(j > S.nb && pu >= S.ns && (pu - S.ns) / S.nhg == (u - S.ns) / S.nhg)) {
       stage_routed(A, tag, K, n, sm.tl[dd], codes, scales);
       __syncthreads();
       if (j == S.nb) trace_at(A, TR_C_STAGED);
@@ -901,12 +976,18 @@ __device__ __forceinline__ void decode_body(const DA& A, uint32_t tag, Smem& sm,
   // phase A: router units, then shared gate/up strips, strided over the grid.
   // With few rows a strip leaves the MXFP4 copy of x in LDS and the other
   // workgroups make it after their units.
-  const int n_ss = A.is() ? 2 * A.is() / 16 : 0;
+  // units after the router's: MXFP8 shared gate/up strips, or the folded
+  // shared expert's gate/up units (all rows select it)
+  const int n_ss = A.is() ? 2 * A.is() / 16 : (A.fd() ? A.i() / 16 : 0);
   const bool early_x4 = T <= kEarlyQuantT;
-  bool have_x4 = false;
+  bool have_x4 = false;      // the MXFP4 copy of x in LDS holds the rows the units need
+  bool have_all_x4 = false;  // ... and it holds every row
   for (int u = blockIdx.x; u < E + n_ss; u += G) {
     if (u < E) {
       unit_router(A, tag, u, lane, wave);
+    } else if (A.fd()) {
+      unit_fold_gu(A, tag, sm, u - E, xq4_lds, xs4_lds, have_all_x4, lane, wave);
+      have_x4 = true;
     } else {
       unit_shared_strip(A, tag, sm, u - E, x8_lds, xq4_lds, xs4_lds, lane, wave);
       have_x4 = early_x4;
@@ -975,8 +1056,9 @@ __device__ __forceinline__ void decode_body(const DA& A, uint32_t tag, Smem& sm,
   S.D = sm.D;
   S.nhg = A.h() / 64;
   S.ns = A.is() ? S.nhg : 0;
+  S.fold = A.fd();
   {
-    const int NB = S.D * (A.i() / 16);
+    const int NB = (S.D - S.fold) * (A.i() / 16);  // the folded expert's gate/up ran in phase A
     const int NCU = S.ns + S.D * S.nhg;
     const unsigned b = blockIdx.x, g = (unsigned)G;  // products stay below 2^24
     S.b0 = (int)((unsigned)NB * b / g);
@@ -992,7 +1074,7 @@ __device__ __forceinline__ void decode_body(const DA& A, uint32_t tag, Smem& sm,
   // before the pipeline's weight tiles are requested: a wait for x issued
   // after them would also wait for every tile in flight.
   uint32_t need = 0;
-  if (!early_x4 && S.nb > 0) {
+  if (!early_x4 && !have_all_x4 && S.nb > 0) {
     const int per = A.i() / 16;
     for (int dd = S.b0 / per; dd <= (S.b0 + S.nb - 1) / per; ++dd)
       for (int s = 0; s < sm.ecount[dd]; ++s) need |= 1u << (sm.tl[dd][s] / A.kk());
