@@ -84,9 +84,12 @@ def build_layers(binding, synth, name, count, fold=False):
     return cfg, layers
 
 
-def time_decode(binding, synth, name, rotate, steps, warmup, pool=64, isolated=True, fold=False):
+def time_decode(binding, synth, name, rotate, steps, warmup, pool=64, isolated=True, fold=False, norm=False):
     import torch
     cfg, layers = build_layers(binding, synth, name, rotate, fold)
+    if norm:  # the pre-router RMSNorm fused in: the input is the residual stream
+        gamma = torch.from_numpy(synth.norm_weight(cfg)).cuda()
+        layers = [L.with_norm(gamma) for L in layers]
     T = cfg["T"]
     xs = [torch.from_numpy(synth.activations(cfg, T=T, index=j).view(np.int16)).cuda().view(torch.bfloat16)
           for j in range(pool)]
@@ -140,7 +143,8 @@ def time_decode(binding, synth, name, rotate, steps, warmup, pool=64, isolated=T
         raise RuntimeError("a device-side wait timed out during the benchmark")
     ids_np = ids.cpu().numpy()
     D = np.array([len(np.unique(ids_np[i])) for i in range(steps)])
-    nbytes = np.array([layer_bytes(cfg["H"], cfg["I"], cfg["E"], cfg["I_s"], d, T, folded=fold) for d in D])
+    nbytes = np.array([layer_bytes(cfg["H"], cfg["I"], cfg["E"], cfg["I_s"], d, T, folded=fold) +
+                       (cfg["H"] * 4 if norm else 0) for d in D])
     del layers
     torch.cuda.empty_cache()
     return {
@@ -330,6 +334,7 @@ def main():
     ap.add_argument("--no-chain", action="store_true", help="skip the 8-layer graph-replayed chain")
     ap.add_argument("--no-folded", action="store_true",
                     help="skip the layers with the shared expert folded into the table as an MXFP4 expert")
+    ap.add_argument("--no-norm", action="store_true", help="skip the layers with the pre-router RMSNorm fused in")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-isolated", action="store_true",
                     help="skip the one-launch-at-a-time timing (profiler runs: only back-to-back launches)")
@@ -369,6 +374,15 @@ def main():
                                    isolated=False, fold=True)
             print(f"[bench] {label}, shared expert folded (MXFP4 expert 128): {rf[name]['us_launch']:.2f} us per "
                   f"launch, {rf[name]['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    rn = {}
+    if not args.no_norm:
+        for name, label in (("decode1", "1 row"), ("decode16", "16 rows")):
+            if name == "decode16" and args.no_16:
+                continue
+            rn[name] = time_decode(binding, synth, name, max(4, args.rotate // 2), args.steps, args.warmup,
+                                   isolated=False, norm=True)
+            print(f"[bench] {label}, pre-router RMSNorm fused in: {rn[name]['us_launch']:.2f} us per launch, "
+                  f"{rn[name]['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
     rc = None
     if not args.no_chain:
         rc = time_chain(binding, synth)
@@ -433,6 +447,14 @@ def main():
                 "frac": round(r["gbs"] / HBM_PEAK_GBS, 4), "distinct_routed_experts_mean":
                 round(r["distinct_experts_mean"], 2), "algorithmic_bytes_per_launch": int(r["bytes_mean"])}
                for n, r in rf.items()}}
+    if rn:
+        out["fused_norm"] = {
+            "workload": "the same layers with the pre-router RMSNorm fused into the launch (input = residual "
+                        "stream h, MoE on RMSNorm(h), h added back)",
+            **{("rows1" if n == "decode1" else "rows16"): {
+                "us_per_launch": round(r["us_launch"], 3), "gbs": round(r["gbs"], 1),
+                "frac": round(r["gbs"] / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": int(r["bytes_mean"])}
+               for n, r in rn.items()}}
     if rc:
         out["chain8"] = {
             "workload": "8 distinct layers (hidden 3072, 128 experts top-4, I 1024, MXFP8 shared 1024), 4 rows, "

@@ -164,6 +164,18 @@ moe_status mxfp4_quant_act(const uint16_t* x, int rows, int cols, uint8_t* codes
  * The router still chooses among experts 0..E-1.  Requires shared_inter = 0
  * (the ws* pointers are ignored), top_k <= 7 and num_experts <= 255.
  * shared_folded = 0: an MXFP8 shared expert as given by shared_inter / ws*.
+ *
+ * norm_weight != NULL: the RMSNorm in front of the router is fused into the
+ * layer call (mono decode fuses "the RMSNorm and router", article section
+ * "Serving with vLLM / What we Optimized").  The call's input is then the
+ * residual stream h, and with g = norm_weight
+ *   r[t] = 1 / sqrtf(S[t] / H + norm_eps),  S[t] = sum_h h[t,h]^2 in fp32
+ *          (lane l of a wavefront FMAs h = 256 i + 4 l + c, i ascending,
+ *          c = 0..3, then a butterfly over lane distances 32 .. 1)
+ *   x[t,h] = (h[t,h] * r[t]) * g[h]          two fp32 products, no bf16 step
+ * x feeds the router and the MX quantizers, and h itself is added back:
+ *   y[t] = bf16( h[t] + sum_j w[t,j] d[t,j] + s[t] ).
+ * The residual argument of the layer calls must then be NULL.
  */
 typedef struct {
   int32_t hidden;        /* H: multiple of 128 */
@@ -182,6 +194,8 @@ typedef struct {
   const uint8_t* ws2;         /* tiled FP8 [H][I_s], NULL if I_s == 0 */
   const uint8_t* ws2_scale;
   int32_t shared_folded;      /* 0 or 1, see above */
+  const float* norm_weight;   /* [H] fp32 pre-router RMSNorm weight, or NULL (see below) */
+  float norm_eps;             /* its epsilon */
 } moe_layer_t;
 
 /*

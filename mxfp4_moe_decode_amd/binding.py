@@ -44,6 +44,7 @@ class MoeLayerC(ctypes.Structure):
         ("ws13", ctypes.c_void_p), ("ws13_scale", ctypes.c_void_p),
         ("ws2", ctypes.c_void_p), ("ws2_scale", ctypes.c_void_p),
         ("shared_folded", ctypes.c_int32),
+        ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
     ]
 
 
@@ -207,10 +208,11 @@ class MoELayer:
 
     def __init__(self, hidden, inter, num_experts, top_k, shared_inter, router_w, router_bias,
                  w13, w13_scale, w2, w2_scale, ws13=None, ws13_scale=None, ws2=None, ws2_scale=None,
-                 shared_folded=False):
+                 shared_folded=False, norm_weight=None, norm_eps=1e-6):
         self.hidden, self.inter, self.num_experts, self.top_k, self.shared_inter = (
             hidden, inter, num_experts, top_k, shared_inter)
         self.shared_folded = bool(shared_folded)
+        self.norm_weight, self.norm_eps = norm_weight, float(norm_eps)
         self.router_w, self.router_bias = router_w, router_bias
         self.w13, self.w13_scale, self.w2, self.w2_scale = w13, w13_scale, w2, w2_scale
         self.ws13, self.ws13_scale, self.ws2, self.ws2_scale = ws13, ws13_scale, ws2, ws2_scale
@@ -220,7 +222,8 @@ class MoELayer:
                             ws13.data_ptr() if ws13 is not None else None,
                             ws13_scale.data_ptr() if ws13_scale is not None else None,
                             ws2.data_ptr() if ws2 is not None else None,
-                            ws2_scale.data_ptr() if ws2_scale is not None else None, int(self.shared_folded))
+                            ws2_scale.data_ptr() if ws2_scale is not None else None, int(self.shared_folded),
+                            norm_weight.data_ptr() if norm_weight is not None else None, self.norm_eps)
 
     @property
     def c(self):
@@ -267,6 +270,13 @@ class MoELayer:
             sh = dict(ws13=q13, ws13_scale=q13s, ws2=q2, ws2_scale=q2s)
         return cls(H, I, E, top_k, Is, dev_f32(router_w), rb, w13, w13s, w2, w2s, **sh)
 
+    def with_norm(self, weight, eps=1e-6):
+        """The same layer with the pre-router RMSNorm fused in (``weight``: an
+        fp32 [H] CUDA tensor): its input is then the residual stream."""
+        return MoELayer(self.hidden, self.inter, self.num_experts, self.top_k, self.shared_inter, self.router_w,
+                        self.router_bias, self.w13, self.w13_scale, self.w2, self.w2_scale, self.ws13,
+                        self.ws13_scale, self.ws2, self.ws2_scale, self.shared_folded, weight.contiguous(), eps)
+
     def folded_from(self, fp4_13, fp4_13s, fp4_2, fp4_2s):
         """A folded-shared copy of this layer sharing its routed weights:
         the routed tables are copied into (E + 1)-expert tables and expert E
@@ -275,7 +285,8 @@ class MoELayer:
         cat = lambda a, b: torch.cat([a, b.reshape(-1)]).contiguous()
         return MoELayer(self.hidden, self.inter, E, self.top_k, 0, self.router_w, self.router_bias,
                         cat(self.w13, fp4_13), cat(self.w13_scale, fp4_13s), cat(self.w2, fp4_2),
-                        cat(self.w2_scale, fp4_2s), shared_folded=True)
+                        cat(self.w2_scale, fp4_2s), shared_folded=True, norm_weight=self.norm_weight,
+                        norm_eps=self.norm_eps)
 
 
 # --------------------------------------------------------------------------- router / sort

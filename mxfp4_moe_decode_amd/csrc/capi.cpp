@@ -24,6 +24,7 @@ moe_status check_layer(const moe_layer_t* L) {
   if (!aligned(L->router_w, 16) || !aligned(L->router_bias, 4)) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(L->w13, 16) || !aligned(L->w2, 16) || !aligned(L->w13_scale, 4) || !aligned(L->w2_scale, 4))
     return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(L->norm_weight, 16) || !(L->norm_eps >= 0.f)) return MOE_ERR_INVALID_ARGUMENT;
   if (L->shared_folded != 0 && L->shared_folded != 1) return MOE_ERR_INVALID_ARGUMENT;
   if (L->shared_folded && (Is != 0 || k > 7 || E > 255)) return MOE_ERR_INVALID_ARGUMENT;
   if (Is > 0) {
@@ -148,6 +149,7 @@ moe_status fused_moe_mxfp4_decode(const moe_layer_t* layer, const uint16_t* x, i
   const moe_status st = check_layer(layer);
   if (st != MOE_OK) return st;
   if (!x || !y || !ws || T <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (layer->norm_weight && residual) return MOE_ERR_INVALID_ARGUMENT;  // the norm adds its own input
   if (T > kDecodeMaxT || !decode_supported(*layer)) return MOE_ERR_UNSUPPORTED;
   if (static_cast<const void*>(y) == static_cast<const void*>(x)) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(y, 4) || !aligned(residual, 4) || !aligned(ws, 256))
@@ -162,6 +164,7 @@ moe_status fused_moe_mxfp4_decode_noalloc(const moe_layer_t* layer, const uint16
   const moe_status st = check_layer(layer);
   if (st != MOE_OK) return st;
   if (!x || !y || T <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (layer->norm_weight && residual) return MOE_ERR_INVALID_ARGUMENT;  // the norm adds its own input
   if (T > kDecodeMaxT || !decode_supported(*layer)) return MOE_ERR_UNSUPPORTED;
   if (static_cast<const void*>(y) == static_cast<const void*>(x)) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(y, 4) || !aligned(residual, 4)) return MOE_ERR_INVALID_ARGUMENT;
@@ -177,6 +180,7 @@ moe_status grouped_call(const moe_layer_t* layer, const uint16_t* x, int T, cons
   const moe_status st = check_layer(layer);
   if (st != MOE_OK) return st;
   if (!x || !y || !ws || T <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (layer->norm_weight && residual) return MOE_ERR_INVALID_ARGUMENT;  // the norm adds its own input
   if (static_cast<const void*>(y) == static_cast<const void*>(x)) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(residual, 16) || !aligned(ws, 256))
     return MOE_ERR_INVALID_ARGUMENT;

@@ -82,6 +82,9 @@ enum {
 struct DecodeArgs {
   int T, H, I, E, k, Is, G;
   int fold;           // the shared expert is expert E of the table (1) or MXFP8 (0)
+  const float* norm_w;  // pre-router RMSNorm weight [H], or null
+  float norm_eps;
+  int gamma_off;        // dynamic-LDS byte offset of the norm weight's copy
   int KT1, CT1, NC1;  // K = H: tiles of 128, tiles per chunk, chunks
   int KT2, CT2;       // K = I
   int KTs, CTs;       // K = I_s
@@ -112,6 +115,7 @@ struct DecodeArgs {
 constexpr int n_chunks_of(int tiles) { return tiles % 4 == 0 ? 4 : (tiles % 2 == 0 ? 2 : 1); }
 template <int H_, int I_, int IS_, int E_, int K_, int FOLD_>
 struct DArgs : DecodeArgs {
+  static constexpr bool kFixedShape = H_ != 0;  // a compiled instance for one layer shape
   __device__ __forceinline__ int h() const { return H_ ? H_ : H; }
   __device__ __forceinline__ int i() const { return I_ ? I_ : I; }
   __device__ __forceinline__ int is() const { return IS_ ? (IS_ < 0 ? 0 : IS_) : Is; }
@@ -146,6 +150,7 @@ struct Smem {
   float red[kWaves][2][kDecodeMaxT][16];        // chunk sums [chunk][gate/up][row][column]
   int wave_cnt[kWaves];
   uint8_t qrows[kDecodeMaxT];                   // rows of x quantized for this workgroup's gate/up units
+  float rnorm[kDecodeMaxT];                      // pre-router RMSNorm factor of each row
   int D;
   int flag;
   int last;                                     // this workgroup is the call's last to finish
@@ -276,6 +281,41 @@ __device__ __forceinline__ void x_batch_load(const DA& A, int t0, int tasks, con
   }
 }
 
+// With the pre-router norm, before the workgroup's first x quantization: the
+// norm weight copied into LDS and, unless a router unit of this workgroup has
+// left them in sm.rnorm, every row's norm factor.
+template <class DA>
+__device__ __forceinline__ void norm_setup(const DA& A, Smem& sm, float* gamma_lds, bool need_r, int lane, int wave) {
+  for (int i = threadIdx.x; i < A.h() / 4; i += kThreads)
+    reinterpret_cast<float4*>(gamma_lds)[i] = reinterpret_cast<const float4*>(A.norm_w)[i];
+  if (need_r)
+    for (int t = wave; t < A.T; t += kWaves) {
+      const float v = row_rms_inv(A.x + (size_t)t * A.h(), A.h(), A.norm_eps, lane);
+      if (lane == 0) sm.rnorm[t] = v;
+    }
+  __syncthreads();
+}
+
+// With the pre-router norm: the loaded batch becomes (h * r) * g.
+template <bool kRows, class DA>
+__device__ __forceinline__ void x_batch_norm(const DA& A, const Smem& sm, const float* gamma_lds, int t0, int tasks,
+                                             const uint8_t* rows, uint32_t (&bits)[kQBatch][4]) {
+  const int H = A.h(), nb = H / 32, j = threadIdx.x & 7, grp = threadIdx.x / 8;
+#pragma unroll
+  for (int p = 0; p < kQBatch; ++p) {
+    const int task = t0 + p * kQGroups + grp;
+    if (task < tasks) {
+      const int row = kRows ? rows[task / nb] : task / nb;
+      const float r = sm.rnorm[row];
+      const float4 g = *reinterpret_cast<const float4*>(gamma_lds + 32 * (task % nb) + 4 * j);
+      bits[p][0] = normed_bits(bits[p][0], r, g.x);
+      bits[p][1] = normed_bits(bits[p][1], r, g.y);
+      bits[p][2] = normed_bits(bits[p][2], r, g.z);
+      bits[p][3] = normed_bits(bits[p][3], r, g.w);
+    }
+  }
+}
+
 // Quantizes a loaded batch to format F: codes [T][H * bytes per element],
 // scales [T][H/32] (indexed by the real row).
 template <class F, bool kRows, class DA>
@@ -307,13 +347,96 @@ __device__ __forceinline__ void x_batch_quant(const DA& A, int t0, int tasks, co
 // of the expert's weights is loaded once, then the rows go through it two at
 // a time.
 template <class DA>
-__device__ __forceinline__ void unit_router(const DA& A, uint32_t tag, int e, int lane, int wave) {
+__device__ __forceinline__ void unit_router(const DA& A, Smem& sm, uint32_t tag, int e, int lane, int wave) {
   const float* wrow = A.router_w + (size_t)e * A.h();
   const int H = A.h();
   float p[4] = {0.f, 0.f, 0.f, 0.f};
   int nr = 0;
   for (int t = wave; t < A.T; t += kWaves) ++nr;
   if (nr == 0) return;
+  if (A.norm_w) {
+    // The normalized rows (h * r) * g.  With H <= 4096 the unit loads the
+    // expert's weights and g once, then takes the rows two at a time: each
+    // row's norm factor comes from the x values already in registers (same
+    // order as row_rms_inv: lane partial sums over h = 256 i + 4 l + c, then
+    // the butterfly) and is left in sm.rnorm for the workgroup's own x
+    // quantization.  Wider rows, and the run-time shape instance (whose
+    // registers this would exhaust), take the factor from row_rms_inv first.
+    if (DA::kFixedShape && H <= 16 * 256) {
+      float4 w[16], g[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (4 * lane + 256 * j < H) {
+          w[j] = load_stream_f4(wrow + 4 * lane + 256 * j);
+          g[j] = *reinterpret_cast<const float4*>(A.norm_w + 4 * lane + 256 * j);
+        }
+#pragma unroll
+      for (int r0 = 0; r0 < 4; r0 += 2) {
+        if (r0 < nr) {
+          uint2 xv[2][16];
+#pragma unroll
+          for (int r = 0; r < 2; ++r)
+            if (r0 + r < nr) {
+              const uint16_t* xr = A.x + (size_t)(wave + kWaves * (r0 + r)) * H;
+#pragma unroll
+              for (int j = 0; j < 16; ++j)
+                if (4 * lane + 256 * j < H) xv[r][j] = *reinterpret_cast<const uint2*>(xr + 4 * lane + 256 * j);
+            }
+#pragma unroll
+          for (int r = 0; r < 2; ++r)
+            if (r0 + r < nr) {
+              float sq = 0.f;
+#pragma unroll
+              for (int j = 0; j < 16; ++j)
+                if (4 * lane + 256 * j < H) {
+                  const float a = bf16_to_f32(xv[r][j].x & 0xffffu), b = bf16_to_f32(xv[r][j].x >> 16);
+                  const float c = bf16_to_f32(xv[r][j].y & 0xffffu), d = bf16_to_f32(xv[r][j].y >> 16);
+                  sq = fmaf(a, a, sq);
+                  sq = fmaf(b, b, sq);
+                  sq = fmaf(c, c, sq);
+                  sq = fmaf(d, d, sq);
+                }
+              const float rr = 1.0f / sqrtf(wave_sum_butterfly(sq) / (float)H + A.norm_eps);
+              if (lane == 0) sm.rnorm[wave + kWaves * (r0 + r)] = rr;
+              float& acc = p[r0 + r];
+#pragma unroll
+              for (int j = 0; j < 16; ++j)
+                if (4 * lane + 256 * j < H) {
+                  acc = fmaf(__uint_as_float(normed_bits((xv[r][j].x & 0xffffu) << 16, rr, g[j].x)), w[j].x, acc);
+                  acc = fmaf(__uint_as_float(normed_bits(xv[r][j].x & 0xffff0000u, rr, g[j].y)), w[j].y, acc);
+                  acc = fmaf(__uint_as_float(normed_bits((xv[r][j].y & 0xffffu) << 16, rr, g[j].z)), w[j].z, acc);
+                  acc = fmaf(__uint_as_float(normed_bits(xv[r][j].y & 0xffff0000u, rr, g[j].w)), w[j].w, acc);
+                }
+            }
+        }
+      }
+    } else {
+      for (int r = 0; r < nr; ++r) {
+        const int row = wave + kWaves * r;
+        const float rr = row_rms_inv(A.x + (size_t)row * H, H, A.norm_eps, lane);
+        if (lane == 0) sm.rnorm[row] = rr;
+        const uint16_t* xr = A.x + (size_t)row * H;
+        float& acc = p[r];
+        for (int h0 = 4 * lane; h0 < H; h0 += 256) {
+          const float4 w = load_stream_f4(wrow + h0), g = *reinterpret_cast<const float4*>(A.norm_w + h0);
+          const uint2 xv = *reinterpret_cast<const uint2*>(xr + h0);
+          acc = fmaf(__uint_as_float(normed_bits((xv.x & 0xffffu) << 16, rr, g.x)), w.x, acc);
+          acc = fmaf(__uint_as_float(normed_bits(xv.x & 0xffff0000u, rr, g.y)), w.y, acc);
+          acc = fmaf(__uint_as_float(normed_bits((xv.y & 0xffffu) << 16, rr, g.z)), w.z, acc);
+          acc = fmaf(__uint_as_float(normed_bits(xv.y & 0xffff0000u, rr, g.w)), w.w, acc);
+        }
+      }
+    }
+    const float b = A.router_bias ? A.router_bias[e] : 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (r < nr) {
+        float v = wave_sum_butterfly(p[r]);
+        if (A.router_bias) v = v + b;
+        if (lane == 0) st_dev(&A.logits[(wave + kWaves * r) * A.e() + e], tagged(tag, v));
+      }
+    return;
+  }
   for (int h0 = 4 * lane; h0 < H; h0 += 16 * 256) {
     float4 w[16];
 #pragma unroll
@@ -367,8 +490,8 @@ __device__ __forceinline__ void unit_router(const DA& A, uint32_t tag, int e, in
 // goes to a_s[row][16 st + col] as tagged words (gate columns, then up
 // columns); SwiGLU is applied where it is staged.
 template <class DA>
-__device__ __forceinline__ void unit_shared_strip(const DA& A, uint32_t tag, Smem& sm, int st, uint8_t* x8,
-                                                  uint8_t* xq4, uint8_t* xs4, int lane, int wave) {
+__device__ __forceinline__ void unit_shared_strip(const DA& A, uint32_t tag, Smem& sm, const float* gamma_lds, int st,
+                                                  uint8_t* x8, uint8_t* xq4, uint8_t* xs4, int lane, int wave) {
   const int CT = A.ct1(), KG = (A.kt1() + 3) / 4;
   const int m = lane & 15, q = lane >> 4;
   const bool act = wave < A.nc1();
@@ -393,6 +516,7 @@ __device__ __forceinline__ void unit_shared_strip(const DA& A, uint32_t tag, Sme
   }
   for (int b0 = 0; b0 < tasks; b0 += kQBatch * kQGroups) {
     if (b0 > 0) x_batch_load<false>(A, b0, tasks, nullptr, bits);
+    if (A.norm_w) x_batch_norm<false>(A, sm, gamma_lds, b0, tasks, nullptr, bits);
     x_batch_quant<FP8, false>(A, b0, tasks, nullptr, bits, x8, xs8);
     if (A.T <= kEarlyQuantT) x_batch_quant<FP4, false>(A, b0, tasks, nullptr, bits, xq4, xs4);
   }
@@ -433,8 +557,8 @@ __device__ __forceinline__ void unit_shared_strip(const DA& A, uint32_t tag, Sme
 // ahead of the weight tiles), then the unit computes like a routed one and
 // stores the SwiGLU values of slots t*kk + k as tagged words.
 template <class DA>
-__device__ __forceinline__ void unit_fold_gu(const DA& A, uint32_t tag, Smem& sm, int i, uint8_t* xq4, uint8_t* xs4,
-                                             bool& have_x4, int lane, int wave);
+__device__ __forceinline__ void unit_fold_gu(const DA& A, uint32_t tag, Smem& sm, const float* gamma_lds, int i,
+                                             uint8_t* xq4, uint8_t* xs4, bool& have_x4, int lane, int wave);
 
 // Chunk sums of a routed gate/up unit in sm.red, added in chunk order, then
 // SwiGLU: thread (row, column) for row < n; returns false for idle threads.
@@ -649,8 +773,8 @@ __device__ __forceinline__ void gu_compute(const DA& A, Smem& sm, const uint8_t*
 }
 
 template <class DA>
-__device__ __forceinline__ void unit_fold_gu(const DA& A, uint32_t tag, Smem& sm, int i, uint8_t* xq4, uint8_t* xs4,
-                                             bool& have_x4, int lane, int wave) {
+__device__ __forceinline__ void unit_fold_gu(const DA& A, uint32_t tag, Smem& sm, const float* gamma_lds, int i,
+                                             uint8_t* xq4, uint8_t* xs4, bool& have_x4, int lane, int wave) {
   const int tasks = A.T * (A.h() / 32);
   uint32_t bits[kQBatch][4];
   const bool quant = !have_x4;  // uniform
@@ -667,6 +791,7 @@ __device__ __forceinline__ void unit_fold_gu(const DA& A, uint32_t tag, Smem& sm
   if (quant) {
     for (int b0 = 0; b0 < tasks; b0 += kQBatch * kQGroups) {
       if (b0 > 0) x_batch_load<false>(A, b0, tasks, nullptr, bits);
+      if (A.norm_w) x_batch_norm<false>(A, sm, gamma_lds, b0, tasks, nullptr, bits);
       x_batch_quant<FP4, false>(A, b0, tasks, nullptr, bits, xq4, xs4);
     }
     have_x4 = true;
@@ -972,10 +1097,18 @@ __device__ __forceinline__ void decode_body(const DA& A, uint32_t tag, Smem& sm,
   uint8_t* xs4_lds = xq4_lds + (size_t)T * (A.h() / 2);
   uint8_t* stage = xq4_lds + align_up((size_t)kDecodeMaxT * (A.h() / 2 + A.h() / 32), 16);
   uint8_t* x8_lds = stage;
+  float* gamma_lds = reinterpret_cast<float*>(dyn + A.gamma_off);  // the norm weight (with the norm)
 
   // phase A: router units, then shared gate/up strips, strided over the grid.
   // With few rows a strip leaves the MXFP4 copy of x in LDS and the other
   // workgroups make it after their units.
+  // the pre-router norm's factor of every row, in every workgroup (the same
+  // arithmetic everywhere, so all agree)
+  // pre-router norm: a router unit leaves the norm factors of all rows in
+  // sm.rnorm (have_r); norm_setup stages the weight (and the factors if
+  // missing) before the workgroup's first x quantization (have_norm)
+  bool have_r = false, have_norm = false;
+
   // units after the router's: MXFP8 shared gate/up strips, or the folded
   // shared expert's gate/up units (all rows select it)
   const int n_ss = A.is() ? 2 * A.is() / 16 : (A.fd() ? A.i() / 16 : 0);
@@ -984,21 +1117,35 @@ __device__ __forceinline__ void decode_body(const DA& A, uint32_t tag, Smem& sm,
   bool have_all_x4 = false;  // ... and it holds every row
   for (int u = blockIdx.x; u < E + n_ss; u += G) {
     if (u < E) {
-      unit_router(A, tag, u, lane, wave);
-    } else if (A.fd()) {
-      unit_fold_gu(A, tag, sm, u - E, xq4_lds, xs4_lds, have_all_x4, lane, wave);
-      have_x4 = true;
+      unit_router(A, sm, tag, u, lane, wave);
+      have_r = true;
     } else {
-      unit_shared_strip(A, tag, sm, u - E, x8_lds, xq4_lds, xs4_lds, lane, wave);
-      have_x4 = early_x4;
+      if (A.norm_w && !have_norm) {
+        __syncthreads();  // the router unit's factors are in sm.rnorm
+        norm_setup(A, sm, gamma_lds, !have_r, lane, wave);
+        have_norm = have_r = true;
+      }
+      if (A.fd()) {
+        unit_fold_gu(A, tag, sm, gamma_lds, u - E, xq4_lds, xs4_lds, have_all_x4, lane, wave);
+        have_x4 = true;
+      } else {
+        unit_shared_strip(A, tag, sm, gamma_lds, u - E, x8_lds, xq4_lds, xs4_lds, lane, wave);
+        have_x4 = early_x4;
+      }
     }
     if (threadIdx.x == 0 && u == (int)blockIdx.x) tr[TR_FIRST] = wall_clock64();
+  }
+  if (A.norm_w && !have_norm) {  // workgroups with router units only, or with no phase-A unit
+    __syncthreads();
+    norm_setup(A, sm, gamma_lds, !have_r, lane, wave);
+    have_norm = have_r = true;
   }
   if (early_x4 && !have_x4) {
     const int tasks = T * (A.h() / 32);
     for (int t0 = 0; t0 < tasks; t0 += kQBatch * kQGroups) {
       uint32_t bits[kQBatch][4];
       x_batch_load<false>(A, t0, tasks, nullptr, bits);
+      if (A.norm_w) x_batch_norm<false>(A, sm, gamma_lds, t0, tasks, nullptr, bits);
       x_batch_quant<FP4, false>(A, t0, tasks, nullptr, bits, xq4_lds, xs4_lds);
     }
     trace_at(A, TR_XQ);
@@ -1087,6 +1234,7 @@ __device__ __forceinline__ void decode_body(const DA& A, uint32_t tag, Smem& sm,
     for (int t0 = 0; t0 < q_tasks; t0 += kQBatch * kQGroups) {
       uint32_t bits[kQBatch][4];
       x_batch_load<true>(A, t0, q_tasks, sm.qrows, bits);
+      if (A.norm_w) x_batch_norm<true>(A, sm, gamma_lds, t0, q_tasks, sm.qrows, bits);
       x_batch_quant<FP4, true>(A, t0, q_tasks, sm.qrows, bits, xq4_lds, xs4_lds);
     }
     trace_at(A, TR_XQ);
@@ -1214,7 +1362,12 @@ size_t dyn_lds_bytes(const moe_layer_t& L) {
   const size_t st8 = T * ((size_t)L.shared_inter + L.shared_inter / 32);
   const size_t st = align_up(st4 > st8 ? st4 : st8, 16);
   const size_t x8 = L.shared_inter ? align_up(T * (L.hidden + L.hidden / 32), 16) : 0;
-  return logits + xq + (st > x8 ? st : x8);
+  return logits + xq + (st > x8 ? st : x8) + (L.norm_weight ? (size_t)L.hidden * 4 : 0);
+}
+
+// Offset of the norm weight's copy: the end of the other dynamic LDS data.
+size_t gamma_lds_offset(const moe_layer_t& L) {
+  return dyn_lds_bytes(L) - (L.norm_weight ? (size_t)L.hidden * 4 : 0);
 }
 
 // Grid of the persistent launch: as many workgroups as the device keeps
@@ -1284,6 +1437,9 @@ hipError_t launch_decode(const moe_layer_t& L, const uint16_t* x, int T, const u
   A.E = L.num_experts;
   A.k = L.top_k;
   A.fold = L.shared_folded ? 1 : 0;
+  A.norm_w = L.norm_weight;
+  A.norm_eps = L.norm_eps;
+  A.gamma_off = (int)gamma_lds_offset(L);
   A.Is = L.shared_inter;
   A.KT1 = A.H / 128;
   A.NC1 = n_chunks(A.KT1);
@@ -1304,7 +1460,7 @@ hipError_t launch_decode(const moe_layer_t& L, const uint16_t* x, int T, const u
   A.ws2 = L.ws2;
   A.ws2s = L.ws2_scale;
   A.x = x;
-  A.residual = residual;
+  A.residual = L.norm_weight ? x : residual;  // with the norm: its own input is the residual
   A.y = y;
   A.ids_out = ids_out;
   A.w_out = w_out;

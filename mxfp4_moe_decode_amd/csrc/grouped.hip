@@ -473,7 +473,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(int T, int k, int H, 
 int pick_chunk(int tiles) { return tiles / (tiles % 4 == 0 ? 4 : (tiles % 2 == 0 ? 2 : 1)); }
 
 struct GCarve {
-  size_t ids, w, logits, sort_ws, sorted, bexp, eoff, npad, xq4, xs4, xq8, xs8, a4, as4, a8, as8, d_part, total;
+  size_t ids, w, logits, sort_ws, sorted, bexp, eoff, npad, xq4, xs4, xq8, xs8, a4, as4, a8, as8, d_part, rnorm, total;
   size_t cap, nblk;
 };
 
@@ -505,6 +505,7 @@ GCarve gcarve(const moe_layer_t& L, int T) {
   c.a8 = Is ? take((size_t)T * Is) : 0;
   c.as8 = Is ? take((size_t)T * Is / 32) : 0;
   c.d_part = take(S * H * 4);
+  c.rnorm = L.norm_weight ? take((size_t)T * 4) : 0;
   c.total = o;
   return c;
 }
@@ -568,12 +569,19 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
                                at(c.sort_ws), stream)) != hipSuccess)
     return err;
   if ((err = mark(2)) != hipSuccess) return err;
-  // MXFP4 x (and, with a shared expert, MXFP8 x) from one read of x
+  // MXFP4 x (and, with a shared expert, MXFP8 x) from one read of x; with
+  // the pre-router norm, of the normalized rows (the router normalizes its own)
+  float* rnorm = nullptr;
+  if (L.norm_weight) {
+    rnorm = reinterpret_cast<float*>(at(c.rnorm));
+    if ((err = launch_rms_rows(x, T, H, L.norm_eps, rnorm, stream)) != hipSuccess) return err;
+    residual = x;  // the fused residual: the layer's own input
+  }
   if (Is > 0)
     err = launch_quant_act_dual(x, T, H, xq4, xs4, reinterpret_cast<uint8_t*>(at(c.xq8)),
-                                reinterpret_cast<uint8_t*>(at(c.xs8)), stream);
+                                reinterpret_cast<uint8_t*>(at(c.xs8)), stream, rnorm, L.norm_weight);
   else
-    err = launch_quant_act(x, T, H, MX_FMT_FP4, xq4, xs4, stream);
+    err = launch_quant_act(x, T, H, MX_FMT_FP4, xq4, xs4, stream, rnorm, L.norm_weight);
   if (err != hipSuccess) return err;
   if ((err = mark(3)) != hipSuccess) return err;
 

@@ -34,13 +34,18 @@ inline int current_device() {
 hipError_t launch_quant_weights(const float* w, int rows, int cols, int fmt, int layout,
                                 uint8_t* codes, uint8_t* scales, hipStream_t stream);
 // Row-major activation quantization: codes [rows, cols/2] (FP4) or [rows, cols]
-// (FP8), scales [rows, cols/32].
+// (FP8), scales [rows, cols/32].  With gamma: of the RMS-normalized rows
+// (h * rnorm[row]) * gamma[col] instead of x itself.
 hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int fmt, uint8_t* codes,
-                            uint8_t* scales, hipStream_t stream);
+                            uint8_t* scales, hipStream_t stream, const float* rnorm = nullptr,
+                            const float* gamma = nullptr);
 // Both copies at once: MXFP4 codes [rows, cols/2] and MXFP8 codes [rows, cols],
 // each with scales [rows, cols/32].
 hipError_t launch_quant_act_dual(const uint16_t* x, int rows, int cols, uint8_t* codes4, uint8_t* scales4,
-                                 uint8_t* codes8, uint8_t* scales8, hipStream_t stream);
+                                 uint8_t* codes8, uint8_t* scales8, hipStream_t stream,
+                                 const float* rnorm = nullptr, const float* gamma = nullptr);
+// rnorm[t] = 1 / sqrt(mean(x[t]^2) + eps) (the fixed order of row_rms_inv).
+hipError_t launch_rms_rows(const uint16_t* x, int rows, int cols, float eps, float* rnorm, hipStream_t stream);
 hipError_t launch_fill_u32(void* p, size_t words, uint32_t value, hipStream_t stream);
 // MXFP8 -> MXFP4 along the same blocks, either layout.
 hipError_t launch_requant_fp8_fp4(const uint8_t* codes8, const uint8_t* scales8, int rows, int cols, int layout,

@@ -199,6 +199,32 @@ __device__ __forceinline__ float wave_sum_butterfly(float p) {
   return p;
 }
 
+// ---------------------------------------------------------------------------
+// Pre-router RMSNorm, the fixed arithmetic every path uses: the sum of
+// squares of a bf16 row with lane l FMA-ing h = 256 i + 4 l + c (i ascending,
+// c = 0..3), the butterfly over the lanes, r = 1 / sqrtf(S / H + eps); the
+// normalized value is (h * r) * g, two fp32 products.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float row_rms_inv(const uint16_t* row, int H, float eps, int lane) {
+  float p = 0.f;
+  for (int h0 = 4 * lane; h0 < H; h0 += 256) {
+    const uint2 v = *reinterpret_cast<const uint2*>(row + h0);
+    const float a = bf16_to_f32(v.x & 0xffffu), b = bf16_to_f32(v.x >> 16);
+    const float c = bf16_to_f32(v.y & 0xffffu), d = bf16_to_f32(v.y >> 16);
+    p = fmaf(a, a, p);
+    p = fmaf(b, b, p);
+    p = fmaf(c, c, p);
+    p = fmaf(d, d, p);
+  }
+  const float s = wave_sum_butterfly(p);
+  return 1.0f / sqrtf(s / (float)H + eps);
+}
+
+// fp32 bits of the normalized value of bf16 bits-as-fp32 `hbits`.
+__device__ __forceinline__ uint32_t normed_bits(uint32_t hbits, float r, float g) {
+  return __float_as_uint((__uint_as_float(hbits) * r) * g);
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v, int width) {
   for (int off = width / 2; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off));
   return v;

@@ -184,10 +184,33 @@ __global__ void __launch_bounds__(kThreads) quant_weights_kernel(const float* __
   store_block<F, Tiled>(codes, scales, r, b, cols, words, s);
 }
 
+// The pre-router RMSNorm on a 32-value block of a row: (h * r) * g.
+__device__ __forceinline__ void apply_norm(uint32_t (&bits)[32], float r, const float* g) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 gv = *reinterpret_cast<const float4*>(g + 4 * i);
+    bits[4 * i] = normed_bits(bits[4 * i], r, gv.x);
+    bits[4 * i + 1] = normed_bits(bits[4 * i + 1], r, gv.y);
+    bits[4 * i + 2] = normed_bits(bits[4 * i + 2], r, gv.z);
+    bits[4 * i + 3] = normed_bits(bits[4 * i + 3], r, gv.w);
+  }
+}
+
+// r[t] = 1 / sqrt(mean(h[t]^2) + eps) for every row, a wavefront per row.
+__global__ void __launch_bounds__(kThreads) rms_rows_kernel(const uint16_t* __restrict__ x, int rows, int cols,
+                                                            float eps, float* __restrict__ rnorm) {
+  const int r = blockIdx.x * (kThreads / kWave) + (int)threadIdx.x / kWave;
+  if (r >= rows) return;  // whole wavefront
+  const float v = row_rms_inv(x + (size_t)r * cols, cols, eps, threadIdx.x % kWave);
+  if (threadIdx.x % kWave == 0) rnorm[r] = v;
+}
+
 template <class F>
 __global__ void __launch_bounds__(kThreads) quant_act_kernel(const uint16_t* __restrict__ x, int rows,
                                                              int cols, uint8_t* __restrict__ codes,
-                                                             uint8_t* __restrict__ scales) {
+                                                             uint8_t* __restrict__ scales,
+                                                             const float* __restrict__ rnorm,
+                                                             const float* __restrict__ gamma) {
   const int nb = cols / 32;
   const size_t blk = (size_t)blockIdx.x * kThreads + threadIdx.x;
   if (blk >= (size_t)rows * nb) return;
@@ -204,6 +227,7 @@ __global__ void __launch_bounds__(kThreads) quant_act_kernel(const uint16_t* __r
       bits[8 * i + 2 * j + 1] = p[j] & 0xffff0000u;
     }
   }
+  if (gamma) apply_norm(bits, rnorm[r], gamma + 32 * b);
   constexpr int kWords = F::MB == 1 ? 4 : 8;  // 16 or 32 code bytes per block
   uint32_t words[kWords];
   const uint32_t s = quant_block32<F>(bits, words);
@@ -219,7 +243,9 @@ __global__ void __launch_bounds__(kThreads) quant_act_dual_kernel(const uint16_t
                                                                   int cols, uint8_t* __restrict__ codes4,
                                                                   uint8_t* __restrict__ scales4,
                                                                   uint8_t* __restrict__ codes8,
-                                                                  uint8_t* __restrict__ scales8) {
+                                                                  uint8_t* __restrict__ scales8,
+                                                                  const float* __restrict__ rnorm,
+                                                                  const float* __restrict__ gamma) {
   const int nb = cols / 32;
   const size_t blk = (size_t)blockIdx.x * kThreads + threadIdx.x;
   if (blk >= (size_t)rows * nb) return;
@@ -236,6 +262,7 @@ __global__ void __launch_bounds__(kThreads) quant_act_dual_kernel(const uint16_t
       bits[8 * i + 2 * j + 1] = p[j] & 0xffff0000u;
     }
   }
+  if (gamma) apply_norm(bits, rnorm[r], gamma + 32 * b);
   uint32_t w4[4], w8[8];
   const uint32_t s4 = quant_block32<FP4>(bits, w4);
   const uint32_t s8 = quant_block32<FP8>(bits, w8);
@@ -319,23 +346,32 @@ hipError_t launch_quant_weights(const float* w, int rows, int cols, int fmt, int
   return hipGetLastError();
 }
 
+hipError_t launch_rms_rows(const uint16_t* x, int rows, int cols, float eps, float* rnorm, hipStream_t stream) {
+  const unsigned grid = (unsigned)((rows + kThreads / kWave - 1) / (kThreads / kWave));
+  hipLaunchKernelGGL(rms_rows_kernel, dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, eps, rnorm);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int fmt, uint8_t* codes,
-                            uint8_t* scales, hipStream_t stream) {
+                            uint8_t* scales, hipStream_t stream, const float* rnorm, const float* gamma) {
   const size_t nblk = (size_t)rows * (cols / 32);
   const unsigned grid = (unsigned)((nblk + kThreads - 1) / kThreads);
   if (fmt == MX_FMT_FP4)
-    hipLaunchKernelGGL(quant_act_kernel<FP4>, dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, codes, scales);
+    hipLaunchKernelGGL(quant_act_kernel<FP4>, dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, codes, scales,
+                       rnorm, gamma);
   else
-    hipLaunchKernelGGL(quant_act_kernel<FP8>, dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, codes, scales);
+    hipLaunchKernelGGL(quant_act_kernel<FP8>, dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, codes, scales,
+                       rnorm, gamma);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_act_dual(const uint16_t* x, int rows, int cols, uint8_t* codes4, uint8_t* scales4,
-                                 uint8_t* codes8, uint8_t* scales8, hipStream_t stream) {
+                                 uint8_t* codes8, uint8_t* scales8, hipStream_t stream, const float* rnorm,
+                                 const float* gamma) {
   const size_t nblk = (size_t)rows * (cols / 32);
   const unsigned grid = (unsigned)((nblk + kThreads - 1) / kThreads);
   hipLaunchKernelGGL(quant_act_dual_kernel, dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, codes4, scales4,
-                     codes8, scales8);
+                     codes8, scales8, rnorm, gamma);
   return hipGetLastError();
 }
 

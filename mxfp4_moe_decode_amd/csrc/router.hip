@@ -17,8 +17,10 @@ constexpr int kRouterRows = 8;  // rows a workgroup keeps in LDS
 __global__ void __launch_bounds__(kThreads) router_topk_kernel(
     const uint16_t* __restrict__ x, int T, int H, int E, int k, int rows_per_wg,
     const float* __restrict__ wr, const float* __restrict__ bias, float* __restrict__ logits_out,
-    int32_t* __restrict__ ids_out, float* __restrict__ w_out, int ld, int fold_e) {
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, int ld, int fold_e, const float* __restrict__ gamma,
+    float eps) {
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float rn[kRouterRows];  // pre-router RMSNorm factors of the staged rows (with gamma)
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                               // [rows][H]
   float* ls = reinterpret_cast<float*>(smem + align_up((size_t)rows_per_wg * H * 2, 16));  // [rows][E]
   const int t0 = blockIdx.x * rows_per_wg;
@@ -33,6 +35,13 @@ __global__ void __launch_bounds__(kThreads) router_topk_kernel(
         reinterpret_cast<const uint4*>(x + (size_t)(t0 + r) * H)[c];
   }
   __syncthreads();
+  if (gamma) {
+    for (int r = wave; r < nrows; r += kWaves) {
+      const float v = row_rms_inv(xs + (size_t)r * H, H, eps, lane);
+      if (lane == 0) rn[r] = v;
+    }
+    __syncthreads();
+  }
 
   // A wavefront per expert: each batch of up to 16 strides of the expert's
   // weights is loaded once into registers and applied to every staged row, so
@@ -47,19 +56,42 @@ __global__ void __launch_bounds__(kThreads) router_topk_kernel(
 #pragma unroll
       for (int j = 0; j < 16; ++j)
         if (h0 + 256 * j < H) w[j] = *reinterpret_cast<const float4*>(wrow + h0 + 256 * j);
+      if (gamma) {
+        float4 g[16];
 #pragma unroll
-      for (int r = 0; r < kRouterRows; ++r) {
-        if (r < nrows) {
-          const uint16_t* xr = xs + (size_t)r * H;
+        for (int j = 0; j < 16; ++j)
+          if (h0 + 256 * j < H) g[j] = *reinterpret_cast<const float4*>(gamma + h0 + 256 * j);
 #pragma unroll
-          for (int j = 0; j < 16; ++j)
-            if (h0 + 256 * j < H) {
-              const uint2 xv = *reinterpret_cast<const uint2*>(xr + h0 + 256 * j);
-              p[r] = fmaf(bf16_to_f32(xv.x & 0xffffu), w[j].x, p[r]);
-              p[r] = fmaf(bf16_to_f32(xv.x >> 16), w[j].y, p[r]);
-              p[r] = fmaf(bf16_to_f32(xv.y & 0xffffu), w[j].z, p[r]);
-              p[r] = fmaf(bf16_to_f32(xv.y >> 16), w[j].w, p[r]);
-            }
+        for (int r = 0; r < kRouterRows; ++r) {
+          if (r < nrows) {
+            const uint16_t* xr = xs + (size_t)r * H;
+            const float rr = rn[r];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              if (h0 + 256 * j < H) {
+                const uint2 xv = *reinterpret_cast<const uint2*>(xr + h0 + 256 * j);
+                p[r] = fmaf(__uint_as_float(normed_bits((xv.x & 0xffffu) << 16, rr, g[j].x)), w[j].x, p[r]);
+                p[r] = fmaf(__uint_as_float(normed_bits(xv.x & 0xffff0000u, rr, g[j].y)), w[j].y, p[r]);
+                p[r] = fmaf(__uint_as_float(normed_bits((xv.y & 0xffffu) << 16, rr, g[j].z)), w[j].z, p[r]);
+                p[r] = fmaf(__uint_as_float(normed_bits(xv.y & 0xffff0000u, rr, g[j].w)), w[j].w, p[r]);
+              }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < kRouterRows; ++r) {
+          if (r < nrows) {
+            const uint16_t* xr = xs + (size_t)r * H;
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              if (h0 + 256 * j < H) {
+                const uint2 xv = *reinterpret_cast<const uint2*>(xr + h0 + 256 * j);
+                p[r] = fmaf(bf16_to_f32(xv.x & 0xffffu), w[j].x, p[r]);
+                p[r] = fmaf(bf16_to_f32(xv.x >> 16), w[j].y, p[r]);
+                p[r] = fmaf(bf16_to_f32(xv.y & 0xffffu), w[j].z, p[r]);
+                p[r] = fmaf(bf16_to_f32(xv.y >> 16), w[j].w, p[r]);
+              }
+          }
         }
       }
     }
@@ -109,7 +141,9 @@ constexpr int kTileVals = kTileRows * kTileExperts;
 
 __global__ void __launch_bounds__(kThreads, 2) router_logits_tiled_kernel(
     const uint16_t* __restrict__ x, int T, int H, int E, const float* __restrict__ wr,
-    const float* __restrict__ bias, float* __restrict__ logits, int n_rblk, int n_eblk) {
+    const float* __restrict__ bias, float* __restrict__ logits, int n_rblk, int n_eblk,
+    const float* __restrict__ gamma, float eps) {
+  __shared__ float rn[kTileRows];  // pre-router RMSNorm factors of the tile's rows (with gamma)
   // workgroups are dealt to the 8 XCDs in turn; renumber so that each XCD
   // takes a contiguous run of tiles (the expert groups of one row block share
   // that XCD's L2)
@@ -119,6 +153,13 @@ __global__ void __launch_bounds__(kThreads, 2) router_logits_tiled_kernel(
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int t0 = (tile / n_eblk) * kTileRows;
   const int e0 = (tile % n_eblk) * (kTileExperts * kWaves) + wave * kTileExperts;
+  if (gamma) {
+    for (int r = wave; r < kTileRows; r += kWaves) {
+      const float v = row_rms_inv(x + (size_t)min(t0 + r, T - 1) * H, H, eps, lane);
+      if (lane == 0) rn[r] = v;
+    }
+    __syncthreads();
+  }
   if (e0 >= E) return;
   const uint16_t* xr[kTileRows];
 #pragma unroll
@@ -137,10 +178,19 @@ __global__ void __launch_bounds__(kThreads, 2) router_logits_tiled_kernel(
     for (int r = 0; r < kTileRows; ++r) xv[r] = *reinterpret_cast<const uint2*>(xr[r] + h);
 #pragma unroll
     for (int e = 0; e < kTileExperts; ++e) wv[e] = *reinterpret_cast<const float4*>(wp[e] + h);
+    float4 gv = make_float4(1.f, 1.f, 1.f, 1.f);
+    if (gamma) gv = *reinterpret_cast<const float4*>(gamma + h);
 #pragma unroll
     for (int r = 0; r < kTileRows; ++r) {
-      const float x0 = bf16_to_f32(xv[r].x & 0xffffu), x1 = bf16_to_f32(xv[r].x >> 16);
-      const float x2 = bf16_to_f32(xv[r].y & 0xffffu), x3 = bf16_to_f32(xv[r].y >> 16);
+      float x0 = bf16_to_f32(xv[r].x & 0xffffu), x1 = bf16_to_f32(xv[r].x >> 16);
+      float x2 = bf16_to_f32(xv[r].y & 0xffffu), x3 = bf16_to_f32(xv[r].y >> 16);
+      if (gamma) {
+        const float rr = rn[r];
+        x0 = (x0 * rr) * gv.x;
+        x1 = (x1 * rr) * gv.y;
+        x2 = (x2 * rr) * gv.z;
+        x3 = (x3 * rr) * gv.w;
+      }
 #pragma unroll
       for (int e = 0; e < kTileExperts; ++e) {
         float& a = acc[r * kTileExperts + e];
@@ -207,7 +257,7 @@ hipError_t launch_router_topk(const moe_layer_t& L, const uint16_t* x, int T, fl
     const int n_eblk = (E + kTileExperts * kWaves - 1) / (kTileExperts * kWaves);
     const unsigned grid = (unsigned)((n_rblk * n_eblk + 7) / 8 * 8);
     hipLaunchKernelGGL(router_logits_tiled_kernel, dim3(grid), dim3(kThreads), 0, stream, x, T, H, E,
-                       L.router_w, L.router_bias, logits, n_rblk, n_eblk);
+                       L.router_w, L.router_bias, logits, n_rblk, n_eblk, L.norm_weight, L.norm_eps);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)((T + 15) / 16)), dim3(kThreads), 0, stream, logits, T, E,
@@ -219,7 +269,8 @@ hipError_t launch_router_topk(const moe_layer_t& L, const uint16_t* x, int T, fl
   const size_t lds = align_up((size_t)rows * H * 2, 16) + (size_t)rows * E * 4;
   const unsigned grid = (unsigned)((T + rows - 1) / rows);
   hipLaunchKernelGGL(router_topk_kernel, dim3(grid), dim3(kThreads), lds, stream, x, T, H, E,
-                     L.top_k, rows, L.router_w, L.router_bias, logits, ids, w, ld, fold_e);
+                     L.top_k, rows, L.router_w, L.router_bias, logits, ids, w, ld, fold_e, L.norm_weight,
+                     L.norm_eps);
   return hipGetLastError();
 }
 

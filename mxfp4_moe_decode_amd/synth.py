@@ -57,7 +57,7 @@ WORKLOADS = {
                 zipf=None, residual=False),
 }
 _WID = {name: i + 1 for i, name in enumerate(WORKLOADS)}
-_TAG = {"router": 1, "w13": 2, "w2": 3, "ws13": 4, "ws2": 5, "bias": 6, "x": 7, "nvfp4": 8}
+_TAG = {"router": 1, "w13": 2, "w2": 3, "ws13": 4, "ws2": 5, "bias": 6, "x": 7, "nvfp4": 8, "norm": 9}
 WEIGHT_STD = 0.02
 
 
@@ -178,3 +178,9 @@ def nvfp4_matrix(cfg, layer, index, rows, cols, n_global=1):
     bscales = g.integers(0x40, 0x7F, size=(rows, cols // 16)).astype(np.uint8)
     gscale = (2e-5 * np.exp(g.uniform(-0.5, 0.5, size=n_global))).astype(np.float32)
     return codes, bscales, gscale
+
+
+def norm_weight(cfg, layer=0):
+    """fp32 [H] weight of the pre-router RMSNorm: 1 + 0.1 N(0, 1)."""
+    g = _rng(cfg, layer, "norm")
+    return (1.0 + 0.1 * g.standard_normal(cfg["H"])).astype(np.float32)

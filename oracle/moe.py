@@ -120,8 +120,13 @@ class Layer:
 
     def __init__(self, H, I, E, k, I_s, router_w, router_bias,
                  w13_codes, w13_scales, w2_codes, w2_scales,
-                 ws13_codes=None, ws13_scales=None, ws2_codes=None, ws2_scales=None, shared_folded=False):
+                 ws13_codes=None, ws13_scales=None, ws2_codes=None, ws2_scales=None, shared_folded=False,
+                 norm_weight=None, norm_eps=1e-6):
         self.H, self.I, self.E, self.k, self.I_s = H, I, E, k, I_s
+        # norm_weight [H] (or None): the layer's input is the residual stream
+        # h and the MoE runs on RMSNorm(h), see moe_layer
+        self.norm_weight = None if norm_weight is None else np.asarray(norm_weight, np.float64)
+        self.norm_eps = float(norm_eps)
         # shared_folded: expert E of the (E + 1)-expert table is the shared
         # expert in MXFP4, selected for every token with weight 1 (I_s is 0)
         self.shared_folded = shared_folded
@@ -212,13 +217,25 @@ def mx_ffn(x, w13_codes, w13_scales, w2_codes, w2_scales, fmt):
     aq = mx.mx_dequantize(ac, as_, fmt)
     w2 = mx.mx_dequantize(w2_codes, w2_scales, fmt)
     d = aq @ w2.T
-    return d, {"x_codes": xc, "x_scales": xs, "g": g, "u": u, "a": a, "a_codes": ac, "a_scales": as_,
+    return d, {"x": x, "x_codes": xc, "x_scales": xs, "g": g, "u": u, "a": a, "a_codes": ac, "a_scales": as_,
                "xq": xq, "w13": w13, "aq": aq, "w2": w2, "fmt": fmt}
 
 
 # ---------------------------------------------------------------------------
 # The layer
 # ---------------------------------------------------------------------------
+
+def rmsnorm(h, weight, eps):
+    """RMSNorm of rows h [T, H] (fp64): h / sqrt(mean(h^2) + eps) * weight,
+    the normalization in front of the router that mono decode fuses into the
+    MoE launch (article "MiniMax-M3.1 on AMD Instinct GPUs: Day-0 support and
+    optimization", section "Serving with vLLM / What we Optimized": "the
+    RMSNorm and router").  The result is not rounded to bf16: inside one fused
+    launch it goes straight to the router and the MX quantizers."""
+    h = np.asarray(h, np.float64)
+    ms = np.mean(h * h, axis=1, keepdims=True)
+    return h / np.sqrt(ms + eps) * np.asarray(weight, np.float64)[None, :]
+
 
 def moe_layer(x_bits, layer, residual_bits=None, ids=None, on_ffn=None):
     """One MoE layer on bf16 rows ``x_bits`` [T, H] (uint16 patterns).
@@ -234,6 +251,14 @@ def moe_layer(x_bits, layer, residual_bits=None, ids=None, on_ffn=None):
     x = mx.bf16_bits_to_f64(x_bits)
     T, H = x.shape
     k = layer.k
+    h_res = None
+    if layer.norm_weight is not None:
+        # the input is the residual stream h: the MoE runs on RMSNorm(h) and h
+        # itself is added back (the fused residual); no separate residual
+        if residual_bits is not None:
+            raise ValueError("a layer with a pre-router norm adds its own input as the residual")
+        h_res = x
+        x = rmsnorm(x, layer.norm_weight, layer.norm_eps)
     logits = router_logits(x, layer.router_w, layer.router_bias)
     if ids is None:
         ids, w = select_topk(logits, k)
@@ -271,6 +296,8 @@ def moe_layer(x_bits, layer, residual_bits=None, ids=None, on_ffn=None):
     y = np.einsum("tj,tjh->th", w, d) + s
     if residual_bits is not None:
         y = y + mx.bf16_bits_to_f64(residual_bits)
+    if h_res is not None:
+        y = y + h_res
     return {"y_bits": mx.round_to_bf16_bits(y), "y": y, "logits": logits,
             "ids": ids, "weights": w, "d": d, "s": s}
 

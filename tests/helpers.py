@@ -72,7 +72,10 @@ def prefetch(ol, experts, threads=16):
 def oracle_experts(x_bits, ol, ids=None):
     """Experts the oracle's routing (or the given ids) selects for x."""
     if ids is None:
-        logits = moe.router_logits(mx.bf16_bits_to_f64(x_bits), ol.router_w, ol.router_bias)
+        x = mx.bf16_bits_to_f64(x_bits)
+        if ol.norm_weight is not None:
+            x = moe.rmsnorm(x, ol.norm_weight, ol.norm_eps)
+        logits = moe.router_logits(x, ol.router_w, ol.router_bias)
         ids, _ = moe.select_topk(logits, ol.k)
     return np.unique(np.asarray(ids))
 
@@ -124,11 +127,23 @@ def gpu_layer(cfg, layer=0, device="cuda"):
         lambda e: synth.device_expert_w2(cfg, layer, e, device), device=device, **sh)
 
 
-def logit_bound(x_bits, w_r, logits_ref):
-    """Per-(row, expert) bound on |l_gpu - l| for the kernel's fp32 order."""
-    x = np.abs(mx.bf16_bits_to_f64(x_bits))
-    s = x @ np.abs(np.asarray(w_r, np.float64)).T
-    return gamma(56) * s + 2 * U32 * np.abs(logits_ref)
+def logit_bound(x_bits, w_r, logits_ref, x=None, x_rel=0.0):
+    """Per-(row, expert) bound on |l_gpu - l| for the kernel's fp32 order.
+    ``x`` (fp64, default the bf16 rows) is the router input; ``x_rel`` bounds
+    the relative error of the GPU's copy of it (the fp32 pre-router norm)."""
+    xa = np.abs(mx.bf16_bits_to_f64(x_bits) if x is None else np.asarray(x, np.float64))
+    s = xa @ np.abs(np.asarray(w_r, np.float64)).T
+    return (gamma(56) + x_rel) * s + 2 * U32 * np.abs(logits_ref)
+
+
+def norm_rel_error(H):
+    """Relative error bound of the GPU's normalized x = (h * r) * g against the
+    exact one: the fp32 sum of squares (positive terms, at most H/256 * 4 + 6
+    roundings each), the division by H, the epsilon add, the square root and
+    the reciprocal (one rounding each, the square root halving the sum's
+    relative error), then the two products."""
+    n = 4 * ((H + 255) // 256) + 6
+    return gamma(n) / 2 + 6 * U32
 
 
 def check_logits(l_gpu, l_ref, bound):
@@ -211,18 +226,25 @@ def requant_deviation(a, da, fmt):
     return dev.reshape(n, I)
 
 
-def ffn_deviation(info, fmt):
+def ffn_deviation(info, fmt, x_rel=0.0):
     """Bound on |d_gpu - d_oracle| [n, H] for one SwiGLU FFN of the oracle
-    (``info`` from oracle.moe.mx_ffn): fp32 rounding of the gate/up sums,
-    of SwiGLU (expf, division, product: 10 roundings) and the oracle's own
-    fp32 roundings of g, u, a, then the re-quantization steps that can
-    follow, then the down product's rounding."""
+    (``info`` from oracle.moe.mx_ffn): with ``x_rel`` > 0 (the GPU's x has
+    that relative error), the MX codes of x that can differ; fp32 rounding of
+    the gate/up sums, of SwiGLU (expf, division, product: 10 roundings) and
+    the oracle's own fp32 roundings of g, u, a, then the re-quantization steps
+    that can follow, then the down product's rounding."""
     xq, w13, g, u, a, aq, w2 = (info[k] for k in ("xq", "w13", "g", "u", "a", "aq", "w2"))
     I = g.shape[1]
     H = xq.shape[1]
-    s13 = np.abs(xq) @ np.abs(w13).T
-    dg = gamma(gemm_roundings(H)) * s13[:, :I] + 2 * U32 * np.abs(g)
-    du = gamma(gemm_roundings(H)) * s13[:, I:] + 2 * U32 * np.abs(u)
+    w13a = np.abs(w13)
+    dxq = np.zeros_like(xq)
+    if x_rel > 0:
+        x = np.asarray(info["x"], np.float64)
+        dxq = requant_deviation(x, x_rel * np.abs(x), fmt)
+    s13 = (np.abs(xq) + dxq) @ w13a.T
+    e13 = dxq @ w13a.T
+    dg = gamma(gemm_roundings(H)) * s13[:, :I] + e13[:, :I] + 2 * U32 * np.abs(g)
+    du = gamma(gemm_roundings(H)) * s13[:, I:] + e13[:, I:] + 2 * U32 * np.abs(u)
     sil = g / (1.0 + np.exp(-g))
     da = SILU_SLOPE * np.abs(u) * dg + np.abs(sil) * du + SILU_SLOPE * dg * du + 10 * U32 * np.abs(a)
     daq = requant_deviation(a, da, fmt)
@@ -236,17 +258,18 @@ class LayerBound:
 
     W_RTOL, W_ATOL = 1e-5, 1e-6  # the routing-weight tolerance the tests assert
 
-    def __init__(self, T, k, H):
+    def __init__(self, T, k, H, x_rel=0.0):
         self.dd = np.zeros((T, k, H))
         self.ds = np.zeros((T, H))
+        self.x_rel = x_rel
 
     def __call__(self, kind, e, rows, info):
         if kind == "routed":
-            dev = ffn_deviation(info, "fp4")
+            dev = ffn_deviation(info, "fp4", self.x_rel)
             for r, (t, j) in enumerate(rows):
                 self.dd[t, j] = dev[r]
         else:
-            self.ds[:] = ffn_deviation(info, info["fmt"])
+            self.ds[:] = ffn_deviation(info, info["fmt"], self.x_rel)
 
     def bound(self, ref, residual_bits=None):
         w, d, s = ref["weights"], ref["d"], ref["s"]
@@ -277,9 +300,11 @@ def check_elementwise(y_bits, ref, bound):
 def oracle_with_bound(x_bits, layer, residual_bits=None, ids=None):
     """Oracle layer output plus the element-wise bound of its comparison."""
     T = np.asarray(x_bits).shape[0]
-    lb = LayerBound(T, layer.k, layer.H)
+    normed = layer.norm_weight is not None
+    lb = LayerBound(T, layer.k, layer.H, norm_rel_error(layer.H) if normed else 0.0)
     ref = moe.moe_layer(x_bits, layer, residual_bits, ids=ids, on_ffn=lb)
-    return ref, lb.bound(ref, residual_bits)
+    # with the norm the layer adds its own input back
+    return ref, lb.bound(ref, x_bits if normed else residual_bits)
 
 
 def compare_with_oracle(cfg, gl, ol, x_bits, y, ids=None, w=None, residual_bits=None, layer=0,
@@ -305,9 +330,14 @@ def compare_with_oracle(cfg, gl, ol, x_bits, y, ids=None, w=None, residual_bits=
     else:
         assert np.array_equal(ids, ids_r), "the call's routing differs from the standalone router's"
         assert np.array_equal(w, w_r), "the call's routing weights differ from the standalone router's"
-    ref_logits = moe.router_logits(mx.bf16_bits_to_f64(x_bits), ol.router_w, ol.router_bias)
+    xr = mx.bf16_bits_to_f64(x_bits)
+    x_rel = 0.0
+    if ol.norm_weight is not None:
+        xr = moe.rmsnorm(xr, ol.norm_weight, ol.norm_eps)
+        x_rel = norm_rel_error(ol.H)
+    ref_logits = moe.router_logits(xr, ol.router_w, ol.router_bias)
     wr = synth.router_weights(cfg, layer) if router_w is None else router_w
-    bound_l = logit_bound(x_bits, wr, ref_logits)
+    bound_l = logit_bound(x_bits, wr, ref_logits, x=xr, x_rel=x_rel)
     check_logits(logits, ref_logits, bound_l)
     ref_ids, _ = moe.select_topk(ref_logits, ol.k)
     use_ids = None

@@ -1,0 +1,30 @@
+"""Build-time properties the kernels rely on, checked with the compiler's
+resource report (no GPU needed): the persistent fused decode grid must have
+every workgroup resident at once, so no instance of its kernel may use
+scratch memory (a dispatch waiting for scratch can hold workgroups back)."""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from mxfp4_moe_decode_amd import build
+
+pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
+                                reason="hipcc not available")
+
+
+def test_fused_decode_kernel_uses_no_scratch(tmp_path):
+    src = os.path.join(build.CSRC, "decode.hip")
+    cmd = [build.hipcc()] + build._flags() + ["-x", "hip", f"--offload-arch={build.ARCH}", "-Xclang",
+                                               "-target-feature", "-Xclang", "-packed-fp32-ops", "-c", src,
+                                               "-o", str(tmp_path / "d.o"), "-Rpass-analysis=kernel-resource-usage"]
+    out = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert out.returncode == 0, out.stderr[-2000:]
+    names = re.findall(r"Function Name: (\S*fused_decode_kernel\S*)", out.stderr)
+    scratch = [int(v) for v in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", out.stderr)]
+    assert len(names) >= 3, "expected the MiniMax, folded MiniMax and run-time shape instances"
+    assert len(scratch) == len(names)
+    assert all(v == 0 for v in scratch), dict(zip(names, scratch))

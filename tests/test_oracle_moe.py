@@ -287,3 +287,39 @@ def test_folded_layer_routes_over_the_original_experts_only():
     c2, s2 = mx.requant_fp8_to_fp4(layer.ws2_codes, layer.ws2_scales)
     s_ref, _ = moe.mx_ffn(mx.bf16_bits_to_f64(x), c13, s13, c2, s2, "fp4")
     assert np.array_equal(b["s"], s_ref)
+
+
+def test_rmsnorm_closed_forms():
+    # constant rows: mean square c^2, so x = c / sqrt(c^2 + eps) * weight
+    H = 64
+    wgt = np.linspace(0.5, 1.5, H)
+    h = np.stack([np.full(H, 3.0), np.full(H, -0.25)])
+    x = moe.rmsnorm(h, wgt, 1e-6)
+    np.testing.assert_allclose(x[0], 3.0 / math.sqrt(9.0 + 1e-6) * wgt, rtol=1e-15)
+    np.testing.assert_allclose(x[1], -0.25 / math.sqrt(0.0625 + 1e-6) * wgt, rtol=1e-15)
+    # eps = 0: invariant to scaling the row by a power of two (exact)
+    rng = np.random.default_rng(2)
+    r = rng.standard_normal((3, H))
+    assert np.array_equal(moe.rmsnorm(r * 8.0, wgt, 0.0), moe.rmsnorm(r, wgt, 0.0))
+    # every normalized row has mean square 1 (unit weight, eps = 0)
+    np.testing.assert_allclose(np.mean(moe.rmsnorm(r, np.ones(H), 0.0) ** 2, axis=1), 1.0, rtol=1e-14)
+
+
+def test_normed_layer_on_unit_rms_rows_is_the_plain_layer_with_residual():
+    # rows of +-1 have mean square 1: with unit weight and eps = 0 the norm
+    # is the identity, so the normed layer equals the plain layer with its
+    # input added back as the residual
+    layer, rng = _random_layer(I_s=64)
+    x = synth.f32_to_bf16_bits(rng.choice([-1.0, 1.0], size=(5, 256)).astype(np.float32))
+    plain = moe.moe_layer(x, layer, residual_bits=x)
+    layer.norm_weight, layer.norm_eps = np.ones(256), 0.0
+    normed = moe.moe_layer(x, layer)
+    assert np.array_equal(normed["y"], plain["y"]) and np.array_equal(normed["ids"], plain["ids"])
+    # a row scaled by 4 normalizes to the same x, so only the residual differs
+    x4 = synth.f32_to_bf16_bits((4.0 * mx.bf16_bits_to_f64(x)).astype(np.float32))
+    normed4 = moe.moe_layer(x4, layer)
+    assert np.array_equal(normed4["ids"], normed["ids"])
+    np.testing.assert_allclose(normed4["y"] - mx.bf16_bits_to_f64(x4), normed["y"] - mx.bf16_bits_to_f64(x),
+                               rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        moe.moe_layer(x, layer, residual_bits=x)
