@@ -84,9 +84,14 @@ def build_layers(binding, synth, name, count, fold=False):
     return cfg, layers
 
 
-def time_decode(binding, synth, name, rotate, steps, warmup, pool=64, isolated=True, fold=False, norm=False):
+def time_decode(binding, synth, name, rotate, steps, warmup, pool=64, isolated=True, fold=False, norm=False,
+                rows=None, grouped=False):
+    """Fused launches of the workload (``rows`` overrides its row count); with
+    ``grouped``, the grouped path on the same layers and inputs instead."""
     import torch
     cfg, layers = build_layers(binding, synth, name, rotate, fold)
+    if rows is not None:
+        cfg = dict(cfg, T=rows)
     if norm:  # the pre-router RMSNorm fused in: the input is the residual stream
         gamma = torch.from_numpy(synth.norm_weight(cfg)).cuda()
         layers = [L.with_norm(gamma) for L in layers]
@@ -101,13 +106,19 @@ def time_decode(binding, synth, name, rotate, steps, warmup, pool=64, isolated=T
     stream = torch.cuda.current_stream()
     sp = binding.ctypes.c_void_p(stream.cuda_stream)
 
+    gws = binding.grouped_workspace(layers[0], T) if grouped else None
+
     def launch(i, rec_ids=None, rec_w=None):
         L = layers[i % rotate]
-        st = lib.fused_moe_mxfp4_decode(L.c, binding._ptr(xs[i % pool]), T, None, binding._ptr(ys[i % 4]),
-                                        binding._ptr(ws), ws.numel(), binding._ptr(rec_ids),
-                                        binding._ptr(rec_w), sp)
+        if grouped:
+            st = lib.fused_moe_mxfp4_grouped(L.c, binding._ptr(xs[i % pool]), T, None, binding._ptr(ys[i % 4]),
+                                             binding._ptr(gws), gws.numel(), sp)
+        else:
+            st = lib.fused_moe_mxfp4_decode(L.c, binding._ptr(xs[i % pool]), T, None, binding._ptr(ys[i % 4]),
+                                            binding._ptr(ws), ws.numel(), binding._ptr(rec_ids),
+                                            binding._ptr(rec_w), sp)
         if st != 0:
-            raise binding.MoeError("fused_moe_mxfp4_decode", st)
+            raise binding.MoeError("layer call", st)
 
     # every rotated instance is touched once before timing (its first launch
     # pays first-touch costs the steady state does not), then `warmup` more
@@ -141,6 +152,12 @@ def time_decode(binding, synth, name, rotate, steps, warmup, pool=64, isolated=T
         iso = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)]) * 1e3
     if binding.moe_decode_status(ws) != 0:
         raise RuntimeError("a device-side wait timed out during the benchmark")
+    if grouped:  # the routing of the timed steps, for the byte count (outside the timed region)
+        for i in range(steps):
+            L, xi = layers[(warmup + i) % rotate], xs[(warmup + i) % pool]
+            if lib.moe_router_topk(L.c, binding._ptr(xi), T, None, binding._ptr(ids[i]), binding._ptr(w[i]), sp):
+                raise binding.MoeError("moe_router_topk", -4)
+        torch.cuda.synchronize()
     ids_np = ids.cpu().numpy()
     D = np.array([len(np.unique(ids_np[i])) for i in range(steps)])
     nbytes = np.array([layer_bytes(cfg["H"], cfg["I"], cfg["E"], cfg["I_s"], d, T, folded=fold) +
@@ -335,6 +352,7 @@ def main():
     ap.add_argument("--no-folded", action="store_true",
                     help="skip the layers with the shared expert folded into the table as an MXFP4 expert")
     ap.add_argument("--no-norm", action="store_true", help="skip the layers with the pre-router RMSNorm fused in")
+    ap.add_argument("--no-wide", action="store_true", help="skip the 64-row step (wide fused launch vs grouped)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-isolated", action="store_true",
                     help="skip the one-launch-at-a-time timing (profiler runs: only back-to-back launches)")
@@ -383,6 +401,13 @@ def main():
                                    isolated=False, norm=True)
             print(f"[bench] {label}, pre-router RMSNorm fused in: {rn[name]['us_launch']:.2f} us per launch, "
                   f"{rn[name]['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    rw = {}
+    if not args.no_wide:
+        for kind in ("fused", "grouped"):
+            rw[kind] = time_decode(binding, synth, "decode16", max(4, args.rotate // 2), max(20, args.steps // 4),
+                                   args.warmup, isolated=False, rows=64, grouped=kind == "grouped")
+            print(f"[bench] 64 rows, {kind}: {rw[kind]['us_launch']:.2f} us per step, {rw[kind]['gbs']:.0f} GB/s, "
+                  f"D={rw[kind]['distinct_experts_mean']:.1f}", file=sys.stderr, flush=True)
     rc = None
     if not args.no_chain:
         rc = time_chain(binding, synth)
@@ -455,6 +480,15 @@ def main():
                 "us_per_launch": round(r["us_launch"], 3), "gbs": round(r["gbs"], 1),
                 "frac": round(r["gbs"] / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": int(r["bytes_mean"])}
                for n, r in rn.items()}}
+    if rw:
+        out["rows64"] = {
+            "workload": "a 64-row step on the 16-row workload's layer (speculative decoding at 8-16 users): one "
+                        "wide fused launch, against the grouped path's launches (the timing of the latter "
+                        "includes a router call to record the routing)",
+            **{kind: {"us_per_step": round(r["us_launch"], 3), "gbs": round(r["gbs"], 1),
+                      "frac": round(r["gbs"] / HBM_PEAK_GBS, 4),
+                      "distinct_experts_mean": round(r["distinct_experts_mean"], 2),
+                      "algorithmic_bytes_per_step": int(r["bytes_mean"])} for kind, r in rw.items()}}
     if rc:
         out["chain8"] = {
             "workload": "8 distinct layers (hidden 3072, 128 experts top-4, I 1024, MXFP8 shared 1024), 4 rows, "

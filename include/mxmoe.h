@@ -239,13 +239,16 @@ moe_status moe_align_sort(const int32_t* topk_ids, int T, int k, int E, int bloc
                           int32_t* num_padded, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * Workspace for the fused calls.  path 0: fused_moe_mxfp4_decode (T <= 16),
- * path 1: fused_moe_mxfp4_grouped (any T).  Returns 0 for invalid arguments.
+ * Workspace for the fused calls.  path 0: fused_moe_mxfp4_decode (T <= 64; a
+ * workspace sized for T <= 16 serves only steps of up to 16 rows, one sized for
+ * 17 <= T <= 64 serves every step), path 1: fused_moe_mxfp4_grouped (any T).
+ * Returns 0 for invalid arguments.
  * A decode workspace must be zero-filled once (moe_workspace_init) before its
  * first use.  Each decode call tags the words it hands between workgroups
  * with a 32-bit call counter kept in the workspace; the call that would make
  * the counter wrap clears every tagged word itself, so a workspace serves any
- * number of calls without re-initialization.  After moe_decode_status reports
+ * number of calls without re-initialization (and steps of any size in its
+ * range).  After moe_decode_status reports
  * MOE_ERR_TIMEOUT the workspace must be zero-filled again: until then every
  * decode call on it writes NaN (bf16 0x7FC0) to y and computes nothing.
  */
@@ -253,11 +256,16 @@ size_t moe_workspace_bytes(const moe_layer_t* layer, int T, int path);
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * The whole layer for 1..16 rows in ONE kernel launch ("mono decode": one
+ * The whole layer for 1..64 rows in ONE kernel launch ("mono decode": one
  * fused kernel launch per MoE layer for a pure decode of at most 16 tokens,
  * article section "Serving with vLLM / What we Optimized"; the monokernel's
- * "rows (1..16)", vLLM PR #64273 section "Test Result").
- *   x         [T][H] bf16, T in 1..16 (MOE_ERR_UNSUPPORTED otherwise)
+ * "rows (1..16)", vLLM PR #64273 section "Test Result"; and the wider steps
+ * the article names as its next kernel item, section "What's next").  Steps
+ * of 17..64 rows run an instance that takes every unit's rows in 16-row
+ * groups on the same weight tiles, so a step still reads each selected
+ * expert's weights once.
+ *   x         [T][H] bf16, T in 1..64 (MOE_ERR_UNSUPPORTED otherwise, and for
+ *             17..64 rows on shapes whose wide instance does not fit the LDS)
  *   residual  [T][H] bf16 added before the single bf16 rounding, or NULL
  *   y         [T][H] bf16 output; may alias residual, must not alias x
  *   ws        moe_workspace_bytes(layer, T, 0) bytes, zero-filled before first use
@@ -269,7 +277,7 @@ moe_status moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
  * combine order are those of the oracle.  fused_moe_mxfp4_grouped uses the same
  * arithmetic, so both give identical bits for the same rows.
  * Output row t depends only on x[t] (and residual[t]): results are bit-identical
- * for any T and any row order.  Shapes whose gate/up K-chunk is longer than 6
+ * for any T (1..64, either instance) and any row order.  Shapes whose gate/up K-chunk is longer than 6
  * tiles ((H/128)/NC > 6), or whose staged x and intermediates exceed the
  * 160 KiB of LDS, give MOE_ERR_UNSUPPORTED (the grouped call handles them).  The launch is a persistent grid sized to the
  * device's co-resident capacity; its device-side waits are bounded, and a wait
@@ -280,7 +288,8 @@ moe_status fused_moe_mxfp4_decode(const moe_layer_t* layer, const uint16_t* x, i
                                   int32_t* topk_ids_out, float* topk_w_out, hipStream_t stream);
 
 /*
- * fused_moe_mxfp4_decode without a workspace argument, for callers that cannot
+ * fused_moe_mxfp4_decode (steps of 1..16 rows) without a workspace argument,
+ * for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  The workspace is the library's own: a
  * static device array of 8 MiB per GPU, held until the process ends, whose

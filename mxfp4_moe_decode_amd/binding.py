@@ -327,9 +327,10 @@ def moe_workspace_bytes(layer, T, path):
     return load().moe_workspace_bytes(layer.c, T, path)
 
 
-def decode_workspace(layer, device="cuda"):
-    """A zero-initialized workspace for fused_moe_mxfp4_decode (any T <= 16)."""
-    n = moe_workspace_bytes(layer, 16, 0)
+def decode_workspace(layer, device="cuda", max_rows=64):
+    """A zero-initialized workspace for fused_moe_mxfp4_decode, for steps of
+    up to ``max_rows`` rows (16: mono decode steps; 64: also the wide steps)."""
+    n = moe_workspace_bytes(layer, max_rows, 0)
     if n == 0:
         raise ValueError("invalid layer")
     ws = torch.empty(n, dtype=torch.uint8, device=device)
@@ -392,19 +393,26 @@ def fused_moe_mxfp4_grouped(layer, x, residual=None, out=None, workspace=None):
 # Steps of at most this many rows run as one fused launch; wider ones take the
 # grouped path (the article "MiniMax-M3.1 on AMD Instinct GPUs: Day-0 support
 # and optimization", section "Performance, mono decode on vs off": beyond 16
-# tokens the dispatcher leaves the step on the original path).
+# tokens the dispatcher leaves the step on the original path).  The library's
+# fused launch also takes wide steps of up to WIDE_MAX_ROWS rows (the same
+# article's next kernel item, section "What's next": wider mono steps).
 DECODE_MAX_ROWS = 16
+WIDE_MAX_ROWS = 64
 
 
 class MoEForward:
-    """One MoE layer call for any number of rows: the fused single-launch
-    decode for T <= 16 (falling back to the grouped path when the library
-    reports the shape as unsupported by it), the grouped path otherwise.  Keeps
+    """One MoE layer call for any number of rows: the fused single launch for
+    T <= ``fused_max_rows`` (16 by default, as the pages dispatch; up to 64
+    with the wide steps), falling back to the grouped path when the library
+    reports the shape as unsupported by it; the grouped path otherwise.  Keeps
     the decode workspace (zero-filled once) and a grouped workspace grown on
     demand."""
 
-    def __init__(self, layer, device="cuda"):
+    def __init__(self, layer, device="cuda", fused_max_rows=DECODE_MAX_ROWS):
+        if not 1 <= fused_max_rows <= WIDE_MAX_ROWS:
+            raise ValueError(f"fused_max_rows must be in 1..{WIDE_MAX_ROWS}")
         self.layer, self.device = layer, torch.device(device)
+        self.fused_max_rows = fused_max_rows
         self.decode_ws = None
         self.grouped_ws = None
         self.last_path = None
@@ -419,9 +427,11 @@ class MoEForward:
         return fused_moe_mxfp4_grouped(self.layer, x, residual, out, self.grouped_ws)
 
     def __call__(self, x, residual=None, out=None):
-        if x.shape[0] <= DECODE_MAX_ROWS:
+        if x.shape[0] <= self.fused_max_rows:
             if self.decode_ws is None:
-                self.decode_ws = decode_workspace(self.layer, self.device)
+                self.decode_ws = decode_workspace(self.layer, self.device,
+                                                  DECODE_MAX_ROWS if self.fused_max_rows <= DECODE_MAX_ROWS
+                                                  else WIDE_MAX_ROWS)
             try:
                 y = fused_moe_mxfp4_decode(self.layer, x, residual, out, self.decode_ws)
                 self.last_path = "decode"

@@ -133,7 +133,7 @@ moe_status moe_align_sort(const int32_t* topk_ids, int T, int k, int E, int bloc
 
 size_t moe_workspace_bytes(const moe_layer_t* layer, int T, int path) {
   if (check_layer(layer) != MOE_OK) return 0;
-  if (path == 0) return (T >= 1 && T <= kDecodeMaxT) ? decode_ws_bytes(*layer) : 0;
+  if (path == 0) return (T >= 1 && T <= kDecodeWideMaxT) ? decode_ws_bytes(*layer, T) : 0;
   if (path == 1) return T >= 1 ? grouped_ws_bytes(*layer, T) : 0;
   return 0;
 }
@@ -150,11 +150,11 @@ moe_status fused_moe_mxfp4_decode(const moe_layer_t* layer, const uint16_t* x, i
   if (st != MOE_OK) return st;
   if (!x || !y || !ws || T <= 0) return MOE_ERR_INVALID_ARGUMENT;
   if (layer->norm_weight && residual) return MOE_ERR_INVALID_ARGUMENT;  // the norm adds its own input
-  if (T > kDecodeMaxT || !decode_supported(*layer)) return MOE_ERR_UNSUPPORTED;
+  if (T > kDecodeWideMaxT || !decode_supported(*layer, T)) return MOE_ERR_UNSUPPORTED;
   if (static_cast<const void*>(y) == static_cast<const void*>(x)) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(y, 4) || !aligned(residual, 4) || !aligned(ws, 256))
     return MOE_ERR_INVALID_ARGUMENT;
-  if (ws_bytes < decode_ws_bytes(*layer)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (ws_bytes < decode_ws_bytes(*layer, T)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   return from_hip(launch_decode(*layer, x, T, residual, y, ws, topk_ids_out, topk_w_out, stream));
 }
 
@@ -165,10 +165,10 @@ moe_status fused_moe_mxfp4_decode_noalloc(const moe_layer_t* layer, const uint16
   if (st != MOE_OK) return st;
   if (!x || !y || T <= 0) return MOE_ERR_INVALID_ARGUMENT;
   if (layer->norm_weight && residual) return MOE_ERR_INVALID_ARGUMENT;  // the norm adds its own input
-  if (T > kDecodeMaxT || !decode_supported(*layer)) return MOE_ERR_UNSUPPORTED;
+  if (T > kDecodeMaxT || !decode_supported(*layer, T)) return MOE_ERR_UNSUPPORTED;
   if (static_cast<const void*>(y) == static_cast<const void*>(x)) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(y, 4) || !aligned(residual, 4)) return MOE_ERR_INVALID_ARGUMENT;
-  if (decode_ws_bytes(*layer) > kNoAllocScratchBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (decode_ws_bytes(*layer, T) > kNoAllocScratchBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
   void* ws = noalloc_scratch(stream);
   if (!ws) return MOE_ERR_HIP;
   return from_hip(launch_decode(*layer, x, T, residual, y, ws, topk_ids_out, topk_w_out, stream));
@@ -218,7 +218,7 @@ moe_status moe_decode_status(const void* ws, size_t ws_bytes) {
 int moe_decode_trace(const moe_layer_t* layer, const void* ws, size_t ws_bytes, uint64_t* host,
                      size_t n_words) {
   if (check_layer(layer) != MOE_OK || !ws || !host) return MOE_ERR_INVALID_ARGUMENT;
-  if (ws_bytes < decode_ws_bytes(*layer)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (ws_bytes < decode_ws_bytes(*layer, 1)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   uint32_t grid = 0;
   if (hipMemcpy(&grid, static_cast<const char*>(ws) + kDecodeGridOffset, 4, hipMemcpyDeviceToHost) !=
       hipSuccess)

@@ -53,7 +53,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxK = 8;
-constexpr int kMaxSlots = kDecodeMaxT * kMaxK;
+constexpr int kGroup = 16;     // rows of one matrix-instruction row block
 constexpr int kMaxCT = 6;      // tiles of a gate/up K-chunk held in registers
 constexpr int kBufQuads = 12;  // 16-byte weight loads one prefetch buffer holds per lane
 constexpr int kBufWords = 6;   // scale words one prefetch buffer holds per lane
@@ -84,7 +84,8 @@ struct DecodeArgs {
   int fold;           // the shared expert is expert E of the table (1) or MXFP8 (0)
   const float* norm_w;  // pre-router RMSNorm weight [H], or null
   float norm_eps;
-  int gamma_off;        // dynamic-LDS byte offset of the norm weight's copy
+  int gamma_off;        // dynamic-LDS byte offsets: the norm weight's copy,
+  int off_xq4, off_stage, off_x8;  // the MXFP4 x, the staged intermediate, the MXFP8 x
   int KT1, CT1, NC1;  // K = H: tiles of 128, tiles per chunk, chunks
   int KT2, CT2;       // K = I
   int KTs, CTs;       // K = I_s
@@ -113,9 +114,11 @@ struct DecodeArgs {
 // the k routed choices and, with the shared expert folded into the table, one
 // more slot (expert E, weight 1).
 constexpr int n_chunks_of(int tiles) { return tiles % 4 == 0 ? 4 : (tiles % 2 == 0 ? 2 : 1); }
-template <int H_, int I_, int IS_, int E_, int K_, int FOLD_>
+template <int H_, int I_, int IS_, int E_, int K_, int FOLD_, int MT_>
 struct DArgs : DecodeArgs {
   static constexpr bool kFixedShape = H_ != 0;  // a compiled instance for one layer shape
+  static constexpr int kMaxT = MT_;              // rows the instance takes (16, or 64 for wide steps)
+  static constexpr bool kWide = MT_ > kGroup;
   __device__ __forceinline__ int h() const { return H_ ? H_ : H; }
   __device__ __forceinline__ int i() const { return I_ ? I_ : I; }
   __device__ __forceinline__ int is() const { return IS_ ? (IS_ < 0 ? 0 : IS_) : Is; }
@@ -138,23 +141,32 @@ __device__ __forceinline__ void trace_at(const DA& A, int i) {
   if (threadIdx.x == 0) A.trace[(size_t)blockIdx.x * kTraceWords + i] = wall_clock64();
 }
 
-struct Smem {
-  int32_t ids[kMaxSlots];
-  float w[kMaxSlots];
+// Per-workgroup state for an instance taking up to MT rows.  The slots routed
+// to selected expert dd are slist[eoff[dd] .. eoff[dd] + ecount[dd]).
+template <int MT>
+struct SmemT {
+  static constexpr int kSlots = MT * kMaxK;
+  int32_t ids[kSlots];
+  float w[kSlots];
   int hist[256];
   int epos[256];
-  int fill[kMaxSlots];
-  uint8_t elist[kMaxSlots];
-  uint8_t ecount[kMaxSlots];
-  uint8_t tl[kMaxSlots][kDecodeMaxT];           // slots routed to each selected expert
-  float red[kWaves][2][kDecodeMaxT][16];        // chunk sums [chunk][gate/up][row][column]
+  int fill[kSlots];
+  uint8_t elist[kSlots];
+  uint8_t ecount[kSlots];
+  uint16_t eoff[kSlots];
+  uint16_t slist[kSlots];
+  float red[kWaves][2][kGroup][16];             // chunk sums [chunk][gate/up][row][column]
   int wave_cnt[kWaves];
-  uint8_t qrows[kDecodeMaxT];                   // rows of x quantized for this workgroup's gate/up units
-  float rnorm[kDecodeMaxT];                      // pre-router RMSNorm factor of each row
+  int wave_sum[kWaves];
+  uint8_t qrows[MT];                            // rows of x quantized for this workgroup's gate/up units
+  float rnorm[MT];                              // pre-router RMSNorm factor of each row
   int D;
   int flag;
   int last;                                     // this workgroup is the call's last to finish
+  __device__ __forceinline__ int slot(int dd, int i) const { return slist[eoff[dd] + i]; }
 };
+template <class DA>
+using SmemOf = SmemT<DA::kMaxT>;
 
 // ------------------------------------------------------------------ synchronisation
 // Data handed from one workgroup to another (logits, gate/up results,
@@ -264,14 +276,14 @@ constexpr int kQGroups = kThreads / 8;
 // 32 t, MXFP4 code bytes 16 t, scale t.
 template <bool kRows, class DA>
 __device__ __forceinline__ void x_batch_load(const DA& A, int t0, int tasks, const uint8_t* rows,
-                                             uint32_t (&bits)[kQBatch][4]) {
+                                             uint32_t (&bits)[kQBatch][4], int blk0 = 0) {
   const int H = A.h(), nb = H / 32, j = threadIdx.x & 7, grp = threadIdx.x / 8;
 #pragma unroll
   for (int p = 0; p < kQBatch; ++p) {
     const int task = t0 + p * kQGroups + grp;
     bits[p][0] = bits[p][1] = bits[p][2] = bits[p][3] = 0u;
     if (task < tasks) {
-      const size_t off = kRows ? (size_t)rows[task / nb] * H + 32 * (task % nb) : 32 * (size_t)task;
+      const size_t off = kRows ? (size_t)rows[task / nb] * H + 32 * (task % nb) : 32 * ((size_t)blk0 + task);
       const uint2 v = *reinterpret_cast<const uint2*>(A.x + off + 4 * j);
       bits[p][0] = v.x << 16;
       bits[p][1] = v.x & 0xffff0000u;
@@ -285,9 +297,10 @@ __device__ __forceinline__ void x_batch_load(const DA& A, int t0, int tasks, con
 // norm weight copied into LDS and, unless a router unit of this workgroup has
 // left them in sm.rnorm, every row's norm factor.
 template <class DA>
-__device__ __forceinline__ void norm_setup(const DA& A, Smem& sm, float* gamma_lds, bool need_r, int lane, int wave) {
-  for (int i = threadIdx.x; i < A.h() / 4; i += kThreads)
-    reinterpret_cast<float4*>(gamma_lds)[i] = reinterpret_cast<const float4*>(A.norm_w)[i];
+__device__ __forceinline__ void norm_setup(const DA& A, SmemOf<DA>& sm, float* gamma_lds, bool need_r, int lane, int wave) {
+  if (!DA::kWide)
+    for (int i = threadIdx.x; i < A.h() / 4; i += kThreads)
+      reinterpret_cast<float4*>(gamma_lds)[i] = reinterpret_cast<const float4*>(A.norm_w)[i];
   if (need_r)
     for (int t = wave; t < A.T; t += kWaves) {
       const float v = row_rms_inv(A.x + (size_t)t * A.h(), A.h(), A.norm_eps, lane);
@@ -298,16 +311,17 @@ __device__ __forceinline__ void norm_setup(const DA& A, Smem& sm, float* gamma_l
 
 // With the pre-router norm: the loaded batch becomes (h * r) * g.
 template <bool kRows, class DA>
-__device__ __forceinline__ void x_batch_norm(const DA& A, const Smem& sm, const float* gamma_lds, int t0, int tasks,
-                                             const uint8_t* rows, uint32_t (&bits)[kQBatch][4]) {
+__device__ __forceinline__ void x_batch_norm(const DA& A, const SmemOf<DA>& sm, const float* gamma_lds, int t0, int tasks,
+                                             const uint8_t* rows, uint32_t (&bits)[kQBatch][4], int blk0 = 0) {
   const int H = A.h(), nb = H / 32, j = threadIdx.x & 7, grp = threadIdx.x / 8;
 #pragma unroll
   for (int p = 0; p < kQBatch; ++p) {
     const int task = t0 + p * kQGroups + grp;
     if (task < tasks) {
-      const int row = kRows ? rows[task / nb] : task / nb;
+      const int row = kRows ? rows[task / nb] : (blk0 + task) / nb;
       const float r = sm.rnorm[row];
-      const float4 g = *reinterpret_cast<const float4*>(gamma_lds + 32 * (task % nb) + 4 * j);
+      const float* gp = DA::kWide ? A.norm_w : gamma_lds;  // the wide instance keeps no LDS copy
+      const float4 g = *reinterpret_cast<const float4*>(gp + 32 * (task % nb) + 4 * j);
       bits[p][0] = normed_bits(bits[p][0], r, g.x);
       bits[p][1] = normed_bits(bits[p][1], r, g.y);
       bits[p][2] = normed_bits(bits[p][2], r, g.z);
@@ -346,14 +360,13 @@ __device__ __forceinline__ void x_batch_quant(const DA& A, int t0, int tasks, co
 // per-row arithmetic as router_lane_partial: each batch of up to 16 strides
 // of the expert's weights is loaded once, then the rows go through it two at
 // a time.
+// Rows wave + 4 (rc + r), r < nr (at most 4) of one router unit.
 template <class DA>
-__device__ __forceinline__ void unit_router(const DA& A, Smem& sm, uint32_t tag, int e, int lane, int wave) {
+__device__ __forceinline__ void router_rows(const DA& A, SmemOf<DA>& sm, uint32_t tag, int e, int rc, int nr,
+                                            int lane, int wave) {
   const float* wrow = A.router_w + (size_t)e * A.h();
   const int H = A.h();
   float p[4] = {0.f, 0.f, 0.f, 0.f};
-  int nr = 0;
-  for (int t = wave; t < A.T; t += kWaves) ++nr;
-  if (nr == 0) return;
   if (A.norm_w) {
     // The normalized rows (h * r) * g.  With H <= 4096 the unit loads the
     // expert's weights and g once, then takes the rows two at a time: each
@@ -377,7 +390,7 @@ __device__ __forceinline__ void unit_router(const DA& A, Smem& sm, uint32_t tag,
 #pragma unroll
           for (int r = 0; r < 2; ++r)
             if (r0 + r < nr) {
-              const uint16_t* xr = A.x + (size_t)(wave + kWaves * (r0 + r)) * H;
+              const uint16_t* xr = A.x + (size_t)(wave + kWaves * (rc + r0 + r)) * H;
 #pragma unroll
               for (int j = 0; j < 16; ++j)
                 if (4 * lane + 256 * j < H) xv[r][j] = *reinterpret_cast<const uint2*>(xr + 4 * lane + 256 * j);
@@ -397,7 +410,7 @@ __device__ __forceinline__ void unit_router(const DA& A, Smem& sm, uint32_t tag,
                   sq = fmaf(d, d, sq);
                 }
               const float rr = 1.0f / sqrtf(wave_sum_butterfly(sq) / (float)H + A.norm_eps);
-              if (lane == 0) sm.rnorm[wave + kWaves * (r0 + r)] = rr;
+              if (lane == 0) sm.rnorm[wave + kWaves * (rc + r0 + r)] = rr;
               float& acc = p[r0 + r];
 #pragma unroll
               for (int j = 0; j < 16; ++j)
@@ -412,7 +425,7 @@ __device__ __forceinline__ void unit_router(const DA& A, Smem& sm, uint32_t tag,
       }
     } else {
       for (int r = 0; r < nr; ++r) {
-        const int row = wave + kWaves * r;
+        const int row = wave + kWaves * (rc + r);
         const float rr = row_rms_inv(A.x + (size_t)row * H, H, A.norm_eps, lane);
         if (lane == 0) sm.rnorm[row] = rr;
         const uint16_t* xr = A.x + (size_t)row * H;
@@ -433,7 +446,7 @@ __device__ __forceinline__ void unit_router(const DA& A, Smem& sm, uint32_t tag,
       if (r < nr) {
         float v = wave_sum_butterfly(p[r]);
         if (A.router_bias) v = v + b;
-        if (lane == 0) st_dev(&A.logits[(wave + kWaves * r) * A.e() + e], tagged(tag, v));
+        if (lane == 0) st_dev(&A.logits[(wave + kWaves * (rc + r)) * A.e() + e], tagged(tag, v));
       }
     return;
   }
@@ -449,7 +462,7 @@ __device__ __forceinline__ void unit_router(const DA& A, Smem& sm, uint32_t tag,
 #pragma unroll
         for (int r = 0; r < 2; ++r)
           if (r0 + r < nr) {
-            const uint16_t* xr = A.x + (size_t)(wave + kWaves * (r0 + r)) * H;
+            const uint16_t* xr = A.x + (size_t)(wave + kWaves * (rc + r0 + r)) * H;
 #pragma unroll
             for (int j = 0; j < 16; ++j)
               if (h0 + 256 * j < H) xv[r][j] = *reinterpret_cast<const uint2*>(xr + h0 + 256 * j);
@@ -476,30 +489,38 @@ __device__ __forceinline__ void unit_router(const DA& A, Smem& sm, uint32_t tag,
     if (r < nr) {
       float v = wave_sum_butterfly(p[r]);
       if (A.router_bias) v = v + b;
-      if (lane == 0) st_dev(&A.logits[(wave + kWaves * r) * A.e() + e], tagged(tag, v));
+      if (lane == 0) st_dev(&A.logits[(wave + kWaves * (rc + r)) * A.e() + e], tagged(tag, v));
     }
+}
+
+template <class DA>
+__device__ __forceinline__ void unit_router(const DA& A, SmemOf<DA>& sm, uint32_t tag, int e, int lane, int wave) {
+  int nr = 0;
+  for (int t = wave; t < A.T; t += kWaves) ++nr;
+  // four rows per pass (one pass unless the wide instance has more rows)
+  for (int rc = 0; rc < (DA::kWide ? nr : 1); rc += 4)
+    if (rc < nr) router_rows(A, sm, tag, e, rc, min(nr - rc, 4), lane, wave);
 }
 
 // Shared gate/up strip st (0 <= st < 2 I_s/16: gate strips, then up strips):
 // wave w computes K-chunk w (MXFP8 x MXFP8); the chunk sums meet in LDS and
 // are added in chunk order.  The workgroup first quantizes x itself to MXFP8
-// (x8: codes [T][H], scales at kDecodeMaxT * H) and, with at most
+// (x8: codes [16][H], scales at 16 H; 16-row groups in turn) and, with at most
 // kEarlyQuantT rows, to MXFP4 (the copy the routed gate/up units read later);
 // the first batch of x is requested before the weights, so that quantizing
 // does not wait for them.  The fp32 result
 // goes to a_s[row][16 st + col] as tagged words (gate columns, then up
 // columns); SwiGLU is applied where it is staged.
 template <class DA>
-__device__ __forceinline__ void unit_shared_strip(const DA& A, uint32_t tag, Smem& sm, const float* gamma_lds, int st,
+__device__ __forceinline__ void unit_shared_strip(const DA& A, uint32_t tag, SmemOf<DA>& sm, const float* gamma_lds, int st,
                                                   uint8_t* x8, uint8_t* xq4, uint8_t* xs4, int lane, int wave) {
-  const int CT = A.ct1(), KG = (A.kt1() + 3) / 4;
+  const int CT = A.ct1(), KG = (A.kt1() + 3) / 4, nb = A.h() / 32;
   const int m = lane & 15, q = lane >> 4;
   const bool act = wave < A.nc1();
   const int t0 = wave * CT;
-  uint8_t* xs8 = x8 + (size_t)kDecodeMaxT * A.h();
-  const int tasks = A.T * (A.h() / 32);
+  uint8_t* xs8 = x8 + (size_t)kGroup * A.h();
   uint32_t bits[kQBatch][4];
-  x_batch_load<false>(A, 0, tasks, nullptr, bits);
+  x_batch_load<false>(A, 0, min(A.T, kGroup) * nb, nullptr, bits);
   v4i B[kMaxCT][2];
   uint32_t sw[3];
   if (act) {
@@ -514,41 +535,45 @@ __device__ __forceinline__ void unit_shared_strip(const DA& A, uint32_t tag, Sme
 #pragma unroll
     for (int g = 0; g < 3; ++g) sw[g] = load_stream4(sp + (size_t)min(t0 / 4 + g, KG - 1) * 256);
   }
-  for (int b0 = 0; b0 < tasks; b0 += kQBatch * kQGroups) {
-    if (b0 > 0) x_batch_load<false>(A, b0, tasks, nullptr, bits);
-    if (A.norm_w) x_batch_norm<false>(A, sm, gamma_lds, b0, tasks, nullptr, bits);
-    x_batch_quant<FP8, false>(A, b0, tasks, nullptr, bits, x8, xs8);
-    if (A.T <= kEarlyQuantT) x_batch_quant<FP4, false>(A, b0, tasks, nullptr, bits, xq4, xs4);
-  }
-  trace_at(A, TR_XQ);
-  __syncthreads();
-  if (act) {
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
+  // 16-row groups of x (the wide instance), each on the weight tiles in registers
+  for (int g0 = 0; g0 < (DA::kWide ? A.T : 1); g0 += kGroup) {
+    const int ng = min(A.T - g0, kGroup), tasks = ng * nb;
+    for (int b0 = 0; b0 < tasks; b0 += kQBatch * kQGroups) {
+      if (b0 > 0 || g0 > 0) x_batch_load<false>(A, b0, tasks, nullptr, bits, g0 * nb);
+      if (A.norm_w) x_batch_norm<false>(A, sm, gamma_lds, b0, tasks, nullptr, bits, g0 * nb);
+      x_batch_quant<FP8, false>(A, b0, tasks, nullptr, bits, x8, xs8);
+      if (A.T <= kEarlyQuantT) x_batch_quant<FP4, false>(A, b0, tasks, nullptr, bits, xq4, xs4);
+    }
+    trace_at(A, TR_XQ);
+    __syncthreads();
+    if (act) {
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < kMaxCT; ++j)
-      if (j < CT) {
-        const int kt = t0 + j;
-        // rows past T repeat row T - 1: their sums are never read
-        const int mr = m < A.T ? m : A.T - 1;
-        const uint8_t* ap = x8 + (size_t)mr * A.h() + kt * 128 + 16 * q;
-        const v4i a0 = *reinterpret_cast<const v4i*>(ap);
-        const v4i a1 = *reinterpret_cast<const v4i*>(ap + 64);
-        const uint32_t sa = xs8[mr * (A.h() / 32) + 4 * kt + q];
-        const uint32_t word = pick3(sw[0], sw[1], sw[2], kt / 4 - t0 / 4);
-        acc = mfma_fp8(a0, a1, B[j][0], B[j][1], acc, sa, scale_byte(word, kt));
-      }
+      for (int j = 0; j < kMaxCT; ++j)
+        if (j < CT) {
+          const int kt = t0 + j;
+          // rows past the group repeat its last row: their sums are never read
+          const int mr = m < ng ? m : ng - 1;
+          const uint8_t* ap = x8 + (size_t)mr * A.h() + kt * 128 + 16 * q;
+          const v4i a0 = *reinterpret_cast<const v4i*>(ap);
+          const v4i a1 = *reinterpret_cast<const v4i*>(ap + 64);
+          const uint32_t sa = xs8[mr * (A.h() / 32) + 4 * kt + q];
+          const uint32_t word = pick3(sw[0], sw[1], sw[2], kt / 4 - t0 / 4);
+          acc = mfma_fp8(a0, a1, B[j][0], B[j][1], acc, sa, scale_byte(word, kt));
+        }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.red[wave][0][4 * q + r][m] = acc[r];
+      for (int r = 0; r < 4; ++r) sm.red[wave][0][4 * q + r][m] = acc[r];
+    }
+    trace_at(A, TR_S_MMA);
+    __syncthreads();
+    const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
+    if (r < ng) {
+      float v = sm.red[0][0][r][c];
+      for (int ch = 1; ch < A.nc1(); ++ch) v = v + sm.red[ch][0][r][c];
+      st_dev(&A.a_s[(size_t)(g0 + r) * (2 * A.is()) + 16 * st + c], tagged(tag, v));
+    }
+    __syncthreads();  // sm.red and x8 are reused
   }
-  trace_at(A, TR_S_MMA);
-  __syncthreads();
-  const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
-  if (r < A.T) {
-    float v = sm.red[0][0][r][c];
-    for (int ch = 1; ch < A.nc1(); ++ch) v = v + sm.red[ch][0][r][c];
-    st_dev(&A.a_s[(size_t)r * (2 * A.is()) + 16 * st + c], tagged(tag, v));
-  }
-  __syncthreads();  // sm.red and x8 are reused
 }
 
 // Gate/up unit i of the folded shared expert (expert E of the table, every
@@ -557,12 +582,13 @@ __device__ __forceinline__ void unit_shared_strip(const DA& A, uint32_t tag, Sme
 // ahead of the weight tiles), then the unit computes like a routed one and
 // stores the SwiGLU values of slots t*kk + k as tagged words.
 template <class DA>
-__device__ __forceinline__ void unit_fold_gu(const DA& A, uint32_t tag, Smem& sm, const float* gamma_lds, int i,
+__device__ __forceinline__ void unit_fold_gu(const DA& A, uint32_t tag, SmemOf<DA>& sm, const float* gamma_lds, int i,
                                              uint8_t* xq4, uint8_t* xs4, bool& have_x4, int lane, int wave);
 
 // Chunk sums of a routed gate/up unit in sm.red, added in chunk order, then
 // SwiGLU: thread (row, column) for row < n; returns false for idle threads.
-__device__ __forceinline__ bool gu_finish(const Smem& sm, int nc, int n, int* row, int* col, float* a) {
+template <class SM>
+__device__ __forceinline__ bool gu_finish(const SM& sm, int nc, int n, int* row, int* col, float* a) {
   const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
   if (r >= n) return false;
   float g = sm.red[0][0][r][c], u = sm.red[0][1][r][c];
@@ -581,31 +607,44 @@ __device__ __forceinline__ bool gu_finish(const Smem& sm, int nc, int n, int* ro
 // list) and the slots routed to each.  The order of slots inside a list is
 // not fixed; nothing depends on it, since every result is addressed by slot.
 template <class DA>
-__device__ __forceinline__ void build_expert_list(const DA& A, Smem& sm, int lane, int wave) {
+__device__ __forceinline__ void build_expert_list(const DA& A, SmemOf<DA>& sm, int lane, int wave) {
+  constexpr int kSlots = SmemOf<DA>::kSlots;
   const int S = A.T * A.kk(), tid = threadIdx.x;
   sm.hist[tid] = 0;
-  if (tid < kMaxSlots) sm.fill[tid] = 0;
+  for (int i = tid; i < kSlots; i += kThreads) sm.fill[i] = 0;
   __syncthreads();
-  if (tid < S) atomicAdd(&sm.hist[sm.ids[tid]], 1);
+  for (int sl = tid; sl < S; sl += kThreads) atomicAdd(&sm.hist[sm.ids[sl]], 1);
   __syncthreads();
   const int cnt = sm.hist[tid];
   const bool used = cnt > 0;
   const uint64_t mask = __ballot(used);
+  // inclusive scan of the counts over the wavefront (expert order)
+  int incl = cnt;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
+  }
   if (lane == 0) sm.wave_cnt[wave] = __popcll(mask);
+  if (lane == kWave - 1) sm.wave_sum[wave] = incl;
   __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += sm.wave_cnt[w];
+  int base = 0, sbase = 0;
+  for (int w = 0; w < wave; ++w) {
+    base += sm.wave_cnt[w];
+    sbase += sm.wave_sum[w];
+  }
   if (used) {
     const int dd = base + __popcll(mask & ((1ull << lane) - 1ull));
     sm.elist[dd] = (uint8_t)tid;
     sm.ecount[dd] = (uint8_t)cnt;
+    sm.eoff[dd] = (uint16_t)(sbase + incl - cnt);
     sm.epos[tid] = dd;
   }
   if (tid == 0) sm.D = sm.wave_cnt[0] + sm.wave_cnt[1] + sm.wave_cnt[2] + sm.wave_cnt[3];
   __syncthreads();
-  if (tid < S) {
-    const int dd = sm.epos[sm.ids[tid]];
-    sm.tl[dd][atomicAdd(&sm.fill[dd], 1)] = (uint8_t)tid;
+  for (int sl = tid; sl < S; sl += kThreads) {
+    const int dd = sm.epos[sm.ids[sl]];
+    sm.slist[sm.eoff[dd] + atomicAdd(&sm.fill[dd], 1)] = (uint16_t)sl;
   }
   __syncthreads();
 }
@@ -686,7 +725,7 @@ __device__ __forceinline__ int down_expert(const Seq& S, int ur) {
 // path: stores to different members on different paths get merged into one
 // store through a pointer, which keeps buf in scratch memory.
 template <class DA>
-__device__ __forceinline__ void issue(const DA& A, const Smem& sm, const Seq& S, int j, int lane, int wave,
+__device__ __forceinline__ void issue(const DA& A, const SmemOf<DA>& sm, const Seq& S, int j, int lane, int wave,
                                       Buf& buf) {
   if (j >= S.nb + S.nc) return;
   uint32_t n0 = 0, n1 = 0, n2 = 0, n3 = 0, n4 = 0, n5 = 0;
@@ -729,21 +768,23 @@ __device__ __forceinline__ void issue(const DA& A, const Smem& sm, const Seq& S,
 
 // Routed gate/up: MFMA chain of this wave's K-chunk for both strips into
 // sm.red (A operand: the MXFP4 x rows of the routed slots, from LDS).
-// Row m of the unit's A operand is x row tok (from the unit's slot list, or
-// the row itself for the folded shared expert's units, which take every row).
+// Row m of the unit's A operand for its row group starting at g0 is x row
+// tok (from the unit's slot list, or the row itself for the folded shared
+// expert's units, which take every row).
 template <class DA>
-__device__ __forceinline__ void gu_compute(const DA& A, Smem& sm, const uint8_t* xq4_lds,
-                                           const uint8_t* xs4_lds, int dd, const Buf& buf, int lane, int wave) {
+__device__ __forceinline__ void gu_compute(const DA& A, SmemOf<DA>& sm, const uint8_t* xq4_lds,
+                                           const uint8_t* xs4_lds, int dd, int g0, const Buf& buf, int lane,
+                                           int wave) {
   if (wave >= A.nc1()) return;
   const int m = lane & 15;
   int tok;
   if (dd >= 0) {
-    const int n = sm.ecount[dd];
-    // rows past the expert's slot count repeat its last token: their
+    const int n = min(sm.ecount[dd] - g0, kGroup);
+    // rows past the group's slot count repeat its last token: their
     // products land in result rows that are never read
-    tok = sm.tl[dd][m < n ? m : n - 1] / A.kk();
+    tok = sm.slot(dd, g0 + (m < n ? m : n - 1)) / A.kk();
   } else {
-    tok = m < A.T ? m : A.T - 1;
+    tok = min(g0 + m, A.T - 1);
   }
   const int q = lane >> 4;
   const int CT = A.ct1(), t0 = wave * CT;
@@ -773,7 +814,7 @@ __device__ __forceinline__ void gu_compute(const DA& A, Smem& sm, const uint8_t*
 }
 
 template <class DA>
-__device__ __forceinline__ void unit_fold_gu(const DA& A, uint32_t tag, Smem& sm, const float* gamma_lds, int i,
+__device__ __forceinline__ void unit_fold_gu(const DA& A, uint32_t tag, SmemOf<DA>& sm, const float* gamma_lds, int i,
                                              uint8_t* xq4, uint8_t* xs4, bool& have_x4, int lane, int wave) {
   const int tasks = A.T * (A.h() / 32);
   uint32_t bits[kQBatch][4];
@@ -798,14 +839,16 @@ __device__ __forceinline__ void unit_fold_gu(const DA& A, uint32_t tag, Smem& sm
     trace_at(A, TR_XQ);
   }
   __syncthreads();  // the x rows are in LDS
-  gu_compute(A, sm, xq4, xs4, -1, buf, lane, wave);
-  trace_at(A, TR_S_MMA);
-  __syncthreads();
-  int row, col;
-  float a;
-  if (gu_finish(sm, A.nc1(), A.T, &row, &col, &a))
-    st_dev(&A.a_r[(size_t)(row * A.kk() + A.kr()) * A.i() + 16 * i + col], tagged(tag, a));
-  __syncthreads();  // sm.red is rewritten by the next unit
+  for (int g0 = 0; g0 < A.T; g0 += kGroup) {  // 16-row groups, the weight tiles kept in registers
+    gu_compute(A, sm, xq4, xs4, -1, g0, buf, lane, wave);
+    trace_at(A, TR_S_MMA);
+    __syncthreads();
+    int row, col;
+    float a;
+    if (gu_finish(sm, A.nc1(), min(A.T - g0, kGroup), &row, &col, &a))
+      st_dev(&A.a_r[(size_t)((g0 + row) * A.kk() + A.kr()) * A.i() + 16 * i + col], tagged(tag, a));
+    __syncthreads();  // sm.red is rewritten by the next group or unit
+  }
 }
 
 // Staging of a down unit's intermediate rows into LDS as MX blocks: codes
@@ -841,7 +884,7 @@ __device__ __forceinline__ void stage_quantize(const float4 (&v)[4], int t0, int
 // K), polled pass by pass until every word of the pass carries this call's
 // tag, then quantized to MXFP4.
 template <class DA>
-__device__ __forceinline__ void stage_routed(const DA& A, uint32_t tag, int K, int n, const uint8_t* slots,
+__device__ __forceinline__ void stage_routed(const DA& A, uint32_t tag, int K, int n, const uint16_t* slots,
                                              uint8_t* codes, uint8_t* scales) {
   const int nb = K / 32, tasks = n * nb, j = threadIdx.x & 7;
   const uint64_t tw = wall_clock64();
@@ -871,8 +914,9 @@ __device__ __forceinline__ void stage_routed(const DA& A, uint32_t tag, int K, i
 // stride 2K: gate columns, then up columns), polled pass by pass until every
 // word of the pass carries this call's tag, then quantized to MXFP8.
 template <class DA>
-__device__ __forceinline__ void stage_shared(const DA& A, uint32_t tag, int K, uint8_t* codes, uint8_t* scales) {
-  const int nb = K / 32, tasks = A.T * nb, j = threadIdx.x & 7;
+__device__ __forceinline__ void stage_shared(const DA& A, uint32_t tag, int K, int g0, int n, uint8_t* codes,
+                                             uint8_t* scales) {
+  const int nb = K / 32, tasks = n * nb, j = threadIdx.x & 7;
   const uint64_t tw = wall_clock64();
   for (int t0 = 0; t0 < tasks; t0 += kStagePass) {
     float g[4][4], u[4][4];
@@ -885,7 +929,7 @@ __device__ __forceinline__ void stage_shared(const DA& A, uint32_t tag, int K, u
 #pragma unroll
         for (int i = 0; i < 4; ++i) g[p][i] = u[p][i] = 0.f;
         if (task < tasks) {
-          const uint64_t* src = A.a_s + (size_t)(task / nb) * (2 * K) + 32 * (task % nb) + 4 * j;
+          const uint64_t* src = A.a_s + (size_t)(g0 + task / nb) * (2 * K) + 32 * (task % nb) + 4 * j;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const uint64_t wg = ld_dev(src + i), wu = ld_dev(src + K + i);
@@ -964,9 +1008,9 @@ __device__ __forceinline__ v4f down_compute(const uint8_t* w, const uint8_t* ws_
 // call has given up by then (the status word, read with the last polls), the
 // group's output is NaN instead.
 template <class DA>
-__device__ __forceinline__ void combine(const DA& A, uint32_t tag, const Smem& sm, int hg) {
-  const int H = A.h(), k = A.kk();
-  constexpr int kPer = kDecodeMaxT * 64 / kThreads;  // (row, column) pairs per thread
+__device__ __forceinline__ void combine(const DA& A, uint32_t tag, const SmemOf<DA>& sm, int hg, int g0) {
+  const int H = A.h(), k = A.kk(), T = min(A.T, g0 + kGroup);  // rows g0 .. T - 1
+  constexpr int kPer = kGroup * 64 / kThreads;  // (row, column) pairs per thread
   float d[kPer][kMaxK], s[kPer];
   const uint64_t t0 = wall_clock64();
   bool ok;
@@ -976,8 +1020,8 @@ __device__ __forceinline__ void combine(const DA& A, uint32_t tag, const Smem& s
     status = ld_dev(ctr(A.sync, S_STATUS));  // read with the polls: no extra round trip
 #pragma unroll
     for (int p = 0; p < kPer; ++p) {
-      const int idx = threadIdx.x + p * kThreads;
-      if (idx < A.T * 64) {
+      const int idx = 64 * g0 + threadIdx.x + p * kThreads;
+      if (idx < T * 64) {
         const int t = idx >> 6, h = 64 * hg + (idx & 63);
 #pragma unroll
         for (int j = 0; j < kMaxK; ++j)
@@ -996,8 +1040,8 @@ __device__ __forceinline__ void combine(const DA& A, uint32_t tag, const Smem& s
   } while (keep_polling(ok, t0, A.sync));
 #pragma unroll
   for (int p = 0; p < kPer; ++p) {
-    const int idx = threadIdx.x + p * kThreads;
-    if (idx < A.T * 64) {
+    const int idx = 64 * g0 + threadIdx.x + p * kThreads;
+    if (idx < T * 64) {
       const int t = idx >> 6, h = 64 * hg + (idx & 63);
       float acc = 0.f;
 #pragma unroll
@@ -1012,24 +1056,29 @@ __device__ __forceinline__ void combine(const DA& A, uint32_t tag, const Smem& s
 }
 
 // One sequence entry: compute from buf, request entry j + kBufs into buf,
-// store the results.
+// store the results.  A unit with more than 16 rows (wide instance) runs its
+// 16-row groups one after another on the weight tiles in registers; the next
+// entry's tiles are requested once the last group's products have read them.
 template <class DA>
-__device__ __forceinline__ void run_entry(const DA& A, uint32_t tag, Smem& sm, const Seq& S, int j, Buf& buf,
+__device__ __forceinline__ void run_entry(const DA& A, uint32_t tag, SmemOf<DA>& sm, const Seq& S, int j, Buf& buf,
                                           uint8_t* xq4_lds, uint8_t* xs4_lds, uint8_t* stage, int lane, int wave) {
   if (j < S.nb) {
     const int u = S.b0 + j, per = A.i() / 16;
-    const int dd = u / per, i = u % per;
-    gu_compute(A, sm, xq4_lds, xs4_lds, dd, buf, lane, wave);
-    if (j == 0) trace_at(A, TR_B_MMA);
-    issue(A, sm, S, j + kBufs, lane, wave, buf);  // buf is free once the matrix products have read it
-    __syncthreads();
-    int row, col;
-    float a;
-    if (gu_finish(sm, A.nc1(), sm.ecount[dd], &row, &col, &a))
-      st_dev(&A.a_r[(size_t)sm.tl[dd][row] * A.i() + 16 * i + col], tagged(tag, a));
-    if (j == 0) trace_at(A, TR_B_STORED);
-    __syncthreads();  // sm.red is rewritten by the next unit
-    if (j == 0) trace_at(A, TR_B_RELEASED);
+    const int dd = u / per, i = u % per, n = sm.ecount[dd];
+    for (int g0 = 0; g0 < (DA::kWide ? n : 1); g0 += kGroup) {
+      gu_compute(A, sm, xq4_lds, xs4_lds, dd, g0, buf, lane, wave);
+      if (j == 0 && g0 == 0) trace_at(A, TR_B_MMA);
+      if (!DA::kWide || g0 + kGroup >= n)
+        issue(A, sm, S, j + kBufs, lane, wave, buf);  // buf is free once the matrix products have read it
+      __syncthreads();
+      int row, col;
+      float a;
+      if (gu_finish(sm, A.nc1(), min(n - g0, kGroup), &row, &col, &a))
+        st_dev(&A.a_r[(size_t)sm.slot(dd, g0 + row) * A.i() + 16 * i + col], tagged(tag, a));
+      if (j == 0 && g0 == 0) trace_at(A, TR_B_STORED);
+      __syncthreads();  // sm.red is rewritten by the next group or unit
+      if (j == 0 && g0 == 0) trace_at(A, TR_B_RELEASED);
+    }
     return;
   }
   const int u = S.c0 + j - S.nb;  // shared down units first, then routed
@@ -1043,60 +1092,75 @@ __device__ __forceinline__ void run_entry(const DA& A, uint32_t tag, Smem& sm, c
     const int e = sm.elist[dd], n = sm.ecount[dd];
     const int K = A.i();
     uint8_t* codes = stage;
-    uint8_t* scales = stage + kDecodeMaxT * (K / 2);
+    uint8_t* scales = stage + kGroup * (K / 2);
     // The staged intermediate is the previous entry's when that entry was a
-    // routed down unit of the same expert.  Every thread derives this from
-    // the sequence itself, so the whole workgroup takes the same branch.
+    // routed down unit of the same expert with at most 16 rows.  Every thread
+    // derives this from the sequence itself, so the whole workgroup takes the
+    // same branch.
     const int pu = u - 1;
-    if (!(j > S.nb && pu >= S.ns && (pu - S.ns) / S.nhg == (u - S.ns) / S.nhg)) {
-      stage_routed(A, tag, K, n, sm.tl[dd], codes, scales);
-      __syncthreads();
-      if (j == S.nb) trace_at(A, TR_C_STAGED);
-    }
+    const bool staged = j > S.nb && pu >= S.ns && (pu - S.ns) / S.nhg == (u - S.ns) / S.nhg && n <= kGroup;
     const int KG = (A.kt2() + 3) / 4;
     const uint8_t* w = A.w2 + (size_t)e * ((size_t)A.h() * A.i() / 2) + (size_t)hs * A.kt2() * 1024 + lane * 16;
     const uint8_t* sw = A.w2s + (size_t)e * ((size_t)(A.h() / 16) * KG * 256) + ((size_t)hs * KG * 64 + lane) * 4;
-    out = down_compute<FP4>(w, sw, A.kt2(), A.ct2(), codes, scales, n, buf, lane);
-    issue(A, sm, S, j + kBufs, lane, wave, buf);
+    for (int g0 = 0; g0 < (DA::kWide ? n : 1); g0 += kGroup) {
+      const int ng = min(n - g0, kGroup);
+      if (!staged) {
+        stage_routed(A, tag, K, ng, &sm.slist[sm.eoff[dd] + g0], codes, scales);
+        __syncthreads();
+        if (j == S.nb && g0 == 0) trace_at(A, TR_C_STAGED);
+      }
+      // a later group needs the first batch of tiles again when the product
+      // went through more than one batch
+      if (DA::kWide && g0 > 0 && A.kt2() > kDownBatch) issue(A, sm, S, j, lane, wave, buf);
+      out = down_compute<FP4>(w, sw, A.kt2(), A.ct2(), codes, scales, ng, buf, lane);
+      if (!DA::kWide || g0 + kGroup >= n) issue(A, sm, S, j + kBufs, lane, wave, buf);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (4 * q + r < n)
-        st_dev(&A.d_part[(size_t)sm.tl[dd][4 * q + r] * A.h() + 16 * hs + m], tagged(tag, out[r]));
+      for (int r = 0; r < 4; ++r)
+        if (4 * q + r < ng)
+          st_dev(&A.d_part[(size_t)sm.slot(dd, g0 + 4 * q + r) * A.h() + 16 * hs + m], tagged(tag, out[r]));
+    }
   } else {
     const int K = A.is();
     uint8_t* codes = stage;
-    uint8_t* scales = stage + kDecodeMaxT * K;
-    // shared down units come first in the sequence: a previous down entry
-    // was a shared one and has staged the intermediate already
-    if (j == S.nb) {
-      stage_shared(A, tag, K, codes, scales);
-      __syncthreads();
-    }
+    uint8_t* scales = stage + kGroup * K;
     const int KG = (A.kts() + 3) / 4;
     const uint8_t* w = A.ws2 + (size_t)hs * A.kts() * 2048 + lane * 16;
     const uint8_t* sw = A.ws2s + ((size_t)hs * KG * 64 + lane) * 4;
-    out = down_compute<FP8>(w, sw, A.kts(), A.cts(), codes, scales, A.T, buf, lane);
-    issue(A, sm, S, j + kBufs, lane, wave, buf);
+    for (int g0 = 0; g0 < (DA::kWide ? A.T : 1); g0 += kGroup) {
+      const int ng = min(A.T - g0, kGroup);
+      // shared down units come first in the sequence: with at most 16 rows a
+      // previous down entry was a shared one and has staged the intermediate
+      if (j == S.nb || A.T > kGroup) {
+        stage_shared(A, tag, K, g0, ng, codes, scales);
+        __syncthreads();
+      }
+      if (DA::kWide && g0 > 0 && A.kts() > kDownBatch / 2) issue(A, sm, S, j, lane, wave, buf);
+      out = down_compute<FP8>(w, sw, A.kts(), A.cts(), codes, scales, ng, buf, lane);
+      if (!DA::kWide || g0 + kGroup >= A.T) issue(A, sm, S, j + kBufs, lane, wave, buf);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (4 * q + r < A.T) st_dev(&A.s_part[(size_t)(4 * q + r) * A.h() + 16 * hs + m], tagged(tag, out[r]));
+      for (int r = 0; r < 4; ++r)
+        if (4 * q + r < ng)
+          st_dev(&A.s_part[(size_t)(g0 + 4 * q + r) * A.h() + 16 * hs + m], tagged(tag, out[r]));
+    }
   }
 }
 
 // ------------------------------------------------------------------ kernel
 // The layer itself: phases A, B, C and the combines of this workgroup.
 template <class DA>
-__device__ __forceinline__ void decode_body(const DA& A, uint32_t tag, Smem& sm, unsigned char* dyn, uint64_t* tr,
+__device__ __forceinline__ void decode_body(const DA& A, uint32_t tag, SmemOf<DA>& sm, unsigned char* dyn, uint64_t* tr,
                                             int lane, int wave) {
   const int G = A.G, T = A.T, E = A.e();
 
-  // dynamic LDS: logits, the MXFP4 x, then the MXFP8 x of a shared strip
-  // (phase A) or the staged down-unit intermediate (later)
+  // dynamic LDS (offsets from the host, see lds_layout): the logits; the
+  // MXFP4 x; the MXFP8 x of a shared strip (phase A) or the staged down-unit
+  // intermediate (phase C); the norm weight.  The wide instance overlays the
+  // staged intermediate on the logits and the MXFP8 x on the MXFP4 x.
   float* logits_lds = reinterpret_cast<float*>(dyn);
-  uint8_t* xq4_lds = dyn + align_up((size_t)kDecodeMaxT * E * 4, 16);
+  uint8_t* xq4_lds = dyn + A.off_xq4;
   uint8_t* xs4_lds = xq4_lds + (size_t)T * (A.h() / 2);
-  uint8_t* stage = xq4_lds + align_up((size_t)kDecodeMaxT * (A.h() / 2 + A.h() / 32), 16);
-  uint8_t* x8_lds = stage;
+  uint8_t* stage = dyn + A.off_stage;
+  uint8_t* x8_lds = dyn + A.off_x8;
   float* gamma_lds = reinterpret_cast<float*>(dyn + A.gamma_off);  // the norm weight (with the norm)
 
   // phase A: router units, then shared gate/up strips, strided over the grid.
@@ -1172,14 +1236,15 @@ __device__ __forceinline__ void decode_body(const DA& A, uint32_t tag, Smem& sm,
   if (T <= kWaves) {  // a wavefront per row
     const int row = wave < T ? wave : 0;
     row_topk64(logits_lds + row * E, wave < T, E, A.kr(), lane, sm.ids + row * A.kk(), sm.w + row * A.kk());
-  } else {  // 16 lanes per row, 16 rows
-    const int row = threadIdx.x / 16;
-    rows_topk16(logits_lds + (row < T ? row : 0) * E, row < T, E, A.kr(), threadIdx.x & 15,
-                sm.ids + (row < T ? row : 0) * A.kk(), sm.w + (row < T ? row : 0) * A.kk());
+  } else {  // 16 lanes per row, 16 rows per pass
+    for (int r0 = 0; r0 < (DA::kWide ? T : 1); r0 += kThreads / 16) {
+      const int row = r0 + (int)threadIdx.x / 16;
+      rows_topk16(logits_lds + (row < T ? row : 0) * E, row < T, E, A.kr(), threadIdx.x & 15,
+                  sm.ids + (row < T ? row : 0) * A.kk(), sm.w + (row < T ? row : 0) * A.kk());
+    }
   }
-  if (A.fd() && threadIdx.x >= kThreads - kDecodeMaxT) {  // the folded shared expert: last slot of each row
-    const int t = threadIdx.x - (kThreads - kDecodeMaxT);
-    if (t < T) {
+  if (A.fd() && threadIdx.x >= kThreads - kGroup) {  // the folded shared expert: last slot of each row
+    for (int t = threadIdx.x - (kThreads - kGroup); t < T; t += kGroup) {
       sm.ids[t * A.kk() + A.kr()] = E;
       sm.w[t * A.kk() + A.kr()] = 1.0f;
     }
@@ -1220,17 +1285,17 @@ __device__ __forceinline__ void decode_body(const DA& A, uint32_t tag, Smem& sm,
   // run of phase-B units), listed in ascending order in sm.qrows.  It is made
   // before the pipeline's weight tiles are requested: a wait for x issued
   // after them would also wait for every tile in flight.
-  uint32_t need = 0;
+  uint64_t need = 0;
   if (!early_x4 && !have_all_x4 && S.nb > 0) {
     const int per = A.i() / 16;
     for (int dd = S.b0 / per; dd <= (S.b0 + S.nb - 1) / per; ++dd)
-      for (int s = 0; s < sm.ecount[dd]; ++s) need |= 1u << (sm.tl[dd][s] / A.kk());
+      for (int s = 0; s < sm.ecount[dd]; ++s) need |= 1ull << (sm.slot(dd, s) / A.kk());
   }
   if (need) {  // uniform
-    if (threadIdx.x < kDecodeMaxT && ((need >> threadIdx.x) & 1u))
-      sm.qrows[__popc(need & ((1u << threadIdx.x) - 1u))] = (uint8_t)threadIdx.x;
+    if (threadIdx.x < DA::kMaxT && ((need >> threadIdx.x) & 1ull))
+      sm.qrows[__popcll(need & ((1ull << threadIdx.x) - 1ull))] = (uint8_t)threadIdx.x;
     __syncthreads();
-    const int q_tasks = __popc(need) * (A.h() / 32);
+    const int q_tasks = __popcll(need) * (A.h() / 32);
     for (int t0 = 0; t0 < q_tasks; t0 += kQBatch * kQGroups) {
       uint32_t bits[kQBatch][4];
       x_batch_load<true>(A, t0, q_tasks, sm.qrows, bits);
@@ -1259,7 +1324,8 @@ __device__ __forceinline__ void decode_body(const DA& A, uint32_t tag, Smem& sm,
   }
 
   // combines: workgroup b takes column groups b, b + G, ...
-  for (int hg = blockIdx.x; hg < S.nhg; hg += G) combine(A, tag, sm, hg);
+  for (int hg = blockIdx.x; hg < S.nhg; hg += G)
+    for (int g0 = 0; g0 < (DA::kWide ? T : 1); g0 += kGroup) combine(A, tag, sm, hg, g0);
 }
 
 // A call on a workspace whose status word is set (an earlier call gave up a
@@ -1276,7 +1342,7 @@ __device__ __forceinline__ void poison_output(const DA& A) {
 template <class DA>
 __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
   const uint64_t t_entry = wall_clock64();
-  __shared__ Smem sm;
+  __shared__ SmemOf<DA> sm;
   extern __shared__ __align__(16) unsigned char dyn[];
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int G = A.G;
@@ -1330,45 +1396,62 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
 // ------------------------------------------------------------------ host side
 struct Carve {
   size_t sync, sync_end;
-  size_t logits, a_r, a_s, d_part, s_part, trace, total;
+  size_t trace, logits, a_r, a_s, d_part, s_part, total;
 };
 
-Carve carve(const moe_layer_t& L) {
-  const size_t T = kDecodeMaxT, H = L.hidden, I = L.inter, E = L.num_experts, k = layer_slots(L),
-               Is = L.shared_inter;
+// Workspace of an instance taking up to MT rows: the sync block, the trace
+// words (offsets independent of MT), then the tagged words.
+Carve carve(const moe_layer_t& L, int MT) {
+  const size_t T = MT, H = L.hidden, I = L.inter, E = L.num_experts, k = layer_slots(L), Is = L.shared_inter;
   Carve c{};
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, 256); return at; };
   const size_t line = kLine * 4;
   c.sync = take(kSyncLines * line);
   c.sync_end = o;
+  c.trace = take((size_t)kDecodeMaxGrid * kTraceWords * 8);
   c.logits = take(T * E * 8);
   c.a_r = take(T * k * I * 8);
   c.a_s = take(T * 2 * Is * 8 + 16);
   c.d_part = take(T * k * H * 8);
   c.s_part = take(T * H * 8);
-  c.trace = take((size_t)kDecodeMaxGrid * kTraceWords * 8);
   c.total = o;
   return c;
 }
 
-// Dynamic LDS: logits, the MXFP4 x, then either the MXFP8 x of a shared strip
-// (phase A) or the staged intermediate.
-size_t dyn_lds_bytes(const moe_layer_t& L) {
-  const size_t T = kDecodeMaxT;
-  const size_t logits = align_up(T * L.num_experts * 4, 16);
-  const size_t xq = align_up(T * (L.hidden / 2 + L.hidden / 32), 16);
-  const size_t st4 = T * (L.inter / 2 + L.inter / 32);
-  const size_t st8 = T * ((size_t)L.shared_inter + L.shared_inter / 32);
+// Dynamic LDS of an instance taking up to MT rows.  Up to 16 rows: logits,
+// the MXFP4 x, then either the MXFP8 x of a shared strip (phase A) or a
+// staged down-unit intermediate (phase C), then the norm weight.  Wide
+// instance: the staged intermediate over the logits (dead after routing) and
+// the MXFP8 x over the MXFP4 x (a strip's copy is dead before the copy for
+// phase B is made); the norm weight is read from memory.
+struct LdsLayout {
+  size_t xq4, stage, x8, gamma, total;
+};
+
+LdsLayout lds_layout(const moe_layer_t& L, int MT) {
+  const size_t H = L.hidden, I = L.inter, E = L.num_experts, Is = L.shared_inter;
+  const size_t logits = align_up((size_t)MT * E * 4, 16);
+  const size_t xq = align_up((size_t)MT * (H / 2 + H / 32), 16);
+  const size_t st4 = (size_t)kGroup * (I / 2 + I / 32), st8 = (size_t)kGroup * (Is + Is / 32);
   const size_t st = align_up(st4 > st8 ? st4 : st8, 16);
-  const size_t x8 = L.shared_inter ? align_up(T * (L.hidden + L.hidden / 32), 16) : 0;
-  return logits + xq + (st > x8 ? st : x8) + (L.norm_weight ? (size_t)L.hidden * 4 : 0);
+  const size_t x8 = Is ? align_up((size_t)kGroup * (H + H / 32), 16) : 0;
+  LdsLayout o{};
+  if (MT <= kGroup) {
+    o.xq4 = logits;
+    o.stage = o.x8 = logits + xq;
+    o.gamma = o.stage + (st > x8 ? st : x8);
+    o.total = o.gamma + (L.norm_weight ? H * 4 : 0);
+  } else {
+    o.stage = 0;
+    o.xq4 = o.x8 = logits > st ? logits : st;
+    o.gamma = 0;
+    o.total = o.xq4 + (xq > x8 ? xq : x8);
+  }
+  return o;
 }
 
-// Offset of the norm weight's copy: the end of the other dynamic LDS data.
-size_t gamma_lds_offset(const moe_layer_t& L) {
-  return dyn_lds_bytes(L) - (L.norm_weight ? (size_t)L.hidden * 4 : 0);
-}
+int max_rows_for(int T) { return T <= kDecodeMaxT ? kDecodeMaxT : kDecodeWideMaxT; }
 
 // Grid of the persistent launch: as many workgroups as the device keeps
 // resident at once (one per CU), since every workgroup must run concurrently.
@@ -1383,7 +1466,7 @@ int grid_size(size_t lds) {
   if (c != 0 && (c >> 32) == lds) return (int)(uint32_t)c;
   int cus = 0, occ = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (lds + sizeof(Smem) > 64 * 1024 &&
+  if (lds + sizeof(SmemOf<DA>) > 64 * 1024 &&
       hipFuncSetAttribute(reinterpret_cast<const void*>(fused_decode_kernel<DA>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return 0;
@@ -1407,28 +1490,36 @@ hipError_t launch_instance(const DecodeArgs& args, size_t lds, hipStream_t strea
 
 // The MiniMax-M3.1 layer shape (hidden 3072, 128 experts top-4, intermediate
 // 1024, shared intermediate 1024) has its own compiled instance.
-using MiniMaxShape = DArgs<3072, 1024, 1024, 128, 4, 0>;
-using MiniMaxFolded = DArgs<3072, 1024, -1, 128, 4, 1>;  // shared expert folded in as expert 128
-using AnyShape = DArgs<0, 0, 0, 0, 0, -1>;
+using MiniMaxShape = DArgs<3072, 1024, 1024, 128, 4, 0, kDecodeMaxT>;
+using MiniMaxFolded = DArgs<3072, 1024, -1, 128, 4, 1, kDecodeMaxT>;  // shared expert folded in as expert 128
+using AnyShape = DArgs<0, 0, 0, 0, 0, -1, kDecodeMaxT>;
+// wide steps (17..64 rows)
+using MiniMaxShapeW = DArgs<3072, 1024, 1024, 128, 4, 0, kDecodeWideMaxT>;
+using MiniMaxFoldedW = DArgs<3072, 1024, -1, 128, 4, 1, kDecodeWideMaxT>;
+using AnyShapeW = DArgs<0, 0, 0, 0, 0, -1, kDecodeWideMaxT>;
 
 int n_chunks(int tiles) { return tiles % 4 == 0 ? 4 : (tiles % 2 == 0 ? 2 : 1); }
 
 }  // namespace
 
-size_t decode_ws_bytes(const moe_layer_t& L) { return carve(L).total; }
-size_t decode_sync_bytes(const moe_layer_t& L) { return carve(L).sync_end; }
-size_t decode_trace_offset(const moe_layer_t& L) { return carve(L).trace; }
+size_t decode_ws_bytes(const moe_layer_t& L, int T) { return carve(L, max_rows_for(T)).total; }
+size_t decode_sync_bytes(const moe_layer_t& L) { return carve(L, kDecodeMaxT).sync_end; }
+size_t decode_trace_offset(const moe_layer_t& L) { return carve(L, kDecodeMaxT).trace; }
 
-bool decode_supported(const moe_layer_t& L) {
-  // a K-chunk of the gate/up (K = H) must fit the register buffers
+bool decode_supported(const moe_layer_t& L, int T) {
+  if (T < 1 || T > kDecodeWideMaxT) return false;
+  // a K-chunk of the gate/up (K = H) must fit the register buffers, the LDS a workgroup
   const int KT1 = L.hidden / 128;
-  return KT1 / n_chunks(KT1) <= kMaxCT && dyn_lds_bytes(L) + sizeof(Smem) <= 160 * 1024;
+  const size_t smem = T <= kDecodeMaxT ? sizeof(SmemT<kDecodeMaxT>) : sizeof(SmemT<kDecodeWideMaxT>);
+  return KT1 / n_chunks(KT1) <= kMaxCT && lds_layout(L, max_rows_for(T)).total + smem <= 160 * 1024;
 }
 
 hipError_t launch_decode(const moe_layer_t& L, const uint16_t* x, int T, const uint16_t* residual,
                          uint16_t* y, void* ws, int32_t* ids_out, float* w_out, hipStream_t stream) {
-  const Carve c = carve(L);
-  const size_t lds = dyn_lds_bytes(L);
+  const int MT = max_rows_for(T);
+  const Carve c = carve(L, MT);
+  const LdsLayout lay = lds_layout(L, MT);
+  const size_t lds = lay.total;
   char* base = reinterpret_cast<char*>(ws);
   DecodeArgs A{};
   A.T = T;
@@ -1439,7 +1530,10 @@ hipError_t launch_decode(const moe_layer_t& L, const uint16_t* x, int T, const u
   A.fold = L.shared_folded ? 1 : 0;
   A.norm_w = L.norm_weight;
   A.norm_eps = L.norm_eps;
-  A.gamma_off = (int)gamma_lds_offset(L);
+  A.gamma_off = (int)lay.gamma;
+  A.off_xq4 = (int)lay.xq4;
+  A.off_stage = (int)lay.stage;
+  A.off_x8 = (int)lay.x8;
   A.Is = L.shared_inter;
   A.KT1 = A.H / 128;
   A.NC1 = n_chunks(A.KT1);
@@ -1473,11 +1567,15 @@ hipError_t launch_decode(const moe_layer_t& L, const uint16_t* x, int T, const u
   A.s_part = reinterpret_cast<uint64_t*>(base + c.s_part);
   A.trace = reinterpret_cast<uint64_t*>(base + c.trace);
   A.tagged = A.logits;
-  A.n_tagged = (uint32_t)((c.trace - c.logits) / 8);
-  if (A.H == 3072 && A.I == 1024 && A.E == 128 && A.k == 4) {
-    if (A.Is == 1024 && !A.fold) return launch_instance<MiniMaxShape>(A, lds, stream);
-    if (A.Is == 0 && A.fold) return launch_instance<MiniMaxFolded>(A, lds, stream);
+  A.n_tagged = (uint32_t)((c.total - c.logits) / 8);
+  const bool minimax = A.H == 3072 && A.I == 1024 && A.E == 128 && A.k == 4;
+  if (MT > kDecodeMaxT) {
+    if (minimax && A.Is == 1024 && !A.fold) return launch_instance<MiniMaxShapeW>(A, lds, stream);
+    if (minimax && A.Is == 0 && A.fold) return launch_instance<MiniMaxFoldedW>(A, lds, stream);
+    return launch_instance<AnyShapeW>(A, lds, stream);
   }
+  if (minimax && A.Is == 1024 && !A.fold) return launch_instance<MiniMaxShape>(A, lds, stream);
+  if (minimax && A.Is == 0 && A.fold) return launch_instance<MiniMaxFolded>(A, lds, stream);
   return launch_instance<AnyShape>(A, lds, stream);
 }
 

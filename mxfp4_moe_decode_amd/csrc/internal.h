@@ -79,13 +79,15 @@ hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int block_
                              int32_t* num_padded, void* ws, hipStream_t stream);
 
 // ------------------------------------------------------------------ fused decode
-constexpr int kDecodeMaxT = 16;
+constexpr int kDecodeMaxT = 16;      // rows of a decode step (mono decode's limit)
+constexpr int kDecodeWideMaxT = 64;  // rows of a wide fused step
 constexpr int kDecodeMaxGrid = 2048;
 constexpr int kTraceWords = 16;
-size_t decode_ws_bytes(const moe_layer_t& L);
-// Shapes the fused decode kernel handles (a gate/up K-chunk fits its register
-// buffers, its LDS fits a workgroup).
-bool decode_supported(const moe_layer_t& L);
+// Workspace for steps of T rows (sized for 16 rows up to T = 16, else for 64).
+size_t decode_ws_bytes(const moe_layer_t& L, int T);
+// Shapes and row counts the fused decode kernel handles (T <= 64, a gate/up
+// K-chunk fits its register buffers, its LDS fits a workgroup).
+bool decode_supported(const moe_layer_t& L, int T);
 hipError_t launch_decode(const moe_layer_t& L, const uint16_t* x, int T, const uint16_t* residual,
                          uint16_t* y, void* ws, int32_t* ids_out, float* w_out,
                          hipStream_t stream);
