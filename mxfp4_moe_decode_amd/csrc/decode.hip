@@ -148,13 +148,17 @@ struct SmemT {
   static constexpr int kSlots = MT * kMaxK;
   int32_t ids[kSlots];
   float w[kSlots];
-  int hist[256];
+  uint64_t rmask[256];  // rows selecting each expert (an expert takes at most one slot per row)
   int epos[256];
-  int fill[kSlots];
   uint8_t elist[kSlots];
   uint8_t ecount[kSlots];
   uint16_t eoff[kSlots];
   uint16_t slist[kSlots];
+  // wide instance: expert-groups q = (selected expert qd[q], rows 16 qg[q] ..
+  // +16), experts in list order; the folded shared expert's are the last NQF
+  uint16_t qd[kSlots];
+  uint8_t qg[kSlots];
+  int NQ, NQF;
   float red[kWaves][2][kGroup][16];             // chunk sums [chunk][gate/up][row][column]
   int wave_cnt[kWaves];
   int wave_sum[kWaves];
@@ -513,14 +517,15 @@ __device__ __forceinline__ void unit_router(const DA& A, SmemOf<DA>& sm, uint32_
 // columns); SwiGLU is applied where it is staged.
 template <class DA>
 __device__ __forceinline__ void unit_shared_strip(const DA& A, uint32_t tag, SmemOf<DA>& sm, const float* gamma_lds, int st,
-                                                  uint8_t* x8, uint8_t* xq4, uint8_t* xs4, int lane, int wave) {
+                                                  int g0, uint8_t* x8, uint8_t* xq4, uint8_t* xs4, int lane,
+                                                  int wave) {
   const int CT = A.ct1(), KG = (A.kt1() + 3) / 4, nb = A.h() / 32;
   const int m = lane & 15, q = lane >> 4;
   const bool act = wave < A.nc1();
   const int t0 = wave * CT;
   uint8_t* xs8 = x8 + (size_t)kGroup * A.h();
   uint32_t bits[kQBatch][4];
-  x_batch_load<false>(A, 0, min(A.T, kGroup) * nb, nullptr, bits);
+  x_batch_load<false>(A, 0, min(A.T - g0, kGroup) * nb, nullptr, bits, g0 * nb);
   v4i B[kMaxCT][2];
   uint32_t sw[3];
   if (act) {
@@ -535,11 +540,11 @@ __device__ __forceinline__ void unit_shared_strip(const DA& A, uint32_t tag, Sme
 #pragma unroll
     for (int g = 0; g < 3; ++g) sw[g] = load_stream4(sp + (size_t)min(t0 / 4 + g, KG - 1) * 256);
   }
-  // 16-row groups of x (the wide instance), each on the weight tiles in registers
-  for (int g0 = 0; g0 < (DA::kWide ? A.T : 1); g0 += kGroup) {
+  // the strip's 16-row group of x (the wide instance schedules one unit per group)
+  {
     const int ng = min(A.T - g0, kGroup), tasks = ng * nb;
     for (int b0 = 0; b0 < tasks; b0 += kQBatch * kQGroups) {
-      if (b0 > 0 || g0 > 0) x_batch_load<false>(A, b0, tasks, nullptr, bits, g0 * nb);
+      if (b0 > 0) x_batch_load<false>(A, b0, tasks, nullptr, bits, g0 * nb);
       if (A.norm_w) x_batch_norm<false>(A, sm, gamma_lds, b0, tasks, nullptr, bits, g0 * nb);
       x_batch_quant<FP8, false>(A, b0, tasks, nullptr, bits, x8, xs8);
       if (A.T <= kEarlyQuantT) x_batch_quant<FP4, false>(A, b0, tasks, nullptr, bits, xq4, xs4);
@@ -603,19 +608,21 @@ __device__ __forceinline__ bool gu_finish(const SM& sm, int nc, int n, int* row,
 }
 
 // ------------------------------------------------------------------ routing
-// Selected experts in ascending expert order (every workgroup builds the same
-// list) and the slots routed to each.  The order of slots inside a list is
-// not fixed; nothing depends on it, since every result is addressed by slot.
+// Selected experts in ascending expert order and the slots routed to each, in
+// ascending row order.  Every workgroup builds the same lists: the wide
+// instance cuts a list into 16-slot groups, and the workgroup writing a
+// group's gate/up results and the one reading them must agree on its slots.
+// A row takes an expert at most once, so the rows selecting expert e form a
+// bit mask, and a slot's place in e's list is the number of earlier rows in it.
 template <class DA>
 __device__ __forceinline__ void build_expert_list(const DA& A, SmemOf<DA>& sm, int lane, int wave) {
-  constexpr int kSlots = SmemOf<DA>::kSlots;
+  static_assert(DA::kMaxT <= 64, "one mask bit per row");
   const int S = A.T * A.kk(), tid = threadIdx.x;
-  sm.hist[tid] = 0;
-  for (int i = tid; i < kSlots; i += kThreads) sm.fill[i] = 0;
+  sm.rmask[tid] = 0ull;
   __syncthreads();
-  for (int sl = tid; sl < S; sl += kThreads) atomicAdd(&sm.hist[sm.ids[sl]], 1);
+  for (int sl = tid; sl < S; sl += kThreads) atomicOr(&sm.rmask[sm.ids[sl]], 1ull << (sl / A.kk()));
   __syncthreads();
-  const int cnt = sm.hist[tid];
+  const int cnt = __popcll(sm.rmask[tid]);
   const bool used = cnt > 0;
   const uint64_t mask = __ballot(used);
   // inclusive scan of the counts over the wavefront (expert order)
@@ -643,8 +650,33 @@ __device__ __forceinline__ void build_expert_list(const DA& A, SmemOf<DA>& sm, i
   if (tid == 0) sm.D = sm.wave_cnt[0] + sm.wave_cnt[1] + sm.wave_cnt[2] + sm.wave_cnt[3];
   __syncthreads();
   for (int sl = tid; sl < S; sl += kThreads) {
-    const int dd = sm.epos[sm.ids[sl]];
-    sm.slist[sm.eoff[dd] + atomicAdd(&sm.fill[dd], 1)] = (uint16_t)sl;
+    const int e = sm.ids[sl];
+    const uint64_t before = sm.rmask[e] & ((1ull << (sl / A.kk())) - 1ull);
+    sm.slist[sm.eoff[sm.epos[e]] + __popcll(before)] = (uint16_t)sl;
+  }
+  if constexpr (DA::kWide) {
+    // expert-groups: ceil(count / 16) per selected expert (thread tid = dd)
+    const int D = sm.D;
+    const int ng = tid < D ? (sm.ecount[tid] + kGroup - 1) / kGroup : 0;
+    int gi = ng;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int v = __shfl_up(gi, d);
+      if (lane >= d) gi += v;
+    }
+    __syncthreads();  // sm.wave_sum is reused
+    if (lane == kWave - 1) sm.wave_sum[wave] = gi;
+    __syncthreads();
+    int gbase = 0;
+    for (int w = 0; w < wave; ++w) gbase += sm.wave_sum[w];
+    for (int g = 0; g < ng; ++g) {
+      sm.qd[gbase + gi - ng + g] = (uint16_t)tid;
+      sm.qg[gbase + gi - ng + g] = (uint8_t)g;
+    }
+    if (tid == 0) {
+      sm.NQ = sm.wave_sum[0] + sm.wave_sum[1] + sm.wave_sum[2] + sm.wave_sum[3];
+      sm.NQF = A.fd() ? (A.T + kGroup - 1) / kGroup : 0;
+    }
   }
   __syncthreads();
 }
@@ -654,8 +686,9 @@ __device__ __forceinline__ void build_expert_list(const DA& A, SmemOf<DA>& sm, i
 // phase-C units [c0, c1).
 struct Seq {
   int b0, nb, c0, nc;
-  int D, nhg, ns;  // selected experts, 64-column groups, shared down units (nhg or 0)
+  int D, nhg, ns;  // selected experts, 64-column groups, shared down units
   int fold;        // the last selected expert is the folded shared expert (gate/up done in phase A)
+  int NQ, NQF;     // wide instance: expert-groups, of which the folded expert's (the last)
 };
 
 struct Buf {
@@ -713,11 +746,37 @@ __device__ __forceinline__ bool issue_gu(const DA& A, int e, int i, int lane, in
   return true;
 }
 
-// Expert (index into the selected-expert list) of routed down unit ur: with
-// the shared expert folded in (the list's last entry) its units come first.
-__device__ __forceinline__ int down_expert(const Seq& S, int ur) {
-  const int q = ur / S.nhg;
-  return S.fold ? (q == 0 ? S.D - 1 : q - 1) : q;
+// Phase-B unit u: selected expert dd, first row g0 of its 16-row group (the
+// wide instance schedules each expert-group separately), 16-column strip i.
+template <class DA>
+__device__ __forceinline__ void b_unit(const DA& A, const SmemOf<DA>& sm, int u, int& dd, int& g0, int& i) {
+  const int per = A.i() / 16, q = u / per;
+  i = u % per;
+  if constexpr (DA::kWide) {
+    dd = sm.qd[q];
+    g0 = kGroup * sm.qg[q];
+  } else {
+    dd = q;
+    g0 = 0;
+  }
+}
+
+// Routed phase-C unit ur (counted after the shared ones): selected expert dd,
+// first row g0, 64-column group hg.  With the shared expert folded in (the
+// list's last expert) its units come first.
+template <class DA>
+__device__ __forceinline__ void c_unit(const DA& A, const SmemOf<DA>& sm, const Seq& S, int ur, int& dd, int& g0,
+                                       int& hg) {
+  const int qc = ur / S.nhg;
+  hg = ur % S.nhg;
+  if constexpr (DA::kWide) {
+    const int q = S.fold ? (qc + S.NQ - S.NQF) % S.NQ : qc;
+    dd = sm.qd[q];
+    g0 = kGroup * sm.qg[q];
+  } else {
+    dd = S.fold ? (qc == 0 ? S.D - 1 : qc - 1) : qc;
+    g0 = 0;
+  }
 }
 
 // Requests the weight tiles and scale words of sequence entry j into buf.
@@ -730,8 +789,9 @@ __device__ __forceinline__ void issue(const DA& A, const SmemOf<DA>& sm, const S
   if (j >= S.nb + S.nc) return;
   uint32_t n0 = 0, n1 = 0, n2 = 0, n3 = 0, n4 = 0, n5 = 0;
   if (j < S.nb) {
-    const int u = S.b0 + j, per = A.i() / 16;
-    if (!issue_gu(A, sm.elist[u / per], u % per, lane, wave, buf, n0, n1, n2, n3, n4, n5)) return;
+    int dd, g0, i;
+    b_unit(A, sm, S.b0 + j, dd, g0, i);
+    if (!issue_gu(A, sm.elist[dd], i, lane, wave, buf, n0, n1, n2, n3, n4, n5)) return;
   } else {
     // down units: both kinds load 1 KB weight blocks at a 1 KB stride (a
     // routed FP4 tile is one block, a shared FP8 tile two) and two scale words
@@ -739,14 +799,15 @@ __device__ __forceinline__ void issue(const DA& A, const SmemOf<DA>& sm, const S
     const uint8_t *wb, *sp;
     int nq, KG;
     if (u >= S.ns) {
-      const int ur = u - S.ns;
-      const int e = sm.elist[down_expert(S, ur)], hs = 4 * (ur % S.nhg) + wave;
+      int dd, g0, hg;
+      c_unit(A, sm, S, u - S.ns, dd, g0, hg);
+      const int e = sm.elist[dd], hs = 4 * hg + wave;
       KG = (A.kt2() + 3) / 4;
       nq = min(A.kt2(), kDownBatch);
       wb = A.w2 + (size_t)e * ((size_t)A.h() * A.i() / 2) + (size_t)hs * A.kt2() * 1024 + lane * 16;
       sp = A.w2s + (size_t)e * ((size_t)(A.h() / 16) * KG * 256) + ((size_t)hs * KG * 64 + lane) * 4;
     } else {
-      const int hs = 4 * u + wave;
+      const int hs = 4 * (u % S.nhg) + wave;
       KG = (A.kts() + 3) / 4;
       nq = 2 * min(A.kts(), kDownBatch / 2);
       wb = A.ws2 + (size_t)hs * A.kts() * 2048 + lane * 16;
@@ -783,8 +844,9 @@ __device__ __forceinline__ void gu_compute(const DA& A, SmemOf<DA>& sm, const ui
     // rows past the group's slot count repeat its last token: their
     // products land in result rows that are never read
     tok = sm.slot(dd, g0 + (m < n ? m : n - 1)) / A.kk();
-  } else {
-    tok = min(g0 + m, A.T - 1);
+  } else {  // the folded expert's units: the group's rows of x, local in LDS
+    const int ng = min(A.T - g0, kGroup);
+    tok = m < ng ? m : ng - 1;
   }
   const int q = lane >> 4;
   const int CT = A.ct1(), t0 = wave * CT;
@@ -815,11 +877,11 @@ __device__ __forceinline__ void gu_compute(const DA& A, SmemOf<DA>& sm, const ui
 
 template <class DA>
 __device__ __forceinline__ void unit_fold_gu(const DA& A, uint32_t tag, SmemOf<DA>& sm, const float* gamma_lds, int i,
-                                             uint8_t* xq4, uint8_t* xs4, bool& have_x4, int lane, int wave) {
-  const int tasks = A.T * (A.h() / 32);
+                                             int g0, uint8_t* xq4, uint8_t* xs4, int& x4_group, int lane, int wave) {
+  const int nb = A.h() / 32, ng = min(A.T - g0, kGroup), tasks = ng * nb;
   uint32_t bits[kQBatch][4];
-  const bool quant = !have_x4;  // uniform
-  if (quant) x_batch_load<false>(A, 0, tasks, nullptr, bits);
+  const bool quant = x4_group != g0;  // uniform: the group's rows are not in LDS yet
+  if (quant) x_batch_load<false>(A, 0, tasks, nullptr, bits, g0 * nb);
   Buf buf;
   uint32_t n0 = 0, n1 = 0, n2 = 0, n3 = 0, n4 = 0, n5 = 0;
   issue_gu(A, A.e(), i, lane, wave, buf, n0, n1, n2, n3, n4, n5);
@@ -830,25 +892,24 @@ __device__ __forceinline__ void unit_fold_gu(const DA& A, uint32_t tag, SmemOf<D
   buf.w4 = n4;
   buf.w5 = n5;
   if (quant) {
+    __syncthreads();  // earlier readers of the LDS rows are done
     for (int b0 = 0; b0 < tasks; b0 += kQBatch * kQGroups) {
-      if (b0 > 0) x_batch_load<false>(A, b0, tasks, nullptr, bits);
-      if (A.norm_w) x_batch_norm<false>(A, sm, gamma_lds, b0, tasks, nullptr, bits);
+      if (b0 > 0) x_batch_load<false>(A, b0, tasks, nullptr, bits, g0 * nb);
+      if (A.norm_w) x_batch_norm<false>(A, sm, gamma_lds, b0, tasks, nullptr, bits, g0 * nb);
       x_batch_quant<FP4, false>(A, b0, tasks, nullptr, bits, xq4, xs4);
     }
-    have_x4 = true;
+    x4_group = g0;
     trace_at(A, TR_XQ);
   }
   __syncthreads();  // the x rows are in LDS
-  for (int g0 = 0; g0 < A.T; g0 += kGroup) {  // 16-row groups, the weight tiles kept in registers
-    gu_compute(A, sm, xq4, xs4, -1, g0, buf, lane, wave);
-    trace_at(A, TR_S_MMA);
-    __syncthreads();
-    int row, col;
-    float a;
-    if (gu_finish(sm, A.nc1(), min(A.T - g0, kGroup), &row, &col, &a))
-      st_dev(&A.a_r[(size_t)((g0 + row) * A.kk() + A.kr()) * A.i() + 16 * i + col], tagged(tag, a));
-    __syncthreads();  // sm.red is rewritten by the next group or unit
-  }
+  gu_compute(A, sm, xq4, xs4, -1, g0, buf, lane, wave);
+  trace_at(A, TR_S_MMA);
+  __syncthreads();
+  int row, col;
+  float a;
+  if (gu_finish(sm, A.nc1(), ng, &row, &col, &a))
+    st_dev(&A.a_r[(size_t)((g0 + row) * A.kk() + A.kr()) * A.i() + 16 * i + col], tagged(tag, a));
+  __syncthreads();  // sm.red is rewritten by the next unit
 }
 
 // Staging of a down unit's intermediate rows into LDS as MX blocks: codes
@@ -1056,92 +1117,75 @@ __device__ __forceinline__ void combine(const DA& A, uint32_t tag, const SmemOf<
 }
 
 // One sequence entry: compute from buf, request entry j + kBufs into buf,
-// store the results.  A unit with more than 16 rows (wide instance) runs its
-// 16-row groups one after another on the weight tiles in registers; the next
-// entry's tiles are requested once the last group's products have read them.
+// store the results.  An entry covers at most 16 rows: the wide instance
+// schedules each 16-row group of an expert as a unit of its own.
 template <class DA>
 __device__ __forceinline__ void run_entry(const DA& A, uint32_t tag, SmemOf<DA>& sm, const Seq& S, int j, Buf& buf,
                                           uint8_t* xq4_lds, uint8_t* xs4_lds, uint8_t* stage, int lane, int wave) {
   if (j < S.nb) {
-    const int u = S.b0 + j, per = A.i() / 16;
-    const int dd = u / per, i = u % per, n = sm.ecount[dd];
-    for (int g0 = 0; g0 < (DA::kWide ? n : 1); g0 += kGroup) {
-      gu_compute(A, sm, xq4_lds, xs4_lds, dd, g0, buf, lane, wave);
-      if (j == 0 && g0 == 0) trace_at(A, TR_B_MMA);
-      if (!DA::kWide || g0 + kGroup >= n)
-        issue(A, sm, S, j + kBufs, lane, wave, buf);  // buf is free once the matrix products have read it
-      __syncthreads();
-      int row, col;
-      float a;
-      if (gu_finish(sm, A.nc1(), min(n - g0, kGroup), &row, &col, &a))
-        st_dev(&A.a_r[(size_t)sm.slot(dd, g0 + row) * A.i() + 16 * i + col], tagged(tag, a));
-      if (j == 0 && g0 == 0) trace_at(A, TR_B_STORED);
-      __syncthreads();  // sm.red is rewritten by the next group or unit
-      if (j == 0 && g0 == 0) trace_at(A, TR_B_RELEASED);
-    }
+    int dd, g0, i;
+    b_unit(A, sm, S.b0 + j, dd, g0, i);
+    gu_compute(A, sm, xq4_lds, xs4_lds, dd, g0, buf, lane, wave);
+    if (j == 0) trace_at(A, TR_B_MMA);
+    issue(A, sm, S, j + kBufs, lane, wave, buf);  // buf is free once the matrix products have read it
+    __syncthreads();
+    int row, col;
+    float a;
+    if (gu_finish(sm, A.nc1(), min(sm.ecount[dd] - g0, kGroup), &row, &col, &a))
+      st_dev(&A.a_r[(size_t)sm.slot(dd, g0 + row) * A.i() + 16 * i + col], tagged(tag, a));
+    if (j == 0) trace_at(A, TR_B_STORED);
+    __syncthreads();  // sm.red is rewritten by the next unit
+    if (j == 0) trace_at(A, TR_B_RELEASED);
     return;
   }
   const int u = S.c0 + j - S.nb;  // shared down units first, then routed
-  const bool routed = u >= S.ns;
-  const int dd = routed ? down_expert(S, u - S.ns) : -1;
-  const int hg = routed ? (u - S.ns) % S.nhg : u;  // 64-column group
-  const int hs = 4 * hg + wave;
   const int m = lane & 15, q = lane >> 4;
+  // The staged intermediate is the previous entry's when that entry was a
+  // down unit of the same kind and (expert-)group.  Every thread derives this
+  // from the sequence itself, so the whole workgroup takes the same branch.
+  const int pu = u - 1;
   v4f out;
-  if (routed) {
-    const int e = sm.elist[dd], n = sm.ecount[dd];
+  if (u >= S.ns) {
+    int dd, g0, hg;
+    c_unit(A, sm, S, u - S.ns, dd, g0, hg);
+    const bool staged = j > S.nb && pu >= S.ns && (pu - S.ns) / S.nhg == (u - S.ns) / S.nhg;
+    const int hs = 4 * hg + wave;
+    const int e = sm.elist[dd], n = min(sm.ecount[dd] - g0, kGroup);
     const int K = A.i();
     uint8_t* codes = stage;
     uint8_t* scales = stage + kGroup * (K / 2);
-    // The staged intermediate is the previous entry's when that entry was a
-    // routed down unit of the same expert with at most 16 rows.  Every thread
-    // derives this from the sequence itself, so the whole workgroup takes the
-    // same branch.
-    const int pu = u - 1;
-    const bool staged = j > S.nb && pu >= S.ns && (pu - S.ns) / S.nhg == (u - S.ns) / S.nhg && n <= kGroup;
+    if (!staged) {
+      stage_routed(A, tag, K, n, &sm.slist[sm.eoff[dd] + g0], codes, scales);
+      __syncthreads();
+      if (j == S.nb) trace_at(A, TR_C_STAGED);
+    }
     const int KG = (A.kt2() + 3) / 4;
     const uint8_t* w = A.w2 + (size_t)e * ((size_t)A.h() * A.i() / 2) + (size_t)hs * A.kt2() * 1024 + lane * 16;
     const uint8_t* sw = A.w2s + (size_t)e * ((size_t)(A.h() / 16) * KG * 256) + ((size_t)hs * KG * 64 + lane) * 4;
-    for (int g0 = 0; g0 < (DA::kWide ? n : 1); g0 += kGroup) {
-      const int ng = min(n - g0, kGroup);
-      if (!staged) {
-        stage_routed(A, tag, K, ng, &sm.slist[sm.eoff[dd] + g0], codes, scales);
-        __syncthreads();
-        if (j == S.nb && g0 == 0) trace_at(A, TR_C_STAGED);
-      }
-      // a later group needs the first batch of tiles again when the product
-      // went through more than one batch
-      if (DA::kWide && g0 > 0 && A.kt2() > kDownBatch) issue(A, sm, S, j, lane, wave, buf);
-      out = down_compute<FP4>(w, sw, A.kt2(), A.ct2(), codes, scales, ng, buf, lane);
-      if (!DA::kWide || g0 + kGroup >= n) issue(A, sm, S, j + kBufs, lane, wave, buf);
+    out = down_compute<FP4>(w, sw, A.kt2(), A.ct2(), codes, scales, n, buf, lane);
+    issue(A, sm, S, j + kBufs, lane, wave, buf);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (4 * q + r < ng)
-          st_dev(&A.d_part[(size_t)sm.slot(dd, g0 + 4 * q + r) * A.h() + 16 * hs + m], tagged(tag, out[r]));
-    }
+    for (int r = 0; r < 4; ++r)
+      if (4 * q + r < n)
+        st_dev(&A.d_part[(size_t)sm.slot(dd, g0 + 4 * q + r) * A.h() + 16 * hs + m], tagged(tag, out[r]));
   } else {
+    const int g0 = kGroup * (u / S.nhg), hs = 4 * (u % S.nhg) + wave, n = min(A.T - g0, kGroup);
+    const bool staged = j > S.nb && pu / S.nhg == u / S.nhg;
     const int K = A.is();
     uint8_t* codes = stage;
     uint8_t* scales = stage + kGroup * K;
+    if (!staged) {
+      stage_shared(A, tag, K, g0, n, codes, scales);
+      __syncthreads();
+    }
     const int KG = (A.kts() + 3) / 4;
     const uint8_t* w = A.ws2 + (size_t)hs * A.kts() * 2048 + lane * 16;
     const uint8_t* sw = A.ws2s + ((size_t)hs * KG * 64 + lane) * 4;
-    for (int g0 = 0; g0 < (DA::kWide ? A.T : 1); g0 += kGroup) {
-      const int ng = min(A.T - g0, kGroup);
-      // shared down units come first in the sequence: with at most 16 rows a
-      // previous down entry was a shared one and has staged the intermediate
-      if (j == S.nb || A.T > kGroup) {
-        stage_shared(A, tag, K, g0, ng, codes, scales);
-        __syncthreads();
-      }
-      if (DA::kWide && g0 > 0 && A.kts() > kDownBatch / 2) issue(A, sm, S, j, lane, wave, buf);
-      out = down_compute<FP8>(w, sw, A.kts(), A.cts(), codes, scales, ng, buf, lane);
-      if (!DA::kWide || g0 + kGroup >= A.T) issue(A, sm, S, j + kBufs, lane, wave, buf);
+    out = down_compute<FP8>(w, sw, A.kts(), A.cts(), codes, scales, n, buf, lane);
+    issue(A, sm, S, j + kBufs, lane, wave, buf);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (4 * q + r < ng)
-          st_dev(&A.s_part[(size_t)(g0 + 4 * q + r) * A.h() + 16 * hs + m], tagged(tag, out[r]));
-    }
+    for (int r = 0; r < 4; ++r)
+      if (4 * q + r < n) st_dev(&A.s_part[(size_t)(g0 + 4 * q + r) * A.h() + 16 * hs + m], tagged(tag, out[r]));
   }
 }
 
@@ -1175,10 +1219,13 @@ __device__ __forceinline__ void decode_body(const DA& A, uint32_t tag, SmemOf<DA
 
   // units after the router's: MXFP8 shared gate/up strips, or the folded
   // shared expert's gate/up units (all rows select it)
-  const int n_ss = A.is() ? 2 * A.is() / 16 : (A.fd() ? A.i() / 16 : 0);
+  // (one unit per strip and 16-row group of x)
+  const int n_base = A.is() ? 2 * A.is() / 16 : (A.fd() ? A.i() / 16 : 0);
+  const int n_ss = n_base * (DA::kWide ? (T + kGroup - 1) / kGroup : 1);
   const bool early_x4 = T <= kEarlyQuantT;
   bool have_x4 = false;      // the MXFP4 copy of x in LDS holds the rows the units need
-  bool have_all_x4 = false;  // ... and it holds every row
+  bool have_all_x4 = false;  // ... and it holds every row, at its own position
+  int x4_group = -1;         // the 16-row group a folded expert's unit left in LDS
   for (int u = blockIdx.x; u < E + n_ss; u += G) {
     if (u < E) {
       unit_router(A, sm, tag, u, lane, wave);
@@ -1189,11 +1236,12 @@ __device__ __forceinline__ void decode_body(const DA& A, uint32_t tag, SmemOf<DA
         norm_setup(A, sm, gamma_lds, !have_r, lane, wave);
         have_norm = have_r = true;
       }
+      const int v = u - E, g0 = kGroup * (v / n_base);
       if (A.fd()) {
-        unit_fold_gu(A, tag, sm, gamma_lds, u - E, xq4_lds, xs4_lds, have_all_x4, lane, wave);
-        have_x4 = true;
+        unit_fold_gu(A, tag, sm, gamma_lds, v % n_base, g0, xq4_lds, xs4_lds, x4_group, lane, wave);
+        have_x4 = have_all_x4 = !DA::kWide;  // up to 16 rows: every row, at its own position
       } else {
-        unit_shared_strip(A, tag, sm, gamma_lds, u - E, x8_lds, xq4_lds, xs4_lds, lane, wave);
+        unit_shared_strip(A, tag, sm, gamma_lds, v % n_base, g0, x8_lds, xq4_lds, xs4_lds, lane, wave);
         have_x4 = early_x4;
       }
     }
@@ -1269,9 +1317,17 @@ __device__ __forceinline__ void decode_body(const DA& A, uint32_t tag, SmemOf<DA
   S.nhg = A.h() / 64;
   S.ns = A.is() ? S.nhg : 0;
   S.fold = A.fd();
+  int NQB = S.D - S.fold, NQC = S.D;  // expert(-group)s of phases B and C
+  if constexpr (DA::kWide) {
+    S.NQ = sm.NQ;
+    S.NQF = sm.NQF;
+    NQB = S.NQ - S.NQF;
+    NQC = S.NQ;
+    S.ns = A.is() ? S.nhg * ((T + kGroup - 1) / kGroup) : 0;
+  }
   {
-    const int NB = (S.D - S.fold) * (A.i() / 16);  // the folded expert's gate/up ran in phase A
-    const int NCU = S.ns + S.D * S.nhg;
+    const int NB = NQB * (A.i() / 16);  // the folded expert's gate/up ran in phase A
+    const int NCU = S.ns + NQC * S.nhg;
     const unsigned b = blockIdx.x, g = (unsigned)G;  // products stay below 2^24
     S.b0 = (int)((unsigned)NB * b / g);
     S.nb = (int)((unsigned)NB * (b + 1) / g) - S.b0;
@@ -1288,8 +1344,11 @@ __device__ __forceinline__ void decode_body(const DA& A, uint32_t tag, SmemOf<DA
   uint64_t need = 0;
   if (!early_x4 && !have_all_x4 && S.nb > 0) {
     const int per = A.i() / 16;
-    for (int dd = S.b0 / per; dd <= (S.b0 + S.nb - 1) / per; ++dd)
-      for (int s = 0; s < sm.ecount[dd]; ++s) need |= 1ull << (sm.slot(dd, s) / A.kk());
+    for (int u = S.b0 - S.b0 % per; u < S.b0 + S.nb; u += per) {  // each expert(-group) of the run
+      int dd, g0, i;
+      b_unit(A, sm, u, dd, g0, i);
+      for (int s = g0; s < min(sm.ecount[dd], g0 + kGroup); ++s) need |= 1ull << (sm.slot(dd, s) / A.kk());
+    }
   }
   if (need) {  // uniform
     if (threadIdx.x < DA::kMaxT && ((need >> threadIdx.x) & 1ull))

@@ -316,11 +316,15 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // write ids[j] and w[j].  Every lane must call it; k is uniform.
 __device__ __forceinline__ void row_topk64(const float* logits_row, bool active, int E, int k, int lane,
                                            int32_t* ids, float* w) {
+  // A key can be 0 (the logit with all bits set), so whether an expert is
+  // still in the running is kept apart from its key.
   uint32_t kv[4];
+  bool live[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int e = lane + 64 * r;
-    kv[r] = (active && e < E) ? logit_order_bits(logits_row[e]) : 0u;
+    live[r] = active && e < E;
+    kv[r] = live[r] ? logit_order_bits(logits_row[e]) : 0u;
   }
   float my_l = 0.f;
   int my_e = 0;
@@ -331,12 +335,15 @@ __device__ __forceinline__ void row_topk64(const float* logits_row, bool active,
       int best = -1;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const uint64_t bal = __ballot(kv[r] == m);
+        const uint64_t bal = __ballot(live[r] && kv[r] == m);
         if (best < 0 && bal != 0ull) best = 64 * r + (__ffsll((unsigned long long)bal) - 1);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (lane + 64 * r == best) kv[r] = 0u;
+        if (lane + 64 * r == best) {
+          kv[r] = 0u;
+          live[r] = false;
+        }
       if (lane == j) {
         my_l = logit_from_order_bits(m);
         my_e = best;
