@@ -139,11 +139,14 @@ constexpr int kTileRows = 16;
 constexpr int kTileExperts = 8;   // per wavefront
 constexpr int kTileVals = kTileRows * kTileExperts;
 
-__global__ void __launch_bounds__(kThreads, 2) router_logits_tiled_kernel(
-    const uint16_t* __restrict__ x, int T, int H, int E, const float* __restrict__ wr,
-    const float* __restrict__ bias, float* __restrict__ logits, int n_rblk, int n_eblk,
-    const float* __restrict__ gamma, float eps) {
-  __shared__ float rn[kTileRows];  // pre-router RMSNorm factors of the tile's rows (with gamma)
+// With the pre-router norm (kNorm) every x value becomes (x r) g first; that
+// instance has its own kernel, since the norm's registers would push the
+// plain one into scratch memory.
+template <bool kNorm>
+__device__ __forceinline__ void router_tiled_body(const uint16_t* __restrict__ x, int T, int H, int E,
+                                                  const float* __restrict__ wr, const float* __restrict__ bias,
+                                                  float* __restrict__ logits, int n_rblk, int n_eblk,
+                                                  const float* __restrict__ gamma, float eps, float* rn) {
   // workgroups are dealt to the 8 XCDs in turn; renumber so that each XCD
   // takes a contiguous run of tiles (the expert groups of one row block share
   // that XCD's L2)
@@ -153,7 +156,7 @@ __global__ void __launch_bounds__(kThreads, 2) router_logits_tiled_kernel(
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int t0 = (tile / n_eblk) * kTileRows;
   const int e0 = (tile % n_eblk) * (kTileExperts * kWaves) + wave * kTileExperts;
-  if (gamma) {
+  if constexpr (kNorm) {
     for (int r = wave; r < kTileRows; r += kWaves) {
       const float v = row_rms_inv(x + (size_t)min(t0 + r, T - 1) * H, H, eps, lane);
       if (lane == 0) rn[r] = v;
@@ -179,12 +182,12 @@ __global__ void __launch_bounds__(kThreads, 2) router_logits_tiled_kernel(
 #pragma unroll
     for (int e = 0; e < kTileExperts; ++e) wv[e] = *reinterpret_cast<const float4*>(wp[e] + h);
     float4 gv = make_float4(1.f, 1.f, 1.f, 1.f);
-    if (gamma) gv = *reinterpret_cast<const float4*>(gamma + h);
+    if constexpr (kNorm) gv = *reinterpret_cast<const float4*>(gamma + h);
 #pragma unroll
     for (int r = 0; r < kTileRows; ++r) {
       float x0 = bf16_to_f32(xv[r].x & 0xffffu), x1 = bf16_to_f32(xv[r].x >> 16);
       float x2 = bf16_to_f32(xv[r].y & 0xffffu), x3 = bf16_to_f32(xv[r].y >> 16);
-      if (gamma) {
+      if constexpr (kNorm) {
         const float rr = rn[r];
         x0 = (x0 * rr) * gv.x;
         x1 = (x1 * rr) * gv.y;
@@ -230,6 +233,20 @@ __global__ void __launch_bounds__(kThreads, 2) router_logits_tiled_kernel(
   }
 }
 
+__global__ void __launch_bounds__(kThreads, 2) router_logits_tiled_kernel(
+    const uint16_t* __restrict__ x, int T, int H, int E, const float* __restrict__ wr,
+    const float* __restrict__ bias, float* __restrict__ logits, int n_rblk, int n_eblk) {
+  router_tiled_body<false>(x, T, H, E, wr, bias, logits, n_rblk, n_eblk, nullptr, 0.f, nullptr);
+}
+
+__global__ void __launch_bounds__(kThreads, 1) router_logits_tiled_norm_kernel(
+    const uint16_t* __restrict__ x, int T, int H, int E, const float* __restrict__ wr,
+    const float* __restrict__ bias, float* __restrict__ logits, int n_rblk, int n_eblk,
+    const float* __restrict__ gamma, float eps) {
+  __shared__ float rn[kTileRows];  // pre-router RMSNorm factors of the tile's rows
+  router_tiled_body<true>(x, T, H, E, wr, bias, logits, n_rblk, n_eblk, gamma, eps, rn);
+}
+
 // Top k of each row of a logits matrix: 16 lanes per row.
 __global__ void __launch_bounds__(kThreads) topk_rows_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                              int32_t* __restrict__ ids_out,
@@ -256,8 +273,12 @@ hipError_t launch_router_topk(const moe_layer_t& L, const uint16_t* x, int T, fl
     const int n_rblk = (T + kTileRows - 1) / kTileRows;
     const int n_eblk = (E + kTileExperts * kWaves - 1) / (kTileExperts * kWaves);
     const unsigned grid = (unsigned)((n_rblk * n_eblk + 7) / 8 * 8);
-    hipLaunchKernelGGL(router_logits_tiled_kernel, dim3(grid), dim3(kThreads), 0, stream, x, T, H, E,
-                       L.router_w, L.router_bias, logits, n_rblk, n_eblk, L.norm_weight, L.norm_eps);
+    if (L.norm_weight)
+      hipLaunchKernelGGL(router_logits_tiled_norm_kernel, dim3(grid), dim3(kThreads), 0, stream, x, T, H, E,
+                         L.router_w, L.router_bias, logits, n_rblk, n_eblk, L.norm_weight, L.norm_eps);
+    else
+      hipLaunchKernelGGL(router_logits_tiled_kernel, dim3(grid), dim3(kThreads), 0, stream, x, T, H, E,
+                         L.router_w, L.router_bias, logits, n_rblk, n_eblk);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)((T + 15) / 16)), dim3(kThreads), 0, stream, logits, T, E,

@@ -1,7 +1,9 @@
 """Build-time properties the kernels rely on, checked with the compiler's
 resource report (no GPU needed): the persistent fused decode grid must have
 every workgroup resident at once, so no instance of its kernel may use
-scratch memory (a dispatch waiting for scratch can hold workgroups back)."""
+scratch memory (a dispatch waiting for scratch can hold workgroups back);
+and the grouped path's kernels keep their values in registers (a spill to
+scratch costs a memory round trip per reload)."""
 
 import os
 import re
@@ -16,15 +18,29 @@ pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.ex
                                 reason="hipcc not available")
 
 
-def test_fused_decode_kernel_uses_no_scratch(tmp_path):
-    src = os.path.join(build.CSRC, "decode.hip")
+def _resource_report(name, tmp_path):
+    src = os.path.join(build.CSRC, name)
     cmd = [build.hipcc()] + build._flags() + ["-x", "hip", f"--offload-arch={build.ARCH}", "-Xclang",
                                                "-target-feature", "-Xclang", "-packed-fp32-ops", "-c", src,
-                                               "-o", str(tmp_path / "d.o"), "-Rpass-analysis=kernel-resource-usage"]
+                                               "-o", str(tmp_path / "k.o"), "-Rpass-analysis=kernel-resource-usage"]
     out = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     assert out.returncode == 0, out.stderr[-2000:]
-    names = re.findall(r"Function Name: (\S*fused_decode_kernel\S*)", out.stderr)
+    names = re.findall(r"Function Name: (\S+)", out.stderr)
     scratch = [int(v) for v in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", out.stderr)]
+    assert len(scratch) == len(names)
+    return dict(zip(names, scratch))
+
+
+@pytest.mark.parametrize("name", ["router.hip", "grouped.hip", "quant.hip", "align_sort.hip"])
+def test_grouped_path_kernels_use_no_scratch(name, tmp_path):
+    report = _resource_report(name, tmp_path)
+    assert report and all(v == 0 for v in report.values()), report
+
+
+def test_fused_decode_kernel_uses_no_scratch(tmp_path):
+    report = _resource_report("decode.hip", tmp_path)
+    names = [n for n in report if "fused_decode_kernel" in n]
+    scratch = [report[n] for n in names]
     assert len(names) >= 3, "expected the MiniMax, folded MiniMax and run-time shape instances"
     assert len(scratch) == len(names)
     assert all(v == 0 for v in scratch), dict(zip(names, scratch))
