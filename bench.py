@@ -459,6 +459,7 @@ def main():
     if r16:
         out["rows16"] = {"us_per_launch": round(r16["us_launch"], 3),
                          "gbs": round(r16["gbs"], 1), "frac": round(r16["gbs"] / HBM_PEAK_GBS, 4),
+                         "traffic": load_traffic("decode16"),
                          "distinct_experts_mean": round(r16["distinct_experts_mean"], 2),
                          "us_isolated_mean": round(r16["us_isolated_mean"], 3),
                          "algorithmic_bytes_per_launch": int(r16["bytes_mean"]),
