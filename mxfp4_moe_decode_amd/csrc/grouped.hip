@@ -490,7 +490,7 @@ GCarve gcarve(const moe_layer_t& L, int T) {
   auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, 256); return at; };
   c.ids = take(S * 4);
   c.w = take(S * 4);
-  c.logits = router_tiled(T) ? take((size_t)T * E * 4) : 0;
+  c.logits = take((size_t)T * E * 4);
   c.sort_ws = take(align_sort_ws_bytes(T, (int)k, (int)E));
   c.sorted = take(rows * 4);
   c.bexp = take(c.nblk * 4);
@@ -561,7 +561,7 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
   float* d_part = reinterpret_cast<float*>(at(c.d_part));
   hipError_t err;
   if ((err = mark(0)) != hipSuccess) return err;
-  if ((err = launch_router_topk(L, x, T, router_tiled(T) ? reinterpret_cast<float*>(at(c.logits)) : nullptr, ids, w,
+  if ((err = launch_router_topk(L, x, T, reinterpret_cast<float*>(at(c.logits)), ids, w,
                                k, L.shared_folded ? L.num_experts : -1, stream)) != hipSuccess)
     return err;
   if ((err = mark(1)) != hipSuccess) return err;

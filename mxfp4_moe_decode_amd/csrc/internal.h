@@ -62,10 +62,8 @@ hipError_t launch_requant_nvfp4(const uint8_t* codes, const uint8_t* block_scale
 inline int layer_slots(const moe_layer_t& L) { return L.top_k + (L.shared_folded ? 1 : 0); }
 
 // ------------------------------------------------------------------ router
-// From this many rows on, a call that keeps the logits takes the tiled logits
-// kernel and a separate top-k pass (same arithmetic, identical results).
-constexpr int kRouterTiledMinT = 64;
-bool router_tiled(int T);
+// With a logits buffer the call takes the tiled logits kernel and a separate
+// top-k pass; without, the per-row kernel (same arithmetic, identical results).
 // ids / w rows are `ld` apart (>= k); with fold_e >= 0 entry k of every row
 // is set to (fold_e, 1.0): the folded shared expert's slot.
 hipError_t launch_router_topk(const moe_layer_t& L, const uint16_t* x, int T, float* logits,

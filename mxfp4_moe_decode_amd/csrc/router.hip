@@ -1,9 +1,10 @@
 // Router logits and top-k for any number of rows (used on its own and by the
-// grouped path).  For a few rows a workgroup takes a group of rows, keeps them
-// in LDS, computes the E logits of each row with the fixed-order dot product of
-// mx_device.h and then 16 lanes per row select the top k.  For many rows a
-// register-tiled kernel writes the logits with the same arithmetic and a second
-// pass selects the top k.
+// grouped path).  With a logits buffer, a register-tiled kernel spread over
+// row x expert tiles writes the logits with the fixed-order dot product of
+// mx_device.h and a second pass selects the top k.  Without one, a workgroup
+// takes up to 8 rows, keeps them in LDS, computes all E logits of each row
+// (a wavefront per expert) and selects the top k itself: one workgroup per 8
+// rows, so the tiled path is much faster at every row count.
 #include "internal.h"
 #include "mx_device.h"
 
@@ -264,12 +265,10 @@ __global__ void __launch_bounds__(kThreads) topk_rows_kernel(const float* __rest
 
 }  // namespace
 
-bool router_tiled(int T) { return T >= kRouterTiledMinT; }
-
 hipError_t launch_router_topk(const moe_layer_t& L, const uint16_t* x, int T, float* logits,
                               int32_t* ids, float* w, int ld, int fold_e, hipStream_t stream) {
   const int H = L.hidden, E = L.num_experts;
-  if (logits && router_tiled(T)) {
+  if (logits) {  // expert-parallel: tiles of rows x experts, then the top-k pass
     const int n_rblk = (T + kTileRows - 1) / kTileRows;
     const int n_eblk = (E + kTileExperts * kWaves - 1) / (kTileExperts * kWaves);
     const unsigned grid = (unsigned)((n_rblk * n_eblk + 7) / 8 * 8);

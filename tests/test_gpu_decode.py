@@ -231,10 +231,13 @@ def test_status_word_poisons_later_calls_until_reinitialized():
 
 
 def test_dispatch_sixteen_rows_fused_seventeen_grouped():
-    """The layer call for any T: up to 16 rows one fused launch, wider steps
-    the grouped path; each result equals the direct call of its path."""
+    """The layer call for any T with the pages' rule (fused_max_rows = 16): up
+    to 16 rows one fused launch, wider steps the grouped path; each result
+    equals the direct call of its path.  The default takes up to 64 rows
+    fused."""
     cfg, gl, _ = _layers("decode16")
-    fwd = binding.MoEForward(gl)
+    assert binding.MoEForward(gl).fused_max_rows == binding.WIDE_MAX_ROWS
+    fwd = binding.MoEForward(gl, fused_max_rows=16)
     x16 = synth.activations(cfg, T=16, index=31)
     x17 = synth.activations(cfg, T=17, index=32)
     y16 = fwd(_dev(x16))
