@@ -91,6 +91,15 @@ struct Geo {
   static_assert(TILES % WAVES == 0 && STRIPS % WAVES == 0, "work splits evenly over the wavefronts");
   // loads per wavefront per K-tile, for the wavefronts that move an A-scale piece and for the others
   static constexpr int CNT_A = TPW + 1 + B_SC, CNT_B = TPW + B_SC;
+  // Scale groups (K a multiple of 512): the ring's stages hold code blocks
+  // only, and the scales of four K-tiles at a time go into a two-slot ring of
+  // groups after it: A, [BM rows][16 bytes] (one 16-byte load per row, by
+  // wavefronts < A_SC); B, [STRIPS][64 lanes][4 bytes].
+  static constexpr int STAGE4 = TILES * 1024;
+  static constexpr int GSA = BM * 16;
+  static constexpr int GSTAGE = GSA + STRIPS * 256;
+  template <bool G4>
+  static constexpr int ring_bytes() { return G4 ? NS * STAGE4 + 2 * GSTAGE : NS * STAGE; }
 };
 
 __device__ __forceinline__ uint32_t row_move32(uint32_t v) {  // neighbour swap inside a quad
@@ -175,6 +184,48 @@ __device__ __forceinline__ void issue_ktile(const uint8_t* (&src)[Gm::TPW], cons
 #endif
 }
 
+// As issue_ktile with scale groups: the code blocks of K-tile kt into its ring
+// stage and, when kt opens a group of four (kt % 4 == 0), that group's scales
+// into group slot (kt / 4) % 2: 16 bytes of each row's A scales (the four
+// K-tiles' four bytes each) and the lane's B-scale word of each strip.
+template <class Gm>
+__device__ __forceinline__ void issue_ktile_g4(const uint8_t* (&src)[Gm::TPW], const int (&step)[Gm::TPW],
+                                               const uint8_t* as_src, const uint8_t* (&bs_src)[Gm::B_SC],
+                                               unsigned char* ring, int wave, int kt) {
+  unsigned char* st = ring + (kt % Gm::NS) * Gm::STAGE4;
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+  for (int i = 0; i < Gm::TPW; ++i)
+    __builtin_amdgcn_global_load_lds(src[i] + (size_t)kt * step[i], st + (wave + Gm::WAVES * i) * 1024, 16, 0, 0);
+  if ((kt & 3) == 0) {
+    unsigned char* gs = ring + Gm::NS * Gm::STAGE4 + ((kt >> 2) & 1) * Gm::GSTAGE;
+    if (wave < Gm::A_SC) __builtin_amdgcn_global_load_lds(as_src + 4 * kt, gs + wave * 1024, 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < Gm::B_SC; ++i)
+      __builtin_amdgcn_global_load_lds(bs_src[i] + (size_t)(kt >> 2) * 256, gs + Gm::GSA + (wave + Gm::WAVES * i) * 256,
+                                       4, 0, 0);
+  }
+#endif
+}
+
+// s_waitcnt until only the loads of K-tiles kt+1 .. kt+ahead are pending, with
+// scale groups: each K-tile brings TPW code-block loads, and the one opening a
+// group SC more (at most one of up to three consecutive K-tiles does).
+template <int TPW, int SC>
+__device__ __forceinline__ void wait_ktiles_g4(int ahead, int kt) {
+  const int ph = kt & 3;  // K-tile kt + 4 - ph opens the next group
+  const bool extra = ahead >= 4 - ph;
+  switch (2 * ahead + (extra ? 1 : 0)) {
+    case 0: case 1: wait_vm<0>(); break;
+    case 2: wait_vm<TPW>(); break;
+    case 3: wait_vm<TPW + SC>(); break;
+    case 4: wait_vm<2 * TPW>(); break;
+    case 5: wait_vm<2 * TPW + SC>(); break;
+    case 6: wait_vm<3 * TPW>(); break;
+    default: wait_vm<3 * TPW + SC>(); break;
+  }
+}
+
 // s_waitcnt until at most `ahead` K-tiles of this wavefront's loads are pending.
 template <int CNT>
 __device__ __forceinline__ void wait_ktiles(int ahead) {
@@ -192,7 +243,7 @@ __device__ __forceinline__ void wait_ktiles(int ahead) {
 // 1 KiB blocks and its share of the K-tile's block scales (4-byte direct
 // loads of the activation scales, the weight-scale words of the K-tile's
 // group of four).
-template <class F, int MODE, int WN>
+template <class F, int MODE, int WN, bool G4>
 __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  // 2 x WN wavefronts
   using Gm = Geo<F, WN>;
   constexpr int MF = Gm::MF, BM = Gm::BM, R = Gm::R, TPW = Gm::TPW, NS = Gm::NS;
@@ -202,23 +253,27 @@ __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  /
   extern __shared__ __align__(16) unsigned char smem[];
 
   // XCD-aware order: consecutive workgroup ids go to different XCDs, so XCD x
-  // is given the contiguous run of tiles x*G/8 .. (x+1)*G/8 (G % 8 == 0).
-  const int G = gridDim.x, L = blockIdx.x;
-  const int tile = (L & 7) * (G >> 3) + (L >> 3);
+  // is given the contiguous run of tiles x*per .. (x+1)*per - 1.  The grid is
+  // sized for the largest padded row count; the live tile count is read here,
+  // so the tiles past the sorted rows' end are spread over every XCD instead
+  // of all falling into the last ones' runs (which would leave those idle).
+  const int L = blockIdx.x;
+  int ntiles = g.MB * g.NT;
+  if constexpr (kRouted) ntiles = min(ntiles, (*g.num_padded + BM - 1) / BM * g.NT);
+  const int per = (ntiles + 7) >> 3;  // tiles per XCD; gridDim.x / 8 >= per
+  if ((L >> 3) >= per) return;
+  const int tile = (L & 7) * per + (L >> 3);
+  if (tile >= ntiles) return;
   const int mb = tile / g.NT, nt = tile % g.NT;
-  if (mb >= g.MB) return;
   int e = 0;
-  if constexpr (kRouted) {
-    if (mb * BM >= *g.num_padded) return;
-    e = g.block_expert[mb];
-  }
+  if constexpr (kRouted) e = g.block_expert[mb];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / WN, wn = wave % WN;
   const int m = lane & 15, q = lane >> 4;
   const int S = g.T * g.k;
   const int KT = g.KT, KG = g.KG;
 
   unsigned char* ring = smem;
-  int32_t* slots = reinterpret_cast<int32_t*>(smem + NS * Gm::STAGE);
+  int32_t* slots = reinterpret_cast<int32_t*>(smem + Gm::template ring_bytes<G4>());
 
   if (threadIdx.x < BM) {
     const int r = mb * BM + (int)threadIdx.x;
@@ -261,17 +316,30 @@ __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  /
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = sum[i][j] = v4f{-0.f, -0.f, -0.f, -0.f};
 
+  auto issue = [&](int kt) {
+    if constexpr (G4)
+      issue_ktile_g4<Gm>(src, step, as_src, bs_src, ring, wave, kt);
+    else
+      issue_ktile<Gm>(src, step, as_src, bs_src, ring, wave, kt);
+  };
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; ++s0)
-    if (s0 < KT) issue_ktile<Gm>(src, step, as_src, bs_src, ring, wave, s0);
+    if (s0 < KT) issue(s0);
   for (int kt = 0, t_in = 0; kt < KT; ++kt) {
     // K-tile kt has landed once only the K-tiles issued after it are pending
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     const int ahead = min(NS - 2, KT - 1 - kt);  // K-tiles issued after kt
-    if (wave < Gm::A_SC)
-      wait_ktiles<Gm::CNT_A>(ahead);
-    else
-      wait_ktiles<Gm::CNT_B>(ahead);
+    if constexpr (G4) {
+      if (wave < Gm::A_SC)
+        wait_ktiles_g4<TPW, 1 + Gm::B_SC>(ahead, kt);
+      else
+        wait_ktiles_g4<TPW, Gm::B_SC>(ahead, kt);
+    } else {
+      if (wave < Gm::A_SC)
+        wait_ktiles<Gm::CNT_A>(ahead);
+      else
+        wait_ktiles<Gm::CNT_B>(ahead);
+    }
     // Each wavefront's own loads of K-tile kt are in LDS (the wait above); the
     // barrier makes that hold for all of them.  It is a bare s_barrier: the
     // workgroup fence of __syncthreads() would wait for every direct-to-LDS
@@ -283,8 +351,11 @@ __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  /
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (kt + NS - 1 < KT) issue_ktile<Gm>(src, step, as_src, bs_src, ring, wave, kt + NS - 1);
-    const unsigned char* st = ring + (kt % NS) * Gm::STAGE;
+    if (kt + NS - 1 < KT) issue(kt + NS - 1);
+    const unsigned char* st = ring + (kt % NS) * (G4 ? Gm::STAGE4 : Gm::STAGE);
+    // scales of K-tile kt: its group slot (G4), or its stage
+    const unsigned char* sc_a = G4 ? ring + NS * Gm::STAGE4 + ((kt >> 2) & 1) * Gm::GSTAGE : st + Gm::A_SC_OFF;
+    const uint32_t* sc_b = reinterpret_cast<const uint32_t*>(G4 ? sc_a + Gm::GSA : st + Gm::B_SC_OFF);
     v4i a[MF][R], b[4][R];
     uint32_t sa[MF], sb[4];
 #pragma unroll
@@ -292,7 +363,7 @@ __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  /
       const int f = wm * MF + i;
 #pragma unroll
       for (int r = 0; r < R; ++r) a[i][r] = *reinterpret_cast<const v4i*>(st + (f * R + r) * 1024 + lane * 16);
-      sa[i] = st[Gm::A_SC_OFF + (16 * f + m) * 4 + q];
+      sa[i] = G4 ? sc_a[(16 * f + m) * 16 + 4 * (kt & 3) + q] : sc_a[(16 * f + m) * 4 + q];
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -300,7 +371,7 @@ __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  /
 #pragma unroll
       for (int r = 0; r < R; ++r)
         b[j][r] = *reinterpret_cast<const v4i*>(st + (Gm::A_TILES + s * R + r) * 1024 + lane * 16);
-      sb[j] = (reinterpret_cast<const uint32_t*>(st + Gm::B_SC_OFF)[s * 64 + lane] >> (8 * (kt & 3))) & 0xffu;
+      sb[j] = (sc_b[s * 64 + lane] >> (8 * (kt & 3))) & 0xffu;
     }
     if (t_in == 0)
       mma_tile<F, MF, R>(a, b, sa, sb, true, acc);
@@ -372,7 +443,7 @@ __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  /
     // four floats against bank conflicts), columns 16 STRIPS nt onwards
     constexpr int CW = 16 * STRIPS;
     constexpr int LD = CW + 4;
-    static_assert(BM * LD * 4 <= NS * Gm::STAGE, "the output tile fits the ring");
+    static_assert(BM * LD * 4 <= Gm::template ring_bytes<G4>(), "the output tile fits the ring");
     float* tf = reinterpret_cast<float*>(ring);
     __syncthreads();  // every wavefront is done reading the ring
 #pragma unroll
@@ -512,10 +583,10 @@ GCarve gcarve(const moe_layer_t& L, int T) {
 
 unsigned grid8(int tiles) { return (unsigned)((tiles + 7) / 8 * 8); }
 
-template <class F, int MODE, int WN>
-hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
+template <class F, int MODE, int WN, bool G4>
+hipError_t launch_gemm_as(const GemmArgs& g, hipStream_t stream) {
   using Gm = Geo<F, WN>;
-  const size_t lds = (size_t)Gm::NS * Gm::STAGE + (size_t)Gm::BM * 4;
+  const size_t lds = (size_t)Gm::template ring_bytes<G4>() + (size_t)Gm::BM * 4;
   // the kernel's dynamic LDS limit is raised once per device (a lock-free
   // flag per device; racing first calls both set the same attribute)
   static std::atomic<bool> lds_set[kMaxDevices];
@@ -523,15 +594,23 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
     const int dev = current_device();
     if (dev < 0) return hipErrorInvalidDevice;
     if (!lds_set[dev].load(std::memory_order_relaxed)) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_kernel<F, MODE, WN>),
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_kernel<F, MODE, WN, G4>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return hipErrorInvalidValue;
       lds_set[dev].store(true, std::memory_order_relaxed);
     }
   }
-  hipLaunchKernelGGL((grouped_gemm_kernel<F, MODE, WN>), dim3(grid8(g.MB * g.NT)), dim3(Gm::THREADS), lds, stream,
+  hipLaunchKernelGGL((grouped_gemm_kernel<F, MODE, WN, G4>), dim3(grid8(g.MB * g.NT)), dim3(Gm::THREADS), lds, stream,
                      g);
   return hipGetLastError();
+}
+
+// Scale groups need whole groups of four K-tiles and 16-byte aligned rows of
+// A scales (K a multiple of 512); other shapes load the scales per K-tile.
+template <class F, int MODE, int WN>
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
+  const bool g4 = g.KT % 4 == 0 && g.as_stride % 16 == 0 && reinterpret_cast<uintptr_t>(g.as) % 16 == 0;
+  return g4 ? launch_gemm_as<F, MODE, WN, true>(g, stream) : launch_gemm_as<F, MODE, WN, false>(g, stream);
 }
 
 }  // namespace
