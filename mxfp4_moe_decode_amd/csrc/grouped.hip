@@ -162,6 +162,24 @@ __device__ __forceinline__ int w_strip(const GemmArgs& g, int nt, int s) {
   return 4 * WN * nt + s;
 }
 
+// Direct global -> LDS load of BYTES (4 or 16) per lane: lane l's bytes land
+// at lds + l * BYTES (M0 holds the wavefront's LDS address).  Written as asm
+// so that the compiler does not see it: it would otherwise order every LDS
+// read of the kernel behind all direct loads in flight (a full lgkmcnt
+// drain before each matrix instruction), although their completion is
+// counted by vmcnt alone.  The kernel waits for them with explicit vmcnt
+// waits; the load has no register result.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const void* src, unsigned char* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the asm is device code only
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
+  if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+#endif
+}
+
 // Direct global -> LDS loads of this wavefront's share of K-tile kt into its
 // ring slot: code blocks t = wave + WAVES i (1 KiB each, lane l's 16 bytes at
 // l*16), one 256-byte piece of the rows' A scales (wavefronts < A_SC: lane l
@@ -175,12 +193,11 @@ __device__ __forceinline__ void issue_ktile(const uint8_t* (&src)[Gm::TPW], cons
 #if defined(__HIP_DEVICE_COMPILE__)  // the builtin only type-checks in the device pass
 #pragma unroll
   for (int i = 0; i < Gm::TPW; ++i)
-    __builtin_amdgcn_global_load_lds(src[i] + (size_t)kt * step[i], st + (wave + Gm::WAVES * i) * 1024, 16, 0, 0);
-  if (wave < Gm::A_SC) __builtin_amdgcn_global_load_lds(as_src + 4 * kt, st + Gm::A_SC_OFF + wave * 256, 4, 0, 0);
+    lds_dma<16>(src[i] + (size_t)kt * step[i], st + (wave + Gm::WAVES * i) * 1024);
+  if (wave < Gm::A_SC) lds_dma<4>(as_src + 4 * kt, st + Gm::A_SC_OFF + wave * 256);
 #pragma unroll
   for (int i = 0; i < Gm::B_SC; ++i)
-    __builtin_amdgcn_global_load_lds(bs_src[i] + (size_t)(kt >> 2) * 256, st + Gm::B_SC_OFF + (wave + Gm::WAVES * i) * 256,
-                                     4, 0, 0);
+    lds_dma<4>(bs_src[i] + (size_t)(kt >> 2) * 256, st + Gm::B_SC_OFF + (wave + Gm::WAVES * i) * 256);
 #endif
 }
 
@@ -196,14 +213,12 @@ __device__ __forceinline__ void issue_ktile_g4(const uint8_t* (&src)[Gm::TPW], c
 #if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
   for (int i = 0; i < Gm::TPW; ++i)
-    __builtin_amdgcn_global_load_lds(src[i] + (size_t)kt * step[i], st + (wave + Gm::WAVES * i) * 1024, 16, 0, 0);
+    lds_dma<16>(src[i] + (size_t)kt * step[i], st + (wave + Gm::WAVES * i) * 1024);
   if ((kt & 3) == 0) {
     unsigned char* gs = ring + Gm::NS * Gm::STAGE4 + ((kt >> 2) & 1) * Gm::GSTAGE;
-    if (wave < Gm::A_SC) __builtin_amdgcn_global_load_lds(as_src + 4 * kt, gs + wave * 1024, 16, 0, 0);
+    if (wave < Gm::A_SC) lds_dma<16>(as_src + 4 * kt, gs + wave * 1024);
 #pragma unroll
-    for (int i = 0; i < Gm::B_SC; ++i)
-      __builtin_amdgcn_global_load_lds(bs_src[i] + (size_t)(kt >> 2) * 256, gs + Gm::GSA + (wave + Gm::WAVES * i) * 256,
-                                       4, 0, 0);
+    for (int i = 0; i < Gm::B_SC; ++i) lds_dma<4>(bs_src[i] + (size_t)(kt >> 2) * 256, gs + Gm::GSA + (wave + Gm::WAVES * i) * 256);
   }
 #endif
 }
@@ -357,12 +372,15 @@ __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  /
     const unsigned char* sc_a = G4 ? ring + NS * Gm::STAGE4 + ((kt >> 2) & 1) * Gm::GSTAGE : st + Gm::A_SC_OFF;
     const uint32_t* sc_b = reinterpret_cast<const uint32_t*>(G4 ? sc_a + Gm::GSA : st + Gm::B_SC_OFF);
     v4i a[MF][R], b[4][R];
-    uint32_t sa[MF], sb[4];
+    uint32_t sa[MF], sb[4], sbw[4];
+    // LDS reads in the order the matrix instructions consume them: scales,
+    // the B strips, then A fragment by fragment, so that the instructions of
+    // fragment i wait only for the reads up to a[i]
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sbw[j] = sc_b[(4 * wn + j) * 64 + lane];
 #pragma unroll
     for (int i = 0; i < MF; ++i) {
       const int f = wm * MF + i;
-#pragma unroll
-      for (int r = 0; r < R; ++r) a[i][r] = *reinterpret_cast<const v4i*>(st + (f * R + r) * 1024 + lane * 16);
       sa[i] = G4 ? sc_a[(16 * f + m) * 16 + 4 * (kt & 3) + q] : sc_a[(16 * f + m) * 4 + q];
     }
 #pragma unroll
@@ -371,8 +389,16 @@ __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  /
 #pragma unroll
       for (int r = 0; r < R; ++r)
         b[j][r] = *reinterpret_cast<const v4i*>(st + (Gm::A_TILES + s * R + r) * 1024 + lane * 16);
-      sb[j] = (sc_b[s * 64 + lane] >> (8 * (kt & 3))) & 0xffu;
     }
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      const int f = wm * MF + i;
+#pragma unroll
+      for (int r = 0; r < R; ++r) a[i][r] = *reinterpret_cast<const v4i*>(st + (f * R + r) * 1024 + lane * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sb[j] = (sbw[j] >> (8 * (kt & 3))) & 0xffu;
     if (t_in == 0)
       mma_tile<F, MF, R>(a, b, sa, sb, true, acc);
     else
