@@ -89,6 +89,7 @@ struct Geo {
   static constexpr int B_SC_OFF = A_SC_OFF + BM * 4;
   static constexpr int STAGE = B_SC_OFF + STRIPS * 256;
   static_assert(TILES % WAVES == 0 && STRIPS % WAVES == 0, "work splits evenly over the wavefronts");
+  static_assert(NS >= 2 && NS <= 5, "the waits count at most three K-tiles in flight behind the current one");
   // loads per wavefront per K-tile, for the wavefronts that move an A-scale piece and for the others
   static constexpr int CNT_A = TPW + 1 + B_SC, CNT_B = TPW + B_SC;
   // Scale groups (K a multiple of 512): the ring's stages hold code blocks
@@ -436,17 +437,19 @@ __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  /
         const uint32_t am = row16_max32(max(a0 & 0x7fffffffu, a1 & 0x7fffffffu));
         const int ex = block_exponent<F>(am);
         const float inv = block_inv_scale(ex);
-        const uint32_t c0 = quant_elem_fast<F>(a0, inv), c1 = quant_elem_fast<F>(a1, inv);
         uint8_t* op = tc + rl * RB + BPB * wn;
         if constexpr (F::MB == 1) {
-          const uint32_t n0 = row_move32(c0), n1 = row_move32(c1);
+          // even lanes pack columns m, m + 1 (the neighbour's value) into one
+          // byte, low nibble first; the codes are those of quant_quad_fp4
+          const uint32_t w = quant_quad_fp4(a0, row_move32(a0), a1, row_move32(a1), inv);
           if (!(m & 1)) {
-            op[m / 2] = (uint8_t)((c0 & 0xfu) | ((n0 & 0xfu) << 4));
-            op[8 + m / 2] = (uint8_t)((c1 & 0xfu) | ((n1 & 0xfu) << 4));
+            op[m / 2] = (uint8_t)w;
+            op[8 + m / 2] = (uint8_t)(w >> 8);
           }
         } else {
-          op[m] = (uint8_t)c0;
-          op[16 + m] = (uint8_t)c1;
+          const uint32_t w = quant_pair_fp8(a0, a1, inv);
+          op[m] = (uint8_t)w;
+          op[16 + m] = (uint8_t)(w >> 8);
         }
         if (m == 0) ts[rl * WN + wn] = (uint8_t)(ex + 127);
       }

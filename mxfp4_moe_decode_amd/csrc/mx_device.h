@@ -36,40 +36,6 @@ __device__ __forceinline__ int block_exponent(uint32_t amax_bits) {
 // 2^-e as an fp32 value (e = block exponent, -127 <= e <= 126).
 __device__ __forceinline__ float block_inv_scale(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
 
-// Element code of v * 2^-e (v an fp32 bit pattern, inv = block_inv_scale(e)):
-// round to nearest, ties to the even code, saturate to MAXC, sign bit copied
-// (also onto a zero code), with no branches.  q = |v| * 2^-e is exact whenever it is an fp32 normal (a power of
-// two scaling), and when it is not, q < 2^-126 lies far below the first
-// rounding threshold, so the code is 0 either way; q never overflows since
-// |v| <= amax < 2^(e + EMAX + 1).
-//   FP4 (E2M1, magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6): the code counts the
-//   midpoints q has passed; at a midpoint the comparison is strict where the
-//   lower neighbour's code is even and inclusive where the upper one's is, so
-//   ties go to the even code; above 5 (the last midpoint) it is 7, which also
-//   saturates.
-//   FP8 (E4M3): below 2^-6 the code is the subnormal count RNE(q * 2^9),
-//   rounded by adding and removing 2^23 in fp32 (round to nearest even); from
-//   2^-6 up, q's fp32 pattern rounded to 3 mantissa bits (ties to even, a
-//   carry moving into the exponent), re-biased from 127 to 7, saturated at
-//   0x7E (448).
-template <class F>
-__device__ __forceinline__ uint32_t quant_elem_fast(uint32_t bits, float inv) {
-  const uint32_t sign = bits >> 31;
-  const float q = __uint_as_float(bits & 0x7fffffffu) * inv;
-  uint32_t code;
-  if constexpr (F::MB == 1) {
-    code = (uint32_t)(q > 0.25f) + (uint32_t)(q >= 0.75f) + (uint32_t)(q > 1.25f) + (uint32_t)(q >= 1.75f) +
-           (uint32_t)(q > 2.5f) + (uint32_t)(q >= 3.5f) + (uint32_t)(q > 5.0f);
-  } else {
-    const uint32_t sub = (uint32_t)((q * 512.0f + 8388608.0f) - 8388608.0f);
-    const uint32_t b = __float_as_uint(q);
-    uint32_t nrm = ((b + 0x7ffffu + ((b >> 20) & 1u)) >> 20) - (120u << 3);
-    nrm = nrm > (uint32_t)F::MAXC ? (uint32_t)F::MAXC : nrm;
-    code = q < 0.015625f ? sub : nrm;
-  }
-  return code | (sign << F::SIGN);
-}
-
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
 // fp32 -> bf16 round to nearest even (finite inputs).
