@@ -198,13 +198,13 @@ __device__ __forceinline__ void compiler_fence() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_sched_barrier(0);
 }
+
 // s_waitcnt vmcnt(n), expcnt and lgkmcnt left alone (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
-__device__ __forceinline__ float silu_mul(float g, float u) { return (g / (1.f + expf(-g))) * u; }
 
 __device__ __forceinline__ uint64_t tagged_u(uint32_t tag, uint32_t v) { return ((uint64_t)tag << 32) | v; }
 __device__ __forceinline__ uint64_t tagged(uint32_t tag, float v) { return tagged_u(tag, __float_as_uint(v)); }

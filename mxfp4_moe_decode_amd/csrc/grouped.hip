@@ -114,8 +114,6 @@ __device__ __forceinline__ uint32_t row16_max32(uint32_t v) {
   return v;
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return (g / (1.f + expf(-g))) * u; }
-
 // s_waitcnt vmcnt(N), other counters left alone (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vm() {

@@ -36,6 +36,17 @@ __device__ __forceinline__ int block_exponent(uint32_t amax_bits) {
 // 2^-e as an fp32 value (e = block exponent, -127 <= e <= 126).
 __device__ __forceinline__ float block_inv_scale(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
 
+// SwiGLU: silu(g) * u = g / (1 + e^-g) * u, with the hardware base-2
+// exponential and reciprocal: g * rcp(1 + 2^(-g log2 e)) * u.  Relative error
+// against the exact value, to first order in u = 2^-24: the exponent -g log2 e
+// carries two roundings (the constant and the product), which move 2^t by at
+// most 2|g| u; the exponential and the reciprocal are within one ulp (2u) each;
+// the sum and the two products round once each: (2|g| + 7) u.  Overflow of the
+// exponential (g < -88) gives 0 where the exact value is below 2^-120.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return (g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-g * 1.44269504f))) * u;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
 // fp32 -> bf16 round to nearest even (finite inputs).

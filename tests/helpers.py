@@ -230,7 +230,9 @@ def ffn_deviation(info, fmt, x_rel=0.0):
     """Bound on |d_gpu - d_oracle| [n, H] for one SwiGLU FFN of the oracle
     (``info`` from oracle.moe.mx_ffn): with ``x_rel`` > 0 (the GPU's x has
     that relative error), the MX codes of x that can differ; fp32 rounding of
-    the gate/up sums, of SwiGLU (expf, division, product: 10 roundings) and
+    the gate/up sums, of SwiGLU (the hardware exp2 and reciprocal, one ulp
+    each, after an exponent -g log2 e rounded twice: (2|g| + 7) u relative,
+    taken as (2|g| + 16) u, plus 2^-120 where the exponential overflows) and
     the oracle's own fp32 roundings of g, u, a, then the re-quantization steps
     that can follow, then the down product's rounding."""
     xq, w13, g, u, a, aq, w2 = (info[k] for k in ("xq", "w13", "g", "u", "a", "aq", "w2"))
@@ -246,7 +248,8 @@ def ffn_deviation(info, fmt, x_rel=0.0):
     dg = gamma(gemm_roundings(H)) * s13[:, :I] + e13[:, :I] + 2 * U32 * np.abs(g)
     du = gamma(gemm_roundings(H)) * s13[:, I:] + e13[:, I:] + 2 * U32 * np.abs(u)
     sil = g / (1.0 + np.exp(-g))
-    da = SILU_SLOPE * np.abs(u) * dg + np.abs(sil) * du + SILU_SLOPE * dg * du + 10 * U32 * np.abs(a)
+    da = (SILU_SLOPE * np.abs(u) * dg + np.abs(sil) * du + SILU_SLOPE * dg * du
+          + (2 * np.abs(g) + 16) * U32 * np.abs(a) + 2.0 ** -120)
     daq = requant_deviation(a, da, fmt)
     w2a = np.abs(w2)
     return daq @ w2a.T + gamma(gemm_roundings(I)) * ((np.abs(aq) + daq) @ w2a.T)
