@@ -1420,31 +1420,40 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
     poison_output(A);
 
   // exit: the last workgroup to finish advances the epoch (the next call's
-  // tag is one more) and resets the arrival counter
+  // tag is one more) and resets the arrival counter.  Tags are unique per
+  // call, so neither needs this call's stores to have landed first: the next
+  // call starts only after they all have.  The call whose tag is the last
+  // 32-bit value (once in 2^32 calls) is the exception, below.
+  const bool wrap = tag == 0xffffffffu;  // uniform
   __syncthreads();
   if (threadIdx.x == 0) {
     tr[TR_C] = wall_clock64();
     if (blockIdx.x == 0) st_dev(ctr(A.sync, S_GRID), (uint32_t)G);
     compiler_fence();
-    wait_vm<0>();
+    if (wrap) wait_vm<0>();
     const uint32_t old = __hip_atomic_fetch_add(ctr(A.sync, S_DONE), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     compiler_fence();
-    sm.last = old + 1 == (uint32_t)G;
+    const bool last = old + 1 == (uint32_t)G;
+    if (last && !wrap) {
+      st_dev(ctr(A.sync, S_EPOCH), tag);
+      st_dev(ctr(A.sync, S_DONE), 0u);
+    }
+    sm.last = last;
   }
+  if (!wrap) return;  // uniform
   __syncthreads();
   if (sm.last) {  // uniform
     // After 2^32 - 1 calls the tag would wrap to 0, the tag of zero-filled
     // words, and later tags would match words written 2^32 calls earlier.
-    // Instead every tagged word is cleared and the epoch restarts at 0.
-    const bool wrap = tag == 0xffffffffu;
-    if (wrap) {
-      for (uint32_t i = threadIdx.x; i < A.n_tagged; i += kThreads) st_dev(&A.tagged[i], (uint64_t)0);
-      compiler_fence();
-      wait_vm<0>();
-      __syncthreads();
-    }
+    // Instead every tagged word is cleared, once every workgroup's stores
+    // have landed (each waited for its own before counting itself in), and
+    // the epoch restarts at 0.
+    for (uint32_t i = threadIdx.x; i < A.n_tagged; i += kThreads) st_dev(&A.tagged[i], (uint64_t)0);
+    compiler_fence();
+    wait_vm<0>();
+    __syncthreads();
     if (threadIdx.x == 0) {
-      st_dev(ctr(A.sync, S_EPOCH), wrap ? 0u : tag);
+      st_dev(ctr(A.sync, S_EPOCH), 0u);
       compiler_fence();
       wait_vm<0>();
       st_dev(ctr(A.sync, S_DONE), 0u);
