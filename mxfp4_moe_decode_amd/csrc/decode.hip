@@ -618,6 +618,24 @@ template <class DA>
 __device__ __forceinline__ void build_expert_list(const DA& A, SmemOf<DA>& sm, int lane, int wave) {
   static_assert(DA::kMaxT <= 64, "one mask bit per row");
   const int S = A.T * A.kk(), tid = threadIdx.x;
+  if (!DA::kWide && A.T == 1) {
+    // One row: its kk experts are distinct, so an expert's place in the list
+    // is its rank among them and its slot list is its own slot (the lists
+    // below come out the same).
+    const int kk = A.kk();
+    if (tid < kk) {
+      const int e = sm.ids[tid];
+      int dd = 0;
+      for (int j = 0; j < kk; ++j) dd += sm.ids[j] < e ? 1 : 0;
+      sm.elist[dd] = (uint8_t)e;
+      sm.ecount[dd] = 1;
+      sm.eoff[dd] = (uint16_t)dd;
+      sm.slist[dd] = (uint16_t)tid;
+    }
+    if (tid == 0) sm.D = kk;
+    __syncthreads();
+    return;
+  }
   sm.rmask[tid] = 0ull;
   __syncthreads();
   for (int sl = tid; sl < S; sl += kThreads) atomicOr(&sm.rmask[sm.ids[sl]], 1ull << (sl / A.kk()));
