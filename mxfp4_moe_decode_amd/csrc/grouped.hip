@@ -31,6 +31,7 @@
 // numbered so that each XCD receives a contiguous run of tiles: the tiles of
 // one expert's blocks then share that XCD's L2.
 #include <atomic>
+#include <type_traits>
 
 #include "internal.h"
 #include "mx_device.h"
@@ -240,6 +241,50 @@ __device__ __forceinline__ void wait_ktiles_g4(int ahead, int kt) {
   }
 }
 
+// f(std::integral_constant<int, I>{}) for I = B .. E - 1, in order.
+template <int B, int E, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// One K-tile of FP4 products with the B scales taken as byte OPB of each
+// strip's scale word (the word holds the scales of four K-tiles); the first
+// tile of a chunk starts its chain from zero.
+template <int MF, int OPB>
+__device__ __forceinline__ void mma_tile_fp4_sel(const v4i (&a)[MF][1], const v4i (&b)[4][1], const uint32_t (&sa)[MF],
+                                                 const uint32_t (&sbw)[4], bool first, v4f (&acc)[MF][4]) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v8i A = {a[i][0][0], a[i][0][1], a[i][0][2], a[i][0][3], 0, 0, 0, 0};
+      const v8i B = {b[j][0][0], b[j][0][1], b[j][0][2], b[j][0][3], 0, 0, 0, 0};
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, first ? zero : acc[i][j], 4, 4, 0, (int)sa[i],
+                                                                    OPB, (int)sbw[j]);
+    }
+}
+
+// issue_ktile_g4 with the ring stage and whether kt opens a scale group known
+// at compile time.
+template <class Gm, int STAGE_I, bool OPEN>
+__device__ __forceinline__ void issue_ktile_g4c(const uint8_t* (&src)[Gm::TPW], const int (&step)[Gm::TPW],
+                                                const uint8_t* as_src, const uint8_t* (&bs_src)[Gm::B_SC],
+                                                unsigned char* ring, int wave, int kt) {
+  unsigned char* st = ring + STAGE_I * Gm::STAGE4;
+#pragma unroll
+  for (int i = 0; i < Gm::TPW; ++i) lds_dma<16>(src[i] + (size_t)kt * step[i], st + (wave + Gm::WAVES * i) * 1024);
+  if constexpr (OPEN) {
+    unsigned char* gs = ring + Gm::NS * Gm::STAGE4 + ((kt >> 2) & 1) * Gm::GSTAGE;
+    if (wave < Gm::A_SC) lds_dma<16>(as_src + 4 * kt, gs + wave * 1024);
+#pragma unroll
+    for (int i = 0; i < Gm::B_SC; ++i) lds_dma<4>(bs_src[i] + (size_t)(kt >> 2) * 256, gs + Gm::GSA + (wave + Gm::WAVES * i) * 256);
+  }
+}
+
 // s_waitcnt until at most `ahead` K-tiles of this wavefront's loads are pending.
 template <int CNT>
 __device__ __forceinline__ void wait_ktiles(int ahead) {
@@ -256,9 +301,11 @@ __device__ __forceinline__ void wait_ktiles(int ahead) {
 // ahead of the matrix instructions; each wavefront moves TPW of the tile's
 // 1 KiB blocks and its share of the K-tile's block scales (4-byte direct
 // loads of the activation scales, the weight-scale words of the K-tile's
-// group of four).
+// group of four).  Two workgroups share a CU (LDS), so the registers are held
+// to two wavefronts per SIMD (256 per lane, accumulators included).
 template <class F, int MODE, int WN, bool G4>
-__global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  // 2 x WN wavefronts
+__global__ void __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(2)))
+grouped_gemm_kernel(GemmArgs g) {  // 2 x WN wavefronts
   using Gm = Geo<F, WN>;
   constexpr int MF = Gm::MF, BM = Gm::BM, R = Gm::R, TPW = Gm::TPW, NS = Gm::NS;
   constexpr int WAVES = Gm::WAVES, THREADS = Gm::THREADS, STRIPS = Gm::STRIPS;
@@ -339,75 +386,146 @@ __global__ void __launch_bounds__(128 * WN) grouped_gemm_kernel(GemmArgs g) {  /
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; ++s0)
     if (s0 < KT) issue(s0);
-  for (int kt = 0, t_in = 0; kt < KT; ++kt) {
-    // K-tile kt has landed once only the K-tiles issued after it are pending
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    const int ahead = min(NS - 2, KT - 1 - kt);  // K-tiles issued after kt
-    if constexpr (G4) {
-      if (wave < Gm::A_SC)
-        wait_ktiles_g4<TPW, 1 + Gm::B_SC>(ahead, kt);
+  if constexpr (G4 && NS == 4 && F::MB == 1) {
+    // Scale groups with a four-stage ring, unrolled by the group: K-tile
+    // kg + j sits in stage j, the group's scales in group slot (kg / 4) % 2,
+    // and K-tile kg + j's B scales are byte j of each strip's scale word, so
+    // the waits, the stage addresses and the scale bytes are all constants.
+    // Away from the last group two K-tiles are in flight behind the current
+    // one, and the one that opens the next group (behind j = 2 and 3) also
+    // carries its scale loads.
+    const bool a_wave = __builtin_amdgcn_readfirstlane(wave) < Gm::A_SC;  // uniform
+    int t_in = 0;
+    for (int kg = 0; kg < KT; kg += 4) {
+      const bool last = kg + 4 >= KT;
+      const unsigned char* gs = ring + NS * Gm::STAGE4 + ((kg >> 2) & 1) * Gm::GSTAGE;
+      uint32_t sbw[4];
+      static_for<0, 4>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        const int kt = kg + j;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (!last) {
+          if constexpr (j < 2) {
+            wait_vm<2 * TPW>();
+          } else {
+            if (a_wave)
+              wait_vm<2 * TPW + 1 + Gm::B_SC>();
+            else
+              wait_vm<2 * TPW + Gm::B_SC>();
+          }
+        } else {
+          const int ahead = min(NS - 2, KT - 1 - kt);
+          if (a_wave)
+            wait_ktiles_g4<TPW, 1 + Gm::B_SC>(ahead, kt);
+          else
+            wait_ktiles_g4<TPW, Gm::B_SC>(ahead, kt);
+        }
+        // the barrier, as in the general loop below
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (kt + NS - 1 < KT) issue_ktile_g4c<Gm, (j + 3) % 4, j == 1>(src, step, as_src, bs_src, ring, wave, kt + NS - 1);
+        const unsigned char* st = ring + j * Gm::STAGE4;
+        v4i a[MF][1], b[4][1];
+        uint32_t sa[MF];
+        if constexpr (j == 0) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) sbw[jj] = reinterpret_cast<const uint32_t*>(gs + Gm::GSA)[(4 * wn + jj) * 64 + lane];
+        }
+#pragma unroll
+        for (int i = 0; i < MF; ++i) sa[i] = gs[(16 * (wm * MF + i) + m) * 16 + 4 * j + q];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          b[jj][0] = *reinterpret_cast<const v4i*>(st + (Gm::A_TILES + 4 * wn + jj) * 1024 + lane * 16);
+#pragma unroll
+        for (int i = 0; i < MF; ++i) a[i][0] = *reinterpret_cast<const v4i*>(st + (wm * MF + i) * 1024 + lane * 16);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t_in == 0)
+          mma_tile_fp4_sel<MF, j>(a, b, sa, sbw, true, acc);
+        else
+          mma_tile_fp4_sel<MF, j>(a, b, sa, sbw, false, acc);
+        if (++t_in == g.CT) {  // end of a chunk: add its sum in chunk order
+          t_in = 0;
+#pragma unroll
+          for (int i = 0; i < MF; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) sum[i][jj] = sum[i][jj] + acc[i][jj];
+        }
+      });
+    }
+  } else {  // the general loop: scales per K-tile, or a three-stage ring
+    for (int kt = 0, t_in = 0; kt < KT; ++kt) {
+      // K-tile kt has landed once only the K-tiles issued after it are pending
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      const int ahead = min(NS - 2, KT - 1 - kt);  // K-tiles issued after kt
+      if constexpr (G4) {
+        if (wave < Gm::A_SC)
+          wait_ktiles_g4<TPW, 1 + Gm::B_SC>(ahead, kt);
+        else
+          wait_ktiles_g4<TPW, Gm::B_SC>(ahead, kt);
+      } else {
+        if (wave < Gm::A_SC)
+          wait_ktiles<Gm::CNT_A>(ahead);
+        else
+          wait_ktiles<Gm::CNT_B>(ahead);
+      }
+      // Each wavefront's own loads of K-tile kt are in LDS (the wait above); the
+      // barrier makes that hold for all of them.  It is a bare s_barrier: the
+      // workgroup fence of __syncthreads() would wait for every direct-to-LDS
+      // load in flight, the later K-tiles' included, and empty the ring.  The
+      // LDS reads of K-tile kt - 1 are complete (its matrix instructions have
+      // consumed them), so its slot may be refilled once every wavefront is here.
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (kt + NS - 1 < KT) issue(kt + NS - 1);
+      const unsigned char* st = ring + (kt % NS) * (G4 ? Gm::STAGE4 : Gm::STAGE);
+      // scales of K-tile kt: its group slot (G4), or its stage
+      const unsigned char* sc_a = G4 ? ring + NS * Gm::STAGE4 + ((kt >> 2) & 1) * Gm::GSTAGE : st + Gm::A_SC_OFF;
+      const uint32_t* sc_b = reinterpret_cast<const uint32_t*>(G4 ? sc_a + Gm::GSA : st + Gm::B_SC_OFF);
+      v4i a[MF][R], b[4][R];
+      uint32_t sa[MF], sb[4], sbw[4];
+      // LDS reads in the order the matrix instructions consume them: scales,
+      // the B strips, then A fragment by fragment, so that the instructions of
+      // fragment i wait only for the reads up to a[i]
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sbw[j] = sc_b[(4 * wn + j) * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < MF; ++i) {
+        const int f = wm * MF + i;
+        sa[i] = G4 ? sc_a[(16 * f + m) * 16 + 4 * (kt & 3) + q] : sc_a[(16 * f + m) * 4 + q];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int s = 4 * wn + j;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          b[j][r] = *reinterpret_cast<const v4i*>(st + (Gm::A_TILES + s * R + r) * 1024 + lane * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < MF; ++i) {
+        const int f = wm * MF + i;
+#pragma unroll
+        for (int r = 0; r < R; ++r) a[i][r] = *reinterpret_cast<const v4i*>(st + (f * R + r) * 1024 + lane * 16);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sb[j] = (sbw[j] >> (8 * (kt & 3))) & 0xffu;
+      if (t_in == 0)
+        mma_tile<F, MF, R>(a, b, sa, sb, true, acc);
       else
-        wait_ktiles_g4<TPW, Gm::B_SC>(ahead, kt);
-    } else {
-      if (wave < Gm::A_SC)
-        wait_ktiles<Gm::CNT_A>(ahead);
-      else
-        wait_ktiles<Gm::CNT_B>(ahead);
-    }
-    // Each wavefront's own loads of K-tile kt are in LDS (the wait above); the
-    // barrier makes that hold for all of them.  It is a bare s_barrier: the
-    // workgroup fence of __syncthreads() would wait for every direct-to-LDS
-    // load in flight, the later K-tiles' included, and empty the ring.  The
-    // LDS reads of K-tile kt - 1 are complete (its matrix instructions have
-    // consumed them), so its slot may be refilled once every wavefront is here.
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (kt + NS - 1 < KT) issue(kt + NS - 1);
-    const unsigned char* st = ring + (kt % NS) * (G4 ? Gm::STAGE4 : Gm::STAGE);
-    // scales of K-tile kt: its group slot (G4), or its stage
-    const unsigned char* sc_a = G4 ? ring + NS * Gm::STAGE4 + ((kt >> 2) & 1) * Gm::GSTAGE : st + Gm::A_SC_OFF;
-    const uint32_t* sc_b = reinterpret_cast<const uint32_t*>(G4 ? sc_a + Gm::GSA : st + Gm::B_SC_OFF);
-    v4i a[MF][R], b[4][R];
-    uint32_t sa[MF], sb[4], sbw[4];
-    // LDS reads in the order the matrix instructions consume them: scales,
-    // the B strips, then A fragment by fragment, so that the instructions of
-    // fragment i wait only for the reads up to a[i]
+        mma_tile<F, MF, R>(a, b, sa, sb, false, acc);
+      if (++t_in == g.CT) {  // end of a chunk: add its sum in chunk order
+        t_in = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sbw[j] = sc_b[(4 * wn + j) * 64 + lane];
+        for (int i = 0; i < MF; ++i)
 #pragma unroll
-    for (int i = 0; i < MF; ++i) {
-      const int f = wm * MF + i;
-      sa[i] = G4 ? sc_a[(16 * f + m) * 16 + 4 * (kt & 3) + q] : sc_a[(16 * f + m) * 4 + q];
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int s = 4 * wn + j;
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-        b[j][r] = *reinterpret_cast<const v4i*>(st + (Gm::A_TILES + s * R + r) * 1024 + lane * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < MF; ++i) {
-      const int f = wm * MF + i;
-#pragma unroll
-      for (int r = 0; r < R; ++r) a[i][r] = *reinterpret_cast<const v4i*>(st + (f * R + r) * 1024 + lane * 16);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sb[j] = (sbw[j] >> (8 * (kt & 3))) & 0xffu;
-    if (t_in == 0)
-      mma_tile<F, MF, R>(a, b, sa, sb, true, acc);
-    else
-      mma_tile<F, MF, R>(a, b, sa, sb, false, acc);
-    if (++t_in == g.CT) {  // end of a chunk: add its sum in chunk order
-      t_in = 0;
-#pragma unroll
-      for (int i = 0; i < MF; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sum[i][j] = sum[i][j] + acc[i][j];
+          for (int j = 0; j < 4; ++j) sum[i][j] = sum[i][j] + acc[i][j];
+      }
     }
   }
 
