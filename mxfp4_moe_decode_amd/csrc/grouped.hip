@@ -253,28 +253,32 @@ __device__ __forceinline__ void static_for(Fn&& f) {
 // One K-tile of FP4 products with the B scales taken as byte OPB of each
 // strip's scale word (the word holds the scales of four K-tiles); the first
 // tile of a chunk starts its chain from zero.
-template <int MF, int OPB>
-__device__ __forceinline__ void mma_tile_fp4_sel(const v4i (&a)[MF][1], const v4i (&b)[4][1], const uint32_t (&sa)[MF],
-                                                 const uint32_t (&sbw)[4], bool first, v4f (&acc)[MF][4]) {
+template <class F, int MF, int R, int OPB>
+__device__ __forceinline__ void mma_tile_sel(const v4i (&a)[MF][R], const v4i (&b)[4][R], const uint32_t (&sa)[MF],
+                                             const uint32_t (&sbw)[4], bool first, v4f (&acc)[MF][4]) {
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  constexpr int FMT = F::MB == 1 ? 4 : 0;  // cbsz / blgp: E2M1 or E4M3 operands
 #pragma unroll
   for (int i = 0; i < MF; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const v8i A = {a[i][0][0], a[i][0][1], a[i][0][2], a[i][0][3], 0, 0, 0, 0};
-      const v8i B = {b[j][0][0], b[j][0][1], b[j][0][2], b[j][0][3], 0, 0, 0, 0};
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, first ? zero : acc[i][j], 4, 4, 0, (int)sa[i],
-                                                                    OPB, (int)sbw[j]);
+      const v8i A = {a[i][0][0], a[i][0][1], a[i][0][2], a[i][0][3],
+                     R == 2 ? a[i][R - 1][0] : 0, R == 2 ? a[i][R - 1][1] : 0, R == 2 ? a[i][R - 1][2] : 0,
+                     R == 2 ? a[i][R - 1][3] : 0};
+      const v8i B = {b[j][0][0], b[j][0][1], b[j][0][2], b[j][0][3],
+                     R == 2 ? b[j][R - 1][0] : 0, R == 2 ? b[j][R - 1][1] : 0, R == 2 ? b[j][R - 1][2] : 0,
+                     R == 2 ? b[j][R - 1][3] : 0};
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, first ? zero : acc[i][j], FMT, FMT, 0,
+                                                                    (int)sa[i], OPB, (int)sbw[j]);
     }
 }
 
-// issue_ktile_g4 with the ring stage and whether kt opens a scale group known
-// at compile time.
-template <class Gm, int STAGE_I, bool OPEN>
+// issue_ktile_g4 with whether kt opens a scale group known at compile time.
+template <class Gm, bool OPEN>
 __device__ __forceinline__ void issue_ktile_g4c(const uint8_t* (&src)[Gm::TPW], const int (&step)[Gm::TPW],
                                                 const uint8_t* as_src, const uint8_t* (&bs_src)[Gm::B_SC],
                                                 unsigned char* ring, int wave, int kt) {
-  unsigned char* st = ring + STAGE_I * Gm::STAGE4;
+  unsigned char* st = ring + (kt % Gm::NS) * Gm::STAGE4;
 #pragma unroll
   for (int i = 0; i < Gm::TPW; ++i) lds_dma<16>(src[i] + (size_t)kt * step[i], st + (wave + Gm::WAVES * i) * 1024);
   if constexpr (OPEN) {
@@ -386,17 +390,17 @@ grouped_gemm_kernel(GemmArgs g) {  // 2 x WN wavefronts
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; ++s0)
     if (s0 < KT) issue(s0);
-  if constexpr (G4 && NS == 4 && F::MB == 1) {
-    // Scale groups with a four-stage ring, unrolled by the group: K-tile
-    // kg + j sits in stage j, the group's scales in group slot (kg / 4) % 2,
-    // and K-tile kg + j's B scales are byte j of each strip's scale word, so
-    // the waits, the stage addresses and the scale bytes are all constants.
-    // Away from the last group two K-tiles are in flight behind the current
-    // one, and the one that opens the next group (behind j = 2 and 3) also
-    // carries its scale loads.
+  if constexpr (G4) {
+    // Scale groups, the loop unrolled by the group: the group's scales sit in
+    // group slot (kg / 4) % 2 and K-tile kg + j's B scales are byte j of each
+    // strip's scale word, so the waits and the scale bytes are constants (with
+    // a four-stage ring the stage, j, is too).  Away from the last group NS - 2
+    // K-tiles are in flight behind the current one, and when one of them opens
+    // the next group (j >= 4 - (NS - 2)) its scale loads are in flight too.
     const bool a_wave = __builtin_amdgcn_readfirstlane(wave) < Gm::A_SC;  // uniform
     int t_in = 0;
-    for (int kg = 0; kg < KT; kg += 4) {
+    for (int g4 = 0; g4 < KT / 4; ++g4) {
+      const int kg = 4 * g4;
       const bool last = kg + 4 >= KT;
       const unsigned char* gs = ring + NS * Gm::STAGE4 + ((kg >> 2) & 1) * Gm::GSTAGE;
       uint32_t sbw[4];
@@ -405,13 +409,13 @@ grouped_gemm_kernel(GemmArgs g) {  // 2 x WN wavefronts
         const int kt = kg + j;
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if (!last) {
-          if constexpr (j < 2) {
-            wait_vm<2 * TPW>();
+          if constexpr (j < 4 - (NS - 2)) {
+            wait_vm<(NS - 2) * TPW>();
           } else {
             if (a_wave)
-              wait_vm<2 * TPW + 1 + Gm::B_SC>();
+              wait_vm<(NS - 2) * TPW + 1 + Gm::B_SC>();
             else
-              wait_vm<2 * TPW + Gm::B_SC>();
+              wait_vm<(NS - 2) * TPW + Gm::B_SC>();
           }
         } else {
           const int ahead = min(NS - 2, KT - 1 - kt);
@@ -426,9 +430,9 @@ grouped_gemm_kernel(GemmArgs g) {  // 2 x WN wavefronts
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (kt + NS - 1 < KT) issue_ktile_g4c<Gm, (j + 3) % 4, j == 1>(src, step, as_src, bs_src, ring, wave, kt + NS - 1);
-        const unsigned char* st = ring + j * Gm::STAGE4;
-        v4i a[MF][1], b[4][1];
+        if (kt + NS - 1 < KT) issue_ktile_g4c<Gm, (j + NS - 1) % 4 == 0>(src, step, as_src, bs_src, ring, wave, kt + NS - 1);
+        const unsigned char* st = ring + (kt % NS) * Gm::STAGE4;
+        v4i a[MF][R], b[4][R];
         uint32_t sa[MF];
         if constexpr (j == 0) {
 #pragma unroll
@@ -438,14 +442,19 @@ grouped_gemm_kernel(GemmArgs g) {  // 2 x WN wavefronts
         for (int i = 0; i < MF; ++i) sa[i] = gs[(16 * (wm * MF + i) + m) * 16 + 4 * j + q];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
-          b[jj][0] = *reinterpret_cast<const v4i*>(st + (Gm::A_TILES + 4 * wn + jj) * 1024 + lane * 16);
 #pragma unroll
-        for (int i = 0; i < MF; ++i) a[i][0] = *reinterpret_cast<const v4i*>(st + (wm * MF + i) * 1024 + lane * 16);
+          for (int r = 0; r < R; ++r)
+            b[jj][r] = *reinterpret_cast<const v4i*>(st + (Gm::A_TILES + (4 * wn + jj) * R + r) * 1024 + lane * 16);
+#pragma unroll
+        for (int i = 0; i < MF; ++i)
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+            a[i][r] = *reinterpret_cast<const v4i*>(st + ((wm * MF + i) * R + r) * 1024 + lane * 16);
         __builtin_amdgcn_sched_barrier(0);
         if (t_in == 0)
-          mma_tile_fp4_sel<MF, j>(a, b, sa, sbw, true, acc);
+          mma_tile_sel<F, MF, R, j>(a, b, sa, sbw, true, acc);
         else
-          mma_tile_fp4_sel<MF, j>(a, b, sa, sbw, false, acc);
+          mma_tile_sel<F, MF, R, j>(a, b, sa, sbw, false, acc);
         if (++t_in == g.CT) {  // end of a chunk: add its sum in chunk order
           t_in = 0;
 #pragma unroll
@@ -455,7 +464,7 @@ grouped_gemm_kernel(GemmArgs g) {  // 2 x WN wavefronts
         }
       });
     }
-  } else {  // the general loop: scales per K-tile, or a three-stage ring
+  } else {  // the general loop: scales per K-tile
     for (int kt = 0, t_in = 0; kt < KT; ++kt) {
       // K-tile kt has landed once only the K-tiles issued after it are pending
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
