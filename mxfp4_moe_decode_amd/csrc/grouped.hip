@@ -469,17 +469,10 @@ grouped_gemm_kernel(GemmArgs g) {  // 2 x WN wavefronts
       // K-tile kt has landed once only the K-tiles issued after it are pending
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       const int ahead = min(NS - 2, KT - 1 - kt);  // K-tiles issued after kt
-      if constexpr (G4) {
-        if (wave < Gm::A_SC)
-          wait_ktiles_g4<TPW, 1 + Gm::B_SC>(ahead, kt);
-        else
-          wait_ktiles_g4<TPW, Gm::B_SC>(ahead, kt);
-      } else {
-        if (wave < Gm::A_SC)
-          wait_ktiles<Gm::CNT_A>(ahead);
-        else
-          wait_ktiles<Gm::CNT_B>(ahead);
-      }
+      if (wave < Gm::A_SC)
+        wait_ktiles<Gm::CNT_A>(ahead);
+      else
+        wait_ktiles<Gm::CNT_B>(ahead);
       // Each wavefront's own loads of K-tile kt are in LDS (the wait above); the
       // barrier makes that hold for all of them.  It is a bare s_barrier: the
       // workgroup fence of __syncthreads() would wait for every direct-to-LDS
@@ -492,10 +485,9 @@ grouped_gemm_kernel(GemmArgs g) {  // 2 x WN wavefronts
       __builtin_amdgcn_sched_barrier(0);
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       if (kt + NS - 1 < KT) issue(kt + NS - 1);
-      const unsigned char* st = ring + (kt % NS) * (G4 ? Gm::STAGE4 : Gm::STAGE);
-      // scales of K-tile kt: its group slot (G4), or its stage
-      const unsigned char* sc_a = G4 ? ring + NS * Gm::STAGE4 + ((kt >> 2) & 1) * Gm::GSTAGE : st + Gm::A_SC_OFF;
-      const uint32_t* sc_b = reinterpret_cast<const uint32_t*>(G4 ? sc_a + Gm::GSA : st + Gm::B_SC_OFF);
+      const unsigned char* st = ring + (kt % NS) * Gm::STAGE;
+      const unsigned char* sc_a = st + Gm::A_SC_OFF;  // the K-tile's scales sit in its stage
+      const uint32_t* sc_b = reinterpret_cast<const uint32_t*>(st + Gm::B_SC_OFF);
       v4i a[MF][R], b[4][R];
       uint32_t sa[MF], sb[4], sbw[4];
       // LDS reads in the order the matrix instructions consume them: scales,
@@ -506,7 +498,7 @@ grouped_gemm_kernel(GemmArgs g) {  // 2 x WN wavefronts
 #pragma unroll
       for (int i = 0; i < MF; ++i) {
         const int f = wm * MF + i;
-        sa[i] = G4 ? sc_a[(16 * f + m) * 16 + 4 * (kt & 3) + q] : sc_a[(16 * f + m) * 4 + q];
+        sa[i] = sc_a[(16 * f + m) * 4 + q];
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
