@@ -56,7 +56,6 @@ constexpr int kMaxK = 8;
 constexpr int kGroup = 16;     // rows of one matrix-instruction row block
 constexpr int kMaxCT = 6;      // tiles of a gate/up K-chunk held in registers
 constexpr int kBufQuads = 12;  // 16-byte weight loads one prefetch buffer holds per lane
-constexpr int kBufWords = 6;   // scale words one prefetch buffer holds per lane
 constexpr int kBufs = 3;       // register buffers of the unit pipeline
 constexpr int kDownBatch = 8;  // routed (MXFP4) down tiles per register batch; MXFP8: half
 constexpr uint64_t kSpinTicks = 100000000ull;  // ~1 s of the 100 MHz constant clock
@@ -979,7 +978,10 @@ __device__ __forceinline__ void stage_routed(const DA& A, uint32_t tag, int K, i
         if (task < tasks) {
           const uint64_t* src = A.a_r + (size_t)slots[task / nb] * K + 32 * (task % nb) + 4 * j;
           const uint64_t w0 = ld_dev(src), w1 = ld_dev(src + 1), w2 = ld_dev(src + 2), w3 = ld_dev(src + 3);
-          ok &= tag_ok(w0, tag) & tag_ok(w1, tag) & tag_ok(w2, tag) & tag_ok(w3, tag);
+          ok &= tag_ok(w0, tag);
+          ok &= tag_ok(w1, tag);
+          ok &= tag_ok(w2, tag);
+          ok &= tag_ok(w3, tag);
           v[p] = make_float4(__uint_as_float((uint32_t)w0), __uint_as_float((uint32_t)w1),
                              __uint_as_float((uint32_t)w2), __uint_as_float((uint32_t)w3));
         }
@@ -1012,7 +1014,8 @@ __device__ __forceinline__ void stage_shared(const DA& A, uint32_t tag, int K, i
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const uint64_t wg = ld_dev(src + i), wu = ld_dev(src + K + i);
-            ok &= tag_ok(wg, tag) & tag_ok(wu, tag);
+            ok &= tag_ok(wg, tag);
+            ok &= tag_ok(wu, tag);
             g[p][i] = __uint_as_float((uint32_t)wg);
             u[p][i] = __uint_as_float((uint32_t)wu);
           }
