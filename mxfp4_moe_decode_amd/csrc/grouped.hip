@@ -587,6 +587,21 @@ grouped_gemm_kernel(GemmArgs g) {  // 2 x WN wavefronts
 #pragma unroll
         for (int w = 0; w < WN; ++w) g.os[(size_t)(mb * BM + rl) * (g.inter / 32) + WN * nt + w] = ts[rl * WN + w];
       }
+  } else if constexpr (MODE == DOWN_ROUTED && WN == 4) {
+    // fp32 results straight from the registers (the 128 x 256 tile is too
+    // large to assemble in the ring): for each of its rows a lane stores one
+    // column of each strip, 16 lanes one 64-byte run
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int slot = slots[wm * 16 * MF + 16 * i + 4 * q + r];
+        if (slot < S) {
+          float* dp = g.d_part + (size_t)slot * g.H + (size_t)(16 * STRIPS) * nt + m;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dp[16 * (4 * wn + j)] = sum[i][j][r];
+        }
+      }
   } else if constexpr (MODE == DOWN_ROUTED) {
     // fp32 result rows per slot: tile [BM][16 STRIPS] (row stride padded by
     // four floats against bank conflicts), columns 16 STRIPS nt onwards
@@ -842,11 +857,14 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
     if ((err = launch_gemm<FP4, GU_ROUTED, 2>(r, stream)) != hipSuccess) return err;
   }
   if ((err = mark(4)) != hipSuccess) return err;
-  // routed down: A = intermediate in sorted order, B = W2[e], out d_part[slot]
+  // routed down: A = intermediate in sorted order, B = W2[e], out d_part[slot];
+  // 256-column tiles (eight wavefronts) when H allows: each block's
+  // intermediate is then read by half as many workgroups
   {
+    const bool wide = H % 256 == 0;
     GemmArgs r = g;
     r.MB = (int)c.nblk;
-    r.NT = H / 128;
+    r.NT = H / (wide ? 256 : 128);
     r.KT = I / 128;
     r.CT = pick_chunk(r.KT);
     r.KG = (r.KT + 3) / 4;
@@ -859,7 +877,8 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
     r.b_estride = tiled_codes_bytes(H, I, MX_FMT_FP4);
     r.bs_estride = tiled_scales_bytes(H, I);
     r.d_part = d_part;
-    if ((err = launch_gemm<FP4, DOWN_ROUTED, 2>(r, stream)) != hipSuccess) return err;
+    err = wide ? launch_gemm<FP4, DOWN_ROUTED, 4>(r, stream) : launch_gemm<FP4, DOWN_ROUTED, 2>(r, stream);
+    if (err != hipSuccess) return err;
   }
   if ((err = mark(5)) != hipSuccess) return err;
   if (Is == 0) {

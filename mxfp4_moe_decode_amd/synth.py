@@ -22,6 +22,9 @@ intermediate sizes are not on the pages and are taken as 3072 / 1024):
 * ``odd``      T=16, H=1280, 16 experts top-3, I=384, shared I_s=640: K-tile
                counts 10 / 3 / 5, so the dot products split into 2 / 1 / 1
                K-chunks and the scale groups end part-filled
+* ``h640``     T=16, H=640, 16 experts top-2, I=256, shared I_s=384: H not a
+               multiple of 256 (the grouped routed down keeps 128-column
+               tiles), K-tile counts 5 / 2 / 3
 
 Draws: expert and shared weights fp32 N(0, 0.02); router weights fp32 N(0, 0.02)
 (``decode16``: uniform); activations N(0, 1) stored as bf16 (round to nearest
@@ -55,6 +58,8 @@ WORKLOADS = {
                  zipf=None, residual=False),
     "odd": dict(T=16, H=1280, E=16, k=3, I=384, I_s=640, router="normal", layers=1,
                 zipf=None, residual=False),
+    "h640": dict(T=16, H=640, E=16, k=2, I=256, I_s=384, router="normal", layers=1,
+                 zipf=None, residual=False),
 }
 _WID = {name: i + 1 for i, name in enumerate(WORKLOADS)}
 _TAG = {"router": 1, "w13": 2, "w2": 3, "ws13": 4, "ws2": 5, "bias": 6, "x": 7, "nvfp4": 8, "norm": 9}

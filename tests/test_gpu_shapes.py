@@ -8,7 +8,9 @@ expert, and the grouped path:
 * ``wide``: 256 experts top-8 (I = I_s = 256);
 * ``odd``: H 1280, 16 experts top-3, I 384, I_s 640, whose K-tile counts
   10 / 3 / 5 split the dot products into 2 / 1 / 1 chunks and leave the scale
-  groups part-filled.
+  groups part-filled;
+* ``h640``: H 640, 16 experts top-2, I 256, I_s 384: H is not a multiple of
+  256, so the grouped routed down runs its 128-column tiles (256 otherwise).
 
 Each against the oracle (decode at 16 rows, grouped at more rows), and decode
 and grouped bit for bit against each other."""
@@ -40,7 +42,7 @@ def _host(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("name", ["tp4", "wide", "odd"])
+@pytest.mark.parametrize("name", ["tp4", "wide", "odd", "h640"])
 def test_shape_decode_matches_oracle_and_grouped(name):
     cfg, gl, ol = _layers(name)
     x = synth.activations(cfg)
@@ -56,7 +58,7 @@ def test_shape_decode_matches_oracle_and_grouped(name):
     assert np.array_equal(_host(yg), y)
 
 
-@pytest.mark.parametrize("name,T", [("tp4", 200), ("odd", 300)])
+@pytest.mark.parametrize("name,T", [("tp4", 200), ("odd", 300), ("h640", 300)])
 def test_shape_grouped_matches_oracle(name, T):
     """Enough rows that expert segments span several 128-row blocks (odd: 16
     experts top-3, about 56 slots each at 300 rows; tp4: about 6 per expert)."""
