@@ -1352,8 +1352,23 @@ __device__ __forceinline__ void decode_body(const DA& A, uint32_t tag, SmemOf<DA
     const unsigned b = blockIdx.x, g = (unsigned)G;  // products stay below 2^24
     S.b0 = (int)((unsigned)NB * b / g);
     S.nb = (int)((unsigned)NB * (b + 1) / g) - S.b0;
-    S.c0 = (int)((unsigned)NCU * b / g);
-    S.nc = (int)((unsigned)NCU * (b + 1) / g) - S.c0;
+    if (T > 1) {
+      // Above one row phase C is cut by cost: a shared down unit (MXFP8)
+      // moves twice the weight bytes of a routed (MXFP4) one and counts
+      // twice.  (At one row there are fewer units than workgroups, and a cut
+      // by cost would give some workgroups two routed units.)  Shared unit
+      // u < ns covers cost positions [2u, 2u + 2), routed unit u >= ns covers
+      // [ns + u, ns + u + 1); workgroup b takes the units whose range starts
+      // in [ct b / G, ct (b + 1) / G), so every unit has one owner and each
+      // run stays contiguous.
+      const unsigned ns = (unsigned)S.ns, ct = 2u * ns + ((unsigned)NCU - ns);
+      auto first_at = [&](unsigned p) -> int { return (int)(p <= 2u * ns ? (p + 1u) / 2u : p - ns); };
+      S.c0 = first_at(ct * b / g);
+      S.nc = first_at(ct * (b + 1) / g) - S.c0;
+    } else {
+      S.c0 = (int)((unsigned)NCU * b / g);
+      S.nc = (int)((unsigned)NCU * (b + 1) / g) - S.c0;
+    }
   }
   const int total = S.nb + S.nc;
 
