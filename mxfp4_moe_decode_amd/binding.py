@@ -405,8 +405,8 @@ class MoEForward:
     T <= ``fused_max_rows``, falling back to the grouped path when the library
     reports the shape as unsupported by it; the grouped path otherwise.  The
     default is 64 rows: the wide fused launch is faster than the grouped path
-    at every row count from 17 to 64 on the MiniMax-M3.1 layer (93 against
-    162 us at 17 rows, 206 against 236 us at 64, one MI355X).  16 gives the
+    at every row count from 17 to 64 on the MiniMax-M3.1 layer (85 against
+    150 us at 17 rows, 187 against 215 us at 64, one MI355X).  16 gives the
     pages' own rule.  Keeps the decode workspace (zero-filled once) and a
     grouped workspace grown on demand."""
 

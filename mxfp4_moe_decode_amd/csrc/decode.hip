@@ -272,6 +272,10 @@ __device__ __forceinline__ uint32_t quant_block8(const uint32_t (&bits)[4], uint
 // issued before any of its blocks is quantized.
 constexpr int kQBatch = 16;
 constexpr int kEarlyQuantT = 4;
+// phase-B/C parts of the late and the other workgroups with the pre-router
+// norm above kEarlyQuantT rows (see decode_body)
+constexpr unsigned kNormEarly = 3, kNormLate = 2;
+static_assert(kNormEarly <= 3 && kNormLate <= kNormEarly, "the unit cut's 32-bit products assume parts of at most 3");
 constexpr int kQGroups = kThreads / 8;
 
 // Without a row list (kRows false) task t is block t of x in row-major
@@ -1349,9 +1353,26 @@ __device__ __forceinline__ void decode_body(const DA& A, uint32_t tag, SmemOf<DA
   {
     const int NB = NQB * (A.i() / 16);  // the folded expert's gate/up ran in phase A
     const int NCU = S.ns + NQC * S.nhg;
-    const unsigned b = blockIdx.x, g = (unsigned)G;  // products stay below 2^24
-    S.b0 = (int)((unsigned)NB * b / g);
-    S.nb = (int)((unsigned)NB * (b + 1) / g) - S.b0;
+    // 32-bit products: decode_supported keeps the phase-B unit count and the
+    // phase-C cost below 2^19 and the grid is at most kDecodeMaxGrid (2^11),
+    // so with parts of at most 3 every cut position below stays under 2^32.
+    const unsigned b = blockIdx.x, g = (unsigned)G;
+    // With the pre-router norm and more than kEarlyQuantT rows, the
+    // workgroups that ran a shared strip or a folded gate/up unit after the
+    // router units (they form the norm factors of every row and quantize
+    // every row first) reach routing long after the router workgroups, so
+    // they take kNormLate parts of the phase-B and phase-C work to the
+    // others' kNormEarly; otherwise every workgroup takes one part.
+    const bool weigh = !DA::kWide && A.norm_w && T > kEarlyQuantT;
+    const unsigned we = weigh ? kNormEarly : 1u, wl = weigh ? kNormLate : 1u;
+    const unsigned l0 = (unsigned)min(E, G), l1 = (unsigned)min(E + n_ss, G);  // the late ones: [l0, l1)
+    auto wsum = [&](unsigned x) -> unsigned {  // weight of workgroups 0 .. x - 1
+      const unsigned late = min(x, l1) > l0 ? min(x, l1) - l0 : 0u;
+      return we * x - (we - wl) * late;
+    };
+    const unsigned wt = wsum(g), w0 = wsum(b), w1 = wsum(b + 1);
+    S.b0 = (int)((unsigned)NB * w0 / wt);
+    S.nb = (int)((unsigned)NB * w1 / wt) - S.b0;
     if (T > 1) {
       // Above one row phase C is cut by cost: a shared down unit (MXFP8)
       // moves twice the weight bytes of a routed (MXFP4) one and counts
@@ -1359,15 +1380,15 @@ __device__ __forceinline__ void decode_body(const DA& A, uint32_t tag, SmemOf<DA
       // by cost would give some workgroups two routed units.)  Shared unit
       // u < ns covers cost positions [2u, 2u + 2), routed unit u >= ns covers
       // [ns + u, ns + u + 1); workgroup b takes the units whose range starts
-      // in [ct b / G, ct (b + 1) / G), so every unit has one owner and each
-      // run stays contiguous.
+      // in [ct w0 / wt, ct w1 / wt), so every unit has one owner and each run
+      // stays contiguous.
       const unsigned ns = (unsigned)S.ns, ct = 2u * ns + ((unsigned)NCU - ns);
       auto first_at = [&](unsigned p) -> int { return (int)(p <= 2u * ns ? (p + 1u) / 2u : p - ns); };
-      S.c0 = first_at(ct * b / g);
-      S.nc = first_at(ct * (b + 1) / g) - S.c0;
+      S.c0 = first_at(ct * w0 / wt);
+      S.nc = first_at(ct * w1 / wt) - S.c0;
     } else {
-      S.c0 = (int)((unsigned)NCU * b / g);
-      S.nc = (int)((unsigned)NCU * (b + 1) / g) - S.c0;
+      S.c0 = (int)((unsigned)NCU * w0 / wt);
+      S.nc = (int)((unsigned)NCU * w1 / wt) - S.c0;
     }
   }
   const int total = S.nb + S.nc;
@@ -1615,6 +1636,13 @@ bool decode_supported(const moe_layer_t& L, int T) {
   // a K-chunk of the gate/up (K = H) must fit the register buffers, the LDS a workgroup
   const int KT1 = L.hidden / 128;
   const size_t smem = T <= kDecodeMaxT ? sizeof(SmemT<kDecodeMaxT>) : sizeof(SmemT<kDecodeWideMaxT>);
+  // the kernel cuts the unit sequences with 32-bit products (unit count or
+  // cost times a cumulative weight of at most 3 * kDecodeMaxGrid)
+  const size_t groups = (size_t)max_rows_for(T) / 16, nq = ((size_t)L.num_experts + 1) * groups;
+  const size_t nhg = (size_t)L.hidden / 64, nb_units = nq * (L.inter / 16);
+  const size_t c_cost = 2 * nhg * groups + nq * nhg;
+  if (nb_units >= (1u << 19) || c_cost >= (1u << 19)) return false;
+  static_assert(3ull * kDecodeMaxGrid * (1u << 19) <= 0xffffffffull, "32-bit unit cut");
   return KT1 / n_chunks(KT1) <= kMaxCT && lds_layout(L, max_rows_for(T)).total + smem <= 160 * 1024;
 }
 
