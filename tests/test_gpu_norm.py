@@ -1,8 +1,8 @@
 """The pre-router RMSNorm fused into the layer call: the input is the
 residual stream h, the MoE runs on RMSNorm(h) (fp32, straight into the router
 and the MX quantizers) and h is added back.  Against the oracle's normed layer
-on the fused decode and grouped paths (MXFP8 and folded shared experts), and
-bit for bit between the two paths."""
+on the fused decode and grouped paths (MXFP8 and folded shared experts), bit
+for bit between the two paths, and bit for bit across batch sizes."""
 
 import copy
 
@@ -84,3 +84,21 @@ def test_normed_layer_rejects_a_separate_residual():
     with pytest.raises(binding.MoeError) as ei:
         binding.fused_moe_mxfp4_decode(gl, x, residual=x.clone())
     assert ei.value.status == -1
+
+
+@pytest.mark.parametrize("fold", [False, True])
+def test_normed_decode_rows_independent_of_batch(fold):
+    """Above four rows the fused launch hands the phase-B and phase-C units
+    out by weight (the workgroups that normalize and quantize every row in
+    phase A take fewer); each row's result must not depend on that."""
+    cfg, gl, ol = _normed("decode16", fold)
+    x = synth.activations(cfg, T=16, index=7)
+    ws = binding.decode_workspace(gl)
+    print(f"[norm] decode16 batches folded={fold}", flush=True)
+    y16 = _host(binding.fused_moe_mxfp4_decode(gl, _dev(x), workspace=ws))
+    torch.cuda.synchronize()
+    for T in (1, 4, 5, 8, 12):
+        yT = _host(binding.fused_moe_mxfp4_decode(gl, _dev(x[:T]), workspace=ws))
+        torch.cuda.synchronize()
+        assert np.array_equal(yT, y16[:T]), T
+    assert binding.moe_decode_status(ws) == 0
