@@ -58,10 +58,13 @@ def test_shape_decode_matches_oracle_and_grouped(name):
     assert np.array_equal(_host(yg), y)
 
 
-@pytest.mark.parametrize("name,T", [("tp4", 200), ("odd", 300), ("h640", 300)])
+@pytest.mark.parametrize("name,T", [("tp4", 200), ("odd", 300), ("h640", 300), ("odd", 700)])
 def test_shape_grouped_matches_oracle(name, T):
     """Enough rows that expert segments span several 128-row blocks (odd: 16
-    experts top-3, about 56 slots each at 300 rows; tp4: about 6 per expert)."""
+    experts top-3, about 56 slots each at 300 rows; tp4: about 6 per expert).
+    At 700 rows the odd shape averages more than one 128-row block per
+    expert, so its routed gate/up takes the 256-column tiles, with K-tile
+    counts that are not whole scale groups."""
     cfg, gl, ol = _layers(name)
     x = synth.activations(cfg, T=T, index=T)
     print(f"[shapes] {name} grouped T={T}", flush=True)
