@@ -25,6 +25,9 @@ intermediate sizes are not on the pages and are taken as 3072 / 1024):
 * ``h640``     T=16, H=640, 16 experts top-2, I=256, shared I_s=384: H not a
                multiple of 256 (the grouped routed down keeps 128-column
                tiles), K-tile counts 5 / 2 / 3
+* ``h384``     T=16, H=384, 16 experts top-2, I=512, shared I_s=512: H not a
+               multiple of 256 with whole scale groups in the down products
+               (K-tile counts 3 / 4 / 4)
 
 Draws: expert and shared weights fp32 N(0, 0.02); router weights fp32 N(0, 0.02)
 (``decode16``: uniform); activations N(0, 1) stored as bf16 (round to nearest
@@ -59,6 +62,8 @@ WORKLOADS = {
     "odd": dict(T=16, H=1280, E=16, k=3, I=384, I_s=640, router="normal", layers=1,
                 zipf=None, residual=False),
     "h640": dict(T=16, H=640, E=16, k=2, I=256, I_s=384, router="normal", layers=1,
+                 zipf=None, residual=False),
+    "h384": dict(T=16, H=384, E=16, k=2, I=512, I_s=512, router="normal", layers=1,
                  zipf=None, residual=False),
 }
 _WID = {name: i + 1 for i, name in enumerate(WORKLOADS)}

@@ -10,7 +10,9 @@ expert, and the grouped path:
   10 / 3 / 5 split the dot products into 2 / 1 / 1 chunks and leave the scale
   groups part-filled;
 * ``h640``: H 640, 16 experts top-2, I 256, I_s 384: H is not a multiple of
-  256, so the grouped routed down runs its 128-column tiles (256 otherwise).
+  256, so the grouped routed down runs its 128-column tiles (256 otherwise);
+* ``h384``: H 384, 16 experts top-2, I = I_s = 512: the same, with the down
+  products' K a multiple of 512 (the scale-group loop).
 
 Each against the oracle (decode at 16 rows, grouped at more rows), and decode
 and grouped bit for bit against each other."""
@@ -42,7 +44,7 @@ def _host(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("name", ["tp4", "wide", "odd", "h640"])
+@pytest.mark.parametrize("name", ["tp4", "wide", "odd", "h640", "h384"])
 def test_shape_decode_matches_oracle_and_grouped(name):
     cfg, gl, ol = _layers(name)
     x = synth.activations(cfg)
@@ -58,7 +60,7 @@ def test_shape_decode_matches_oracle_and_grouped(name):
     assert np.array_equal(_host(yg), y)
 
 
-@pytest.mark.parametrize("name,T", [("tp4", 200), ("odd", 300), ("h640", 300), ("odd", 700)])
+@pytest.mark.parametrize("name,T", [("tp4", 200), ("odd", 300), ("h640", 300), ("odd", 700), ("h384", 300)])
 def test_shape_grouped_matches_oracle(name, T):
     """Enough rows that expert segments span several 128-row blocks (odd: 16
     experts top-3, about 56 slots each at 300 rows; tp4: about 6 per expert).
