@@ -330,73 +330,88 @@ grouped_gemm_kernel(GemmArgs g) {  // 2 x WN wavefronts
   if constexpr (kRouted) ntiles = min(ntiles, (*g.num_padded + BM - 1) / BM * g.NT);
   const int per = (ntiles + 7) >> 3;  // tiles per XCD; gridDim.x / 8 >= per
   if ((L >> 3) >= per) return;
-  const int tile = (L & 7) * per + (L >> 3);
+  // The routed gate/up with 256-column tiles (one workgroup per CU) runs a
+  // persistent grid: the workgroup at position p of its XCD takes tiles
+  // x*per + p, x*per + p + G/8, ... in turn (G the grid size); the others
+  // take one tile each.
+  constexpr bool kPersist = G4 && WN == 4 && MODE == GU_ROUTED;
+  const int xcd = L & 7, stride = kPersist ? (int)(gridDim.x >> 3) : per;
+  int it = L >> 3;
+  int tile = xcd * per + it;
   if (tile >= ntiles) return;
-  int mb = tile / g.NT, nt = tile % g.NT;
-  if constexpr (MODE == GU_SHARED) {
-    // every row block multiplies the same weights: bands of GM row blocks
-    // taken column by column, so the tiles that run together on an XCD share
-    // their weight blocks GM ways (row-major, the XCD's 64 concurrent tiles
-    // would cover four row blocks and every weight block; 3.5% faster at
-    // 8192 rows).  Not for the shared down: its combine reads whole rows of
-    // the routed outputs, which row-major order keeps contiguous.
-    constexpr int GM = 16;
-    const int band = tile / (GM * g.NT), idx = tile % (GM * g.NT);
-    const int gm = min(GM, g.MB - band * GM);
-    mb = band * GM + idx % gm;
-    nt = idx / gm;
-  }
-  int e = 0;
-  if constexpr (kRouted) e = g.block_expert[mb];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / WN, wn = wave % WN;
+  auto locate = [&](int t, int& mb_, int& nt_, int& e_) {
+    int mb = t / g.NT, nt = t % g.NT;
+    if constexpr (MODE == GU_SHARED) {
+      // every row block multiplies the same weights: bands of GM row blocks
+      // taken column by column, so the tiles that run together on an XCD share
+      // their weight blocks GM ways (row-major, the XCD's 64 concurrent tiles
+      // would cover four row blocks and every weight block; 3.5% faster at
+      // 8192 rows).  Not for the shared down: its combine reads whole rows of
+      // the routed outputs, which row-major order keeps contiguous.
+      constexpr int GM = 16;
+      const int band = t / (GM * g.NT), idx = t % (GM * g.NT);
+      const int gm = min(GM, g.MB - band * GM);
+      mb = band * GM + idx % gm;
+      nt = idx / gm;
+    }
+    mb_ = mb;
+    nt_ = nt;
+    e_ = kRouted ? g.block_expert[mb] : 0;
+  };
+  int mb, nt, e;
+  locate(tile, mb, nt, e);
+  // the wavefront index as a uniform value: everything derived from it stays
+  // in scalar registers (the persistent loop needs the vector registers)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN, wn = wave % WN;
   const int m = lane & 15, q = lane >> 4;
   const int S = g.T * g.k;
   const int KT = g.KT, KG = g.KG;
 
   unsigned char* ring = smem;
   int32_t* slots = reinterpret_cast<int32_t*>(smem + Gm::template ring_bytes<G4>());
+  int32_t* slots_next = slots + BM;  // the next tile's (persistent grid)
+  // the gate/up epilogue's output tile, apart from the ring that the next
+  // tile's loads are filling (persistent grid)
+  unsigned char* out_tile = reinterpret_cast<unsigned char*>(slots + 2 * BM);
 
-  if (threadIdx.x < BM) {
-    const int r = mb * BM + (int)threadIdx.x;
-    slots[threadIdx.x] = kRouted ? g.sorted_slots[r] : (r < g.T ? r : S);
-  }
-  __syncthreads();
-
-  // scale sources: A, the 4 bytes of K-tile 0 of row 64*wave + lane; B, lane's
-  // word of group 0 of each strip this wavefront moves
-  const uint8_t* as_src = g.as + (size_t)a_row<MODE, BM>(g, slots, S, mb, (64 * wave + lane) % BM) * g.as_stride;
+  // A tile's rows and operand sources: slots, then (scales) A, the 4 bytes of
+  // K-tile 0 of row 64*wave + lane; B, lane's word of group 0 of each strip
+  // this wavefront moves; (codes) block t = wave + WAVES i of every K-tile
+  const uint8_t* as_src;
   const uint8_t* bs_src[Gm::B_SC];
-  const uint8_t* bsb = g.bs + (size_t)e * g.bs_estride;
-#pragma unroll
-  for (int i = 0; i < Gm::B_SC; ++i)
-    bs_src[i] = bsb + ((size_t)w_strip<MODE, WN>(g, nt, wave + WAVES * i) * KG * 64 + lane) * 4;
-
-  // the blocks this wavefront moves: block t = wave + WAVES i of every K-tile
   const uint8_t* src[TPW];
   int step[TPW];
-  const uint8_t* bb = g.b + (size_t)e * g.b_estride;
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int t = wave + WAVES * i;
-    if (t < Gm::A_TILES) {
-      const int f = t / R, r = t % R;
-      src[i] = g.a + (size_t)a_row<MODE, BM>(g, slots, S, mb, 16 * f + m) * g.a_stride + 64 * r + 16 * q;
-      step[i] = 64 * R;
-    } else {
-      const int sb = (t - Gm::A_TILES) / R, r = (t - Gm::A_TILES) % R;
-      src[i] = bb + (size_t)w_strip<MODE, WN>(g, nt, sb) * KT * 1024 * R + 1024 * r + lane * 16;
-      step[i] = 1024 * R;
+  auto setup = [&](int mb_, int nt_, int e_, int32_t* sl, const uint8_t*& as_s, const uint8_t* (&bs_s)[Gm::B_SC],
+                   const uint8_t* (&sr)[TPW], int (&st)[TPW]) {
+    if (threadIdx.x < BM) {
+      const int r = mb_ * BM + (int)threadIdx.x;
+      sl[threadIdx.x] = kRouted ? g.sorted_slots[r] : (r < g.T ? r : S);
     }
-  }
+    __syncthreads();
+    as_s = g.as + (size_t)a_row<MODE, BM>(g, sl, S, mb_, (64 * wave + lane) % BM) * g.as_stride;
+    const uint8_t* bsb = g.bs + (size_t)e_ * g.bs_estride;
+#pragma unroll
+    for (int i = 0; i < Gm::B_SC; ++i)
+      bs_s[i] = bsb + ((size_t)w_strip<MODE, WN>(g, nt_, wave + WAVES * i) * KG * 64 + lane) * 4;
+    const uint8_t* bb = g.b + (size_t)e_ * g.b_estride;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = wave + WAVES * i;
+      if (t < Gm::A_TILES) {
+        const int f = t / R, r = t % R;
+        sr[i] = g.a + (size_t)a_row<MODE, BM>(g, sl, S, mb_, 16 * f + m) * g.a_stride + 64 * r + 16 * q;
+        st[i] = 64 * R;
+      } else {
+        const int sb = (t - Gm::A_TILES) / R, r = (t - Gm::A_TILES) % R;
+        sr[i] = bb + (size_t)w_strip<MODE, WN>(g, nt_, sb) * KT * 1024 * R + 1024 * r + lane * 16;
+        st[i] = 1024 * R;
+      }
+    }
+  };
+  setup(mb, nt, e, slots, as_src, bs_src, src, step);
 
-  // chunk sums: -0 + x == x bit for bit (signed zeros included), so starting
-  // from -0 and always adding equals taking the first chunk's sum as it is
   v4f acc[MF][4], sum[MF][4];
-#pragma unroll
-  for (int i = 0; i < MF; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = sum[i][j] = v4f{-0.f, -0.f, -0.f, -0.f};
-
   auto issue = [&](int kt) {
     if constexpr (G4)
       issue_ktile_g4<Gm>(src, step, as_src, bs_src, ring, wave, kt);
@@ -406,300 +421,352 @@ grouped_gemm_kernel(GemmArgs g) {  // 2 x WN wavefronts
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; ++s0)
     if (s0 < KT) issue(s0);
-  if constexpr (G4) {
-    // Scale groups, the loop unrolled by the group: the group's scales sit in
-    // group slot (kg / 4) % 2 and K-tile kg + j's B scales are byte j of each
-    // strip's scale word, so the waits and the scale bytes are constants (with
-    // a four-stage ring the stage, j, is too).  Away from the last group NS - 2
-    // K-tiles are in flight behind the current one, and when one of them opens
-    // the next group (j >= 4 - (NS - 2)) its scale loads are in flight too.
-    const bool a_wave = __builtin_amdgcn_readfirstlane(wave) < Gm::A_SC;  // uniform
-    int t_in = 0;
-    for (int g4 = 0; g4 < KT / 4; ++g4) {
-      const int kg = 4 * g4;
-      const bool last = kg + 4 >= KT;
-      const unsigned char* gs = ring + NS * Gm::STAGE4 + ((kg >> 2) & 1) * Gm::GSTAGE;
-      uint32_t sbw[4];
-      static_for<0, 4>([&](auto J) {
-        constexpr int j = decltype(J)::value;
-        const int kt = kg + j;
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (!last) {
-          if constexpr (j < 4 - (NS - 2)) {
-            wait_vm<(NS - 2) * TPW>();
+  for (;;) {
+    // chunk sums: -0 + x == x bit for bit (signed zeros included), so starting
+    // from -0 and always adding equals taking the first chunk's sum as it is
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = sum[i][j] = v4f{-0.f, -0.f, -0.f, -0.f};
+
+    if constexpr (G4) {
+      // Scale groups, the loop unrolled by the group: the group's scales sit in
+      // group slot (kg / 4) % 2 and K-tile kg + j's B scales are byte j of each
+      // strip's scale word, so the waits and the scale bytes are constants (with
+      // a four-stage ring the stage, j, is too).  Away from the last group NS - 2
+      // K-tiles are in flight behind the current one, and when one of them opens
+      // the next group (j >= 4 - (NS - 2)) its scale loads are in flight too.
+      const bool a_wave = __builtin_amdgcn_readfirstlane(wave) < Gm::A_SC;  // uniform
+      int t_in = 0;
+      for (int g4 = 0; g4 < KT / 4; ++g4) {
+        const int kg = 4 * g4;
+        const bool last = kg + 4 >= KT;
+        const unsigned char* gs = ring + NS * Gm::STAGE4 + ((kg >> 2) & 1) * Gm::GSTAGE;
+        uint32_t sbw[4];
+        static_for<0, 4>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          const int kt = kg + j;
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          if (!last) {
+            if constexpr (j < 4 - (NS - 2)) {
+              wait_vm<(NS - 2) * TPW>();
+            } else {
+              if (a_wave)
+                wait_vm<(NS - 2) * TPW + 1 + Gm::B_SC>();
+              else
+                wait_vm<(NS - 2) * TPW + Gm::B_SC>();
+            }
           } else {
+            const int ahead = min(NS - 2, KT - 1 - kt);
             if (a_wave)
-              wait_vm<(NS - 2) * TPW + 1 + Gm::B_SC>();
+              wait_ktiles_g4<TPW, 1 + Gm::B_SC>(ahead, kt);
             else
-              wait_vm<(NS - 2) * TPW + Gm::B_SC>();
+              wait_ktiles_g4<TPW, Gm::B_SC>(ahead, kt);
           }
-        } else {
-          const int ahead = min(NS - 2, KT - 1 - kt);
-          if (a_wave)
-            wait_ktiles_g4<TPW, 1 + Gm::B_SC>(ahead, kt);
+          // the barrier, as in the general loop below
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          if (kt + NS - 1 < KT) issue_ktile_g4c<Gm, (j + NS - 1) % 4 == 0>(src, step, as_src, bs_src, ring, wave, kt + NS - 1);
+          const unsigned char* st = ring + (kt % NS) * Gm::STAGE4;
+          v4i a[MF][R], b[4][R];
+          uint32_t sa[MF];
+          if constexpr (j == 0) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) sbw[jj] = reinterpret_cast<const uint32_t*>(gs + Gm::GSA)[(4 * wn + jj) * 64 + lane];
+          }
+#pragma unroll
+          for (int i = 0; i < MF; ++i) sa[i] = gs[(16 * (wm * MF + i) + m) * 16 + 4 * j + q];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+              b[jj][r] = *reinterpret_cast<const v4i*>(st + (Gm::A_TILES + (4 * wn + jj) * R + r) * 1024 + lane * 16);
+#pragma unroll
+          for (int i = 0; i < MF; ++i)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+              a[i][r] = *reinterpret_cast<const v4i*>(st + ((wm * MF + i) * R + r) * 1024 + lane * 16);
+          __builtin_amdgcn_sched_barrier(0);
+          if (t_in == 0)
+            mma_tile_sel<F, MF, R, j>(a, b, sa, sbw, true, acc);
           else
-            wait_ktiles_g4<TPW, Gm::B_SC>(ahead, kt);
-        }
-        // the barrier, as in the general loop below
+            mma_tile_sel<F, MF, R, j>(a, b, sa, sbw, false, acc);
+          if (++t_in == g.CT) {  // end of a chunk: add its sum in chunk order
+            t_in = 0;
+#pragma unroll
+            for (int i = 0; i < MF; ++i)
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) sum[i][jj] = sum[i][jj] + acc[i][jj];
+          }
+        });
+      }
+    } else {  // the general loop: scales per K-tile
+      for (int kt = 0, t_in = 0; kt < KT; ++kt) {
+        // K-tile kt has landed once only the K-tiles issued after it are pending
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        const int ahead = min(NS - 2, KT - 1 - kt);  // K-tiles issued after kt
+        if (wave < Gm::A_SC)
+          wait_ktiles<Gm::CNT_A>(ahead);
+        else
+          wait_ktiles<Gm::CNT_B>(ahead);
+        // Each wavefront's own loads of K-tile kt are in LDS (the wait above); the
+        // barrier makes that hold for all of them.  It is a bare s_barrier: the
+        // workgroup fence of __syncthreads() would wait for every direct-to-LDS
+        // load in flight, the later K-tiles' included, and empty the ring.  The
+        // LDS reads of K-tile kt - 1 are complete (its matrix instructions have
+        // consumed them), so its slot may be refilled once every wavefront is here.
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (kt + NS - 1 < KT) issue_ktile_g4c<Gm, (j + NS - 1) % 4 == 0>(src, step, as_src, bs_src, ring, wave, kt + NS - 1);
-        const unsigned char* st = ring + (kt % NS) * Gm::STAGE4;
+        if (kt + NS - 1 < KT) issue(kt + NS - 1);
+        const unsigned char* st = ring + (kt % NS) * Gm::STAGE;
+        const unsigned char* sc_a = st + Gm::A_SC_OFF;  // the K-tile's scales sit in its stage
+        const uint32_t* sc_b = reinterpret_cast<const uint32_t*>(st + Gm::B_SC_OFF);
         v4i a[MF][R], b[4][R];
-        uint32_t sa[MF];
-        if constexpr (j == 0) {
+        uint32_t sa[MF], sb[4], sbw[4];
+        // LDS reads in the order the matrix instructions consume them: scales,
+        // the B strips, then A fragment by fragment, so that the instructions of
+        // fragment i wait only for the reads up to a[i]
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) sbw[jj] = reinterpret_cast<const uint32_t*>(gs + Gm::GSA)[(4 * wn + jj) * 64 + lane];
+        for (int j = 0; j < 4; ++j) sbw[j] = sc_b[(4 * wn + j) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < MF; ++i) {
+          const int f = wm * MF + i;
+          sa[i] = sc_a[(16 * f + m) * 4 + q];
         }
 #pragma unroll
-        for (int i = 0; i < MF; ++i) sa[i] = gs[(16 * (wm * MF + i) + m) * 16 + 4 * j + q];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-          for (int r = 0; r < R; ++r)
-            b[jj][r] = *reinterpret_cast<const v4i*>(st + (Gm::A_TILES + (4 * wn + jj) * R + r) * 1024 + lane * 16);
-#pragma unroll
-        for (int i = 0; i < MF; ++i)
+        for (int j = 0; j < 4; ++j) {
+          const int s = 4 * wn + j;
 #pragma unroll
           for (int r = 0; r < R; ++r)
-            a[i][r] = *reinterpret_cast<const v4i*>(st + ((wm * MF + i) * R + r) * 1024 + lane * 16);
+            b[j][r] = *reinterpret_cast<const v4i*>(st + (Gm::A_TILES + s * R + r) * 1024 + lane * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < MF; ++i) {
+          const int f = wm * MF + i;
+#pragma unroll
+          for (int r = 0; r < R; ++r) a[i][r] = *reinterpret_cast<const v4i*>(st + (f * R + r) * 1024 + lane * 16);
+        }
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sb[j] = (sbw[j] >> (8 * (kt & 3))) & 0xffu;
         if (t_in == 0)
-          mma_tile_sel<F, MF, R, j>(a, b, sa, sbw, true, acc);
+          mma_tile<F, MF, R>(a, b, sa, sb, true, acc);
         else
-          mma_tile_sel<F, MF, R, j>(a, b, sa, sbw, false, acc);
+          mma_tile<F, MF, R>(a, b, sa, sb, false, acc);
         if (++t_in == g.CT) {  // end of a chunk: add its sum in chunk order
           t_in = 0;
 #pragma unroll
           for (int i = 0; i < MF; ++i)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) sum[i][jj] = sum[i][jj] + acc[i][jj];
+            for (int j = 0; j < 4; ++j) sum[i][j] = sum[i][j] + acc[i][j];
         }
-      });
-    }
-  } else {  // the general loop: scales per K-tile
-    for (int kt = 0, t_in = 0; kt < KT; ++kt) {
-      // K-tile kt has landed once only the K-tiles issued after it are pending
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      const int ahead = min(NS - 2, KT - 1 - kt);  // K-tiles issued after kt
-      if (wave < Gm::A_SC)
-        wait_ktiles<Gm::CNT_A>(ahead);
-      else
-        wait_ktiles<Gm::CNT_B>(ahead);
-      // Each wavefront's own loads of K-tile kt are in LDS (the wait above); the
-      // barrier makes that hold for all of them.  It is a bare s_barrier: the
-      // workgroup fence of __syncthreads() would wait for every direct-to-LDS
-      // load in flight, the later K-tiles' included, and empty the ring.  The
-      // LDS reads of K-tile kt - 1 are complete (its matrix instructions have
-      // consumed them), so its slot may be refilled once every wavefront is here.
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      if (kt + NS - 1 < KT) issue(kt + NS - 1);
-      const unsigned char* st = ring + (kt % NS) * Gm::STAGE;
-      const unsigned char* sc_a = st + Gm::A_SC_OFF;  // the K-tile's scales sit in its stage
-      const uint32_t* sc_b = reinterpret_cast<const uint32_t*>(st + Gm::B_SC_OFF);
-      v4i a[MF][R], b[4][R];
-      uint32_t sa[MF], sb[4], sbw[4];
-      // LDS reads in the order the matrix instructions consume them: scales,
-      // the B strips, then A fragment by fragment, so that the instructions of
-      // fragment i wait only for the reads up to a[i]
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sbw[j] = sc_b[(4 * wn + j) * 64 + lane];
-#pragma unroll
-      for (int i = 0; i < MF; ++i) {
-        const int f = wm * MF + i;
-        sa[i] = sc_a[(16 * f + m) * 4 + q];
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int s = 4 * wn + j;
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-          b[j][r] = *reinterpret_cast<const v4i*>(st + (Gm::A_TILES + s * R + r) * 1024 + lane * 16);
-      }
-#pragma unroll
-      for (int i = 0; i < MF; ++i) {
-        const int f = wm * MF + i;
-#pragma unroll
-        for (int r = 0; r < R; ++r) a[i][r] = *reinterpret_cast<const v4i*>(st + (f * R + r) * 1024 + lane * 16);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sb[j] = (sbw[j] >> (8 * (kt & 3))) & 0xffu;
-      if (t_in == 0)
-        mma_tile<F, MF, R>(a, b, sa, sb, true, acc);
-      else
-        mma_tile<F, MF, R>(a, b, sa, sb, false, acc);
-      if (++t_in == g.CT) {  // end of a chunk: add its sum in chunk order
-        t_in = 0;
-#pragma unroll
-        for (int i = 0; i < MF; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sum[i][j] = sum[i][j] + acc[i][j];
       }
     }
-  }
 
-  // ---------------------------------------------------------------- epilogues
-  // The routed gate/up and down epilogues assemble the workgroup's output tile
-  // in the (now idle) LDS ring and write it out with 16-byte row-contiguous
-  // stores.
-  if constexpr (kGateUp) {
-    // SwiGLU on the 32 columns of block nb, then MX re-quantization of each
-    // row's block.  sum[i][0], sum[i][1]: gate columns m and 16 + m; sum[i][2],
-    // sum[i][3]: the matching up columns.  Output row of the intermediate: the
-    // sorted position (routed) or the row (shared).
-    constexpr int BPB = F::MB == 1 ? 16 : 32;  // code bytes of a row's 32-column block
-    constexpr int RB = WN * BPB;               // code bytes of a row of the tile
-    uint8_t* tc = ring;                        // [BM][RB] codes
-    uint8_t* ts = ring + BM * RB;              // [BM][WN] scales
-    __syncthreads();  // every wavefront is done reading the ring
+
+    // Persistent grid: the next tile's rows, sources and first K-tiles are
+    // requested here, so their latency overlaps this tile's epilogue (which
+    // uses its own output tile in LDS, not the ring).  Only the routed gate/up
+    // does this: the routed down's fp32 stores would sit in the in-order vmcnt
+    // queue ahead of the next tile's first loads (it ran 3% slower persistent).
+    it += stride;
+    const int tile2 = xcd * per + it;
+    const bool more = kPersist && it < per && tile2 < ntiles;  // uniform
+    int mb2 = 0, nt2 = 0, e2 = 0;
+    const uint8_t* as_src2 = nullptr;
+    const uint8_t* bs_src2[Gm::B_SC];
+    const uint8_t* src2[TPW];
+    int step2[TPW];
+    if constexpr (kPersist) {
+      if (more) {
+        locate(tile2, mb2, nt2, e2);
+        __syncthreads();  // every wavefront is done reading the ring
+        setup(mb2, nt2, e2, slots_next, as_src2, bs_src2, src2, step2);
 #pragma unroll
-    for (int i = 0; i < MF; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rl = wm * 16 * MF + 16 * i + 4 * q + r;
-        const uint32_t a0 = __float_as_uint(silu_mul(sum[i][0][r], sum[i][2][r]));
-        const uint32_t a1 = __float_as_uint(silu_mul(sum[i][1][r], sum[i][3][r]));
-        const uint32_t am = row16_max32(max(a0 & 0x7fffffffu, a1 & 0x7fffffffu));
-        const int ex = block_exponent<F>(am);
-        const float inv = block_inv_scale(ex);
-        uint8_t* op = tc + rl * RB + BPB * wn;
-        if constexpr (F::MB == 1) {
-          // even lanes pack columns m, m + 1 (the neighbour's value) into one
-          // byte, low nibble first; the codes are those of quant_quad_fp4
-          const uint32_t w = quant_quad_fp4(a0, row_move32(a0), a1, row_move32(a1), inv);
-          if (!(m & 1)) {
-            op[m / 2] = (uint8_t)w;
-            op[8 + m / 2] = (uint8_t)(w >> 8);
-          }
-        } else {
-          const uint32_t w = quant_pair_fp8(a0, a1, inv);
-          op[m] = (uint8_t)w;
-          op[16 + m] = (uint8_t)(w >> 8);
-        }
-        if (m == 0) ts[rl * WN + wn] = (uint8_t)(ex + 127);
+        for (int s0 = 0; s0 < NS - 1; ++s0)
+          if (s0 < KT) issue_ktile_g4<Gm>(src2, step2, as_src2, bs_src2, ring, wave, s0);
       }
-    __syncthreads();
-    const size_t row_bytes = F::MB == 1 ? (size_t)g.inter / 2 : (size_t)g.inter;
-    constexpr int PARTS = RB / 16;
-    for (int t = threadIdx.x; t < BM * PARTS; t += THREADS) {
-      const int rl = t / PARTS, part = t % PARTS;
-      if (slots[rl] < S)
-        *reinterpret_cast<uint4*>(g.oc + (size_t)(mb * BM + rl) * row_bytes + (size_t)(WN * nt) * BPB + 16 * part) =
-            *reinterpret_cast<const uint4*>(tc + rl * RB + 16 * part);
     }
-    for (int rl = threadIdx.x; rl < BM; rl += THREADS)
-      if (slots[rl] < S) {
+
+    // ---------------------------------------------------------------- epilogues
+    // The routed gate/up and down epilogues assemble the workgroup's output tile
+    // in the (now idle) LDS ring and write it out with 16-byte row-contiguous
+    // stores.
+    if constexpr (kGateUp) {
+      // SwiGLU on the 32 columns of block nb, then MX re-quantization of each
+      // row's block.  sum[i][0], sum[i][1]: gate columns m and 16 + m; sum[i][2],
+      // sum[i][3]: the matching up columns.  Output row of the intermediate: the
+      // sorted position (routed) or the row (shared).
+      constexpr int BPB = F::MB == 1 ? 16 : 32;  // code bytes of a row's 32-column block
+      constexpr int RB = WN * BPB;               // code bytes of a row of the tile
+      uint8_t* tc = kPersist ? out_tile : ring;   // [BM][RB] codes
+      uint8_t* ts = tc + BM * RB;                // [BM][WN] scales
+      __syncthreads();  // every wavefront is done reading the ring
 #pragma unroll
-        for (int w = 0; w < WN; ++w) g.os[(size_t)(mb * BM + rl) * (g.inter / 32) + WN * nt + w] = ts[rl * WN + w];
-      }
-  } else if constexpr (MODE == DOWN_ROUTED && WN == 4) {
-    // fp32 results straight from the registers (the 128 x 256 tile is too
-    // large to assemble in the ring): for each of its rows a lane stores one
-    // column of each strip, 16 lanes one 64-byte run
-#pragma unroll
-    for (int i = 0; i < MF; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int slot = slots[wm * 16 * MF + 16 * i + 4 * q + r];
-        if (slot < S) {
-          float* dp = g.d_part + (size_t)slot * g.H + (size_t)(16 * STRIPS) * nt + m;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) dp[16 * (4 * wn + j)] = sum[i][j][r];
-        }
-      }
-  } else if constexpr (MODE == DOWN_ROUTED) {
-    // fp32 result rows per slot: tile [BM][16 STRIPS] (row stride padded by
-    // four floats against bank conflicts), columns 16 STRIPS nt onwards
-    constexpr int CW = 16 * STRIPS;
-    constexpr int LD = CW + 4;
-    static_assert(BM * LD * 4 <= Gm::template ring_bytes<G4>(), "the output tile fits the ring");
-    float* tf = reinterpret_cast<float*>(ring);
-    __syncthreads();  // every wavefront is done reading the ring
-#pragma unroll
-    for (int i = 0; i < MF; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rl = wm * 16 * MF + 16 * i + 4 * q + r;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) tf[rl * LD + 16 * (4 * wn + j) + m] = sum[i][j][r];
-      }
-    __syncthreads();
-    constexpr int V = CW / 4;  // float4 per row
-    for (int t = threadIdx.x; t < BM * V; t += THREADS) {
-      const int rl = t / V, c4 = t % V;
-      const int slot = slots[rl];
-      if (slot < S)
-        *reinterpret_cast<float4*>(g.d_part + (size_t)slot * g.H + (size_t)CW * nt + 4 * c4) =
-            *reinterpret_cast<const float4*>(tf + rl * LD + 4 * c4);
-    }
-  } else {
-    // combine: y = bf16( sum_j w_j d_j (j in order) + s + residual ).  Per
-    // row fragment, every load of a batch of four choices (weights, routed
-    // outputs, residual) is issued before any of them is used, so the
-    // fragment waits for memory once rather than once per output.
-    const int k = g.k;
-#pragma unroll
-    for (int i = 0; i < MF; ++i) {
-      int tr[4];
-      float c[4][4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        tr[r] = mb * BM + wm * 16 * MF + 16 * i + 4 * q + r;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) c[r][j] = 0.f;
-      }
-      for (int jc = 0; jc < k; jc += 4) {
-        float wv[4][4], dv[4][4][4];
+      for (int i = 0; i < MF; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int tc = min(tr[r], g.T - 1);  // rows past the end read a real row, nothing is stored
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const bool on = jc + jj < k;
-            wv[r][jj] = on ? g.topk_w[(size_t)tc * k + jc + jj] : 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int h = 16 * w_strip<MODE, WN>(g, nt, 4 * wn + j) + m;
-              dv[r][j][jj] = on ? g.d_part[((size_t)tc * k + jc + jj) * g.H + h] : 0.f;
+          const int rl = wm * 16 * MF + 16 * i + 4 * q + r;
+          const uint32_t a0 = __float_as_uint(silu_mul(sum[i][0][r], sum[i][2][r]));
+          const uint32_t a1 = __float_as_uint(silu_mul(sum[i][1][r], sum[i][3][r]));
+          const uint32_t am = row16_max32(max(a0 & 0x7fffffffu, a1 & 0x7fffffffu));
+          const int ex = block_exponent<F>(am);
+          const float inv = block_inv_scale(ex);
+          uint8_t* op = tc + rl * RB + BPB * wn;
+          if constexpr (F::MB == 1) {
+            // even lanes pack columns m, m + 1 (the neighbour's value) into one
+            // byte, low nibble first; the codes are those of quant_quad_fp4
+            const uint32_t w = quant_quad_fp4(a0, row_move32(a0), a1, row_move32(a1), inv);
+            if (!(m & 1)) {
+              op[m / 2] = (uint8_t)w;
+              op[8 + m / 2] = (uint8_t)(w >> 8);
             }
+          } else {
+            const uint32_t w = quant_pair_fp8(a0, a1, inv);
+            op[m] = (uint8_t)w;
+            op[16 + m] = (uint8_t)(w >> 8);
+          }
+          if (m == 0) ts[rl * WN + wn] = (uint8_t)(ex + 127);
+        }
+      __syncthreads();
+      const size_t row_bytes = F::MB == 1 ? (size_t)g.inter / 2 : (size_t)g.inter;
+      constexpr int PARTS = RB / 16;
+      for (int t = threadIdx.x; t < BM * PARTS; t += THREADS) {
+        const int rl = t / PARTS, part = t % PARTS;
+        if (slots[rl] < S)
+          *reinterpret_cast<uint4*>(g.oc + (size_t)(mb * BM + rl) * row_bytes + (size_t)(WN * nt) * BPB + 16 * part) =
+              *reinterpret_cast<const uint4*>(tc + rl * RB + 16 * part);
+      }
+      for (int rl = threadIdx.x; rl < BM; rl += THREADS)
+        if (slots[rl] < S) {
+#pragma unroll
+          for (int w = 0; w < WN; ++w) g.os[(size_t)(mb * BM + rl) * (g.inter / 32) + WN * nt + w] = ts[rl * WN + w];
+        }
+    } else if constexpr (MODE == DOWN_ROUTED && WN == 4) {
+      // fp32 results straight from the registers (the 128 x 256 tile is too
+      // large to assemble in the ring): for each of its rows a lane stores one
+      // column of each strip, 16 lanes one 64-byte run
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int slot = slots[wm * 16 * MF + 16 * i + 4 * q + r];
+          if (slot < S) {
+            float* dp = g.d_part + (size_t)slot * g.H + (size_t)(16 * STRIPS) * nt + m;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dp[16 * (4 * wn + j)] = sum[i][j][r];
           }
         }
+    } else if constexpr (MODE == DOWN_ROUTED) {
+      // fp32 result rows per slot: tile [BM][16 STRIPS] (row stride padded by
+      // four floats against bank conflicts), columns 16 STRIPS nt onwards
+      constexpr int CW = 16 * STRIPS;
+      constexpr int LD = CW + 4;
+      static_assert(BM * LD * 4 <= Gm::template ring_bytes<G4>(), "the output tile fits the ring");
+      float* tf = reinterpret_cast<float*>(ring);
+      __syncthreads();  // every wavefront is done reading the ring
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rl = wm * 16 * MF + 16 * i + 4 * q + r;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) tf[rl * LD + 16 * (4 * wn + j) + m] = sum[i][j][r];
+        }
+      __syncthreads();
+      constexpr int V = CW / 4;  // float4 per row
+      for (int t = threadIdx.x; t < BM * V; t += THREADS) {
+        const int rl = t / V, c4 = t % V;
+        const int slot = slots[rl];
+        if (slot < S)
+          *reinterpret_cast<float4*>(g.d_part + (size_t)slot * g.H + (size_t)CW * nt + 4 * c4) =
+              *reinterpret_cast<const float4*>(tf + rl * LD + 4 * c4);
+      }
+    } else {
+      // combine: y = bf16( sum_j w_j d_j (j in order) + s + residual ).  Per
+      // row fragment, every load of a batch of four choices (weights, routed
+      // outputs, residual) is issued before any of them is used, so the
+      // fragment waits for memory once rather than once per output.
+      const int k = g.k;
+#pragma unroll
+      for (int i = 0; i < MF; ++i) {
+        int tr[4];
+        float c[4][4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          tr[r] = mb * BM + wm * 16 * MF + 16 * i + 4 * q + r;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) c[r][j] = 0.f;
+        }
+        for (int jc = 0; jc < k; jc += 4) {
+          float wv[4][4], dv[4][4][4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int tc = min(tr[r], g.T - 1);  // rows past the end read a real row, nothing is stored
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const bool on = jc + jj < k;
+              wv[r][jj] = on ? g.topk_w[(size_t)tc * k + jc + jj] : 0.f;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int h = 16 * w_strip<MODE, WN>(g, nt, 4 * wn + j) + m;
+                dv[r][j][jj] = on ? g.d_part[((size_t)tc * k + jc + jj) * g.H + h] : 0.f;
+              }
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              if (jc + jj < k) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) c[r][j] = fmaf(wv[r][jj], dv[r][j][jj], c[r][j]);
+              }
+        }
+        float rv[4][4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            if (jc + jj < k) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) c[r][j] = fmaf(wv[r][jj], dv[r][j][jj], c[r][j]);
-            }
-      }
-      float rv[4][4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int h = 16 * w_strip<MODE, WN>(g, nt, 4 * wn + j) + m;
-          rv[r][j] = g.residual ? bf16_to_f32(g.residual[(size_t)min(tr[r], g.T - 1) * g.H + h]) : 0.f;
-        }
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (tr[r] < g.T) {
-#pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int h = 16 * w_strip<MODE, WN>(g, nt, 4 * wn + j) + m;
-            float v = c[r][j] + sum[i][j][r];
-            if (g.residual) v = v + rv[r][j];
-            g.y[(size_t)tr[r] * g.H + h] = f32_to_bf16(v);
+            rv[r][j] = g.residual ? bf16_to_f32(g.residual[(size_t)min(tr[r], g.T - 1) * g.H + h]) : 0.f;
           }
-        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (tr[r] < g.T) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int h = 16 * w_strip<MODE, WN>(g, nt, 4 * wn + j) + m;
+              float v = c[r][j] + sum[i][j][r];
+              if (g.residual) v = v + rv[r][j];
+              g.y[(size_t)tr[r] * g.H + h] = f32_to_bf16(v);
+            }
+          }
+      }
+    }
+
+    if (!more) break;
+    mb = mb2;
+    nt = nt2;
+    e = e2;
+    {
+      int32_t* t = slots;
+      slots = slots_next;
+      slots_next = t;
+    }
+    as_src = as_src2;
+#pragma unroll
+    for (int i = 0; i < Gm::B_SC; ++i) bs_src[i] = bs_src2[i];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      src[i] = src2[i];
+      step[i] = step2[i];
     }
   }
 }
@@ -760,10 +827,26 @@ GCarve gcarve(const moe_layer_t& L, int T) {
 
 unsigned grid8(int tiles) { return (unsigned)((tiles + 7) / 8 * 8); }
 
+// Compute units of the current device, cached per device (lock-free; racing
+// first calls store the same value).
+int cu_count() {
+  static std::atomic<int> cache[kMaxDevices];
+  const int dev = current_device();
+  if (dev < 0 || dev >= kMaxDevices) return -1;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 template <class F, int MODE, int WN, bool G4>
 hipError_t launch_gemm_as(const GemmArgs& g, hipStream_t stream) {
   using Gm = Geo<F, WN>;
-  const size_t lds = (size_t)Gm::template ring_bytes<G4>() + (size_t)Gm::BM * 4;
+  constexpr bool kPersist = G4 && WN == 4 && MODE == GU_ROUTED;
+  // ring, slots (two sets when persistent) and the gate/up output tile
+  const size_t lds = (size_t)Gm::template ring_bytes<G4>() + (size_t)Gm::BM * 4 * (kPersist ? 2 : 1) +
+                     (kPersist ? (size_t)Gm::BM * (WN * 16 + WN) : 0);
   // the kernel's dynamic LDS limit is raised once per device (a lock-free
   // flag per device; racing first calls both set the same attribute)
   static std::atomic<bool> lds_set[kMaxDevices];
@@ -777,8 +860,14 @@ hipError_t launch_gemm_as(const GemmArgs& g, hipStream_t stream) {
       lds_set[dev].store(true, std::memory_order_relaxed);
     }
   }
-  hipLaunchKernelGGL((grouped_gemm_kernel<F, MODE, WN, G4>), dim3(grid8(g.MB * g.NT)), dim3(Gm::THREADS), lds, stream,
-                     g);
+  unsigned grid = grid8(g.MB * g.NT);
+  if (kPersist) {  // one workgroup per CU, looping over tiles
+    const int cus = cu_count();
+    if (cus <= 0) return hipErrorInvalidDevice;
+    const unsigned cap = (unsigned)(cus / 8 * 8);
+    if (cap > 0 && grid > cap) grid = cap;
+  }
+  hipLaunchKernelGGL((grouped_gemm_kernel<F, MODE, WN, G4>), dim3(grid), dim3(Gm::THREADS), lds, stream, g);
   return hipGetLastError();
 }
 
