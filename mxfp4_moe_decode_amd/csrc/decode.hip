@@ -1460,7 +1460,10 @@ __global__ void __launch_bounds__(kThreads) fused_decode_kernel(DA A) {
   const uint64_t t_entry = wall_clock64();
   __shared__ SmemOf<DA> sm;
   extern __shared__ __align__(16) unsigned char dyn[];
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  // the wavefront index as a uniform value: everything derived from it stays
+  // in scalar registers, which leaves the vector registers to the pipeline
+  // buffers (fewer of them move through AGPRs)
+  const int lane = threadIdx.x % kWave, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int G = A.G;
   const uint32_t tag = ld_dev(ctr(A.sync, S_EPOCH)) + 1u;
   const uint32_t status = ld_dev(ctr(A.sync, S_STATUS));
