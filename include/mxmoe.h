@@ -324,15 +324,25 @@ moe_status fused_moe_mxfp4_decode_noalloc(const moe_layer_t* layer, const uint16
  * matrix instructions, the MXFP8 shared expert, and the combine.
  *   x, residual, y as for the decode call; T >= 1
  *   ws  moe_workspace_bytes(layer, T, 1) bytes (no initialization needed)
+ * The steps that do not depend on the routing (the quantization of x, the
+ * shared gate/up GEMM) run on a second stream that the library creates on
+ * each device at its first call there (default priority, kept until the
+ * process ends), forked from `stream` before the router and joined back
+ * into it before the routed GEMMs: all of the call's work is ordered after
+ * earlier work on `stream` and before later work on it, as for a single
+ * stream.  Calls on one device from several host threads take turns on that
+ * stream.  While `stream` is being captured into a graph every step runs on
+ * `stream` itself.
  */
 moe_status fused_moe_mxfp4_grouped(const moe_layer_t* layer, const uint16_t* x, int T,
                                    const uint16_t* residual, uint16_t* y, void* ws, size_t ws_bytes,
                                    hipStream_t stream);
 
 /*
- * Diagnostic: fused_moe_mxfp4_grouped with an event recorded on `stream`
- * before each of its launch steps and one at the end, so that a caller can
- * time them (hipEventElapsedTime).  events[0..7], caller-created, non-NULL:
+ * Diagnostic: fused_moe_mxfp4_grouped with every step on `stream`, in the
+ * order below, an event recorded on `stream` before each of its launch steps
+ * and one at the end, so that a caller can time them (hipEventElapsedTime).
+ * events[0..7], caller-created, non-NULL:
  *   0 router and top-k, 1 token sort, 2 MX quantization of x, 3 routed
  *   gate/up GEMM, 4 routed down GEMM, 5 shared gate/up GEMM (the combine
  *   kernel when there is no shared expert), 6 shared down GEMM with the

@@ -33,6 +33,8 @@
 #include <atomic>
 #include <type_traits>
 
+#include <mutex>
+
 #include "internal.h"
 #include "mx_device.h"
 
@@ -883,6 +885,36 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
 
 size_t grouped_ws_bytes(const moe_layer_t& L, int T) { return gcarve(L, T).total; }
 
+// The grouped path's second stream on each device (default priority, created
+// with the device current on its first untimed call) and its fork / join
+// events.  Callers hold g_side_mu from the fork's record to the join's wait,
+// so that concurrent host threads cannot interleave their records of the
+// shared events.
+struct SideStream {
+  hipStream_t s;
+  hipEvent_t fork, join;
+};
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+bool g_side_made[kMaxDevices];
+
+hipError_t side_stream(const SideStream** out) {  // g_side_mu held
+  *out = nullptr;
+  const int dev = current_device();
+  if (dev < 0) return hipErrorInvalidDevice;
+  SideStream& S = g_side[dev];
+  if (!g_side_made[dev]) {
+    hipError_t err = hipStreamCreateWithFlags(&S.s, hipStreamNonBlocking);
+    if (err != hipSuccess) return err;
+    if ((err = hipEventCreateWithFlags(&S.fork, hipEventDisableTiming)) != hipSuccess ||
+        (err = hipEventCreateWithFlags(&S.join, hipEventDisableTiming)) != hipSuccess)
+      return err;
+    g_side_made[dev] = true;
+  }
+  *out = &S;
+  return hipSuccess;
+}
+
 hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const uint16_t* residual,
                           uint16_t* y, void* ws, hipStream_t stream, const hipEvent_t* ev) {
   // ev (optional): kGroupedSteps + 1 events, recorded before each step and at the end
@@ -905,6 +937,42 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
   uint8_t* as4 = reinterpret_cast<uint8_t*>(at(c.as4));
   float* d_part = reinterpret_cast<float*>(at(c.d_part));
   hipError_t err;
+  // Untimed and not under stream capture, the steps that do not depend on the
+  // routing (x's MX quantization, the shared gate/up GEMM) run on the
+  // device's side stream, forked from `stream` before the router and joined
+  // back before the routed gate/up: they fill the GPU while the router's tail,
+  // the top-k and the token sort leave it partly idle.
+  std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
+  const SideStream* side = nullptr;
+  if (!ev) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if ((err = hipStreamIsCapturing(stream, &cs)) != hipSuccess) return err;
+    if (cs == hipStreamCaptureStatusNone) {
+      lock.lock();
+      if ((err = side_stream(&side)) != hipSuccess) return err;
+    }
+  }
+  const hipStream_t sq = side ? side->s : stream;  // stream of the quantization and the shared gate/up
+  bool forked = false;
+  auto join = [&]() -> hipError_t {
+    forked = false;
+    hipError_t e = hipEventRecord(side->join, side->s);
+    return e == hipSuccess ? hipStreamWaitEvent(stream, side->join, 0) : e;
+  };
+  // on an error return after the fork, still order the side stream's work
+  // before whatever the caller does next on `stream`
+  struct JoinGuard {
+    bool& f;
+    decltype(join)& j;
+    ~JoinGuard() {
+      if (f) (void)j();
+    }
+  } guard{forked, join};
+  if (side) {
+    if ((err = hipEventRecord(side->fork, stream)) != hipSuccess) return err;
+    if ((err = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return err;
+    forked = true;
+  }
   if ((err = mark(0)) != hipSuccess) return err;
   if ((err = launch_router_topk(L, x, T, reinterpret_cast<float*>(at(c.logits)), ids, w,
                                k, L.shared_folded ? L.num_experts : -1, stream)) != hipSuccess)
@@ -919,14 +987,14 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
   float* rnorm = nullptr;
   if (L.norm_weight) {
     rnorm = reinterpret_cast<float*>(at(c.rnorm));
-    if ((err = launch_rms_rows(x, T, H, L.norm_eps, rnorm, stream)) != hipSuccess) return err;
+    if ((err = launch_rms_rows(x, T, H, L.norm_eps, rnorm, sq)) != hipSuccess) return err;
     residual = x;  // the fused residual: the layer's own input
   }
   if (Is > 0)
     err = launch_quant_act_dual(x, T, H, xq4, xs4, reinterpret_cast<uint8_t*>(at(c.xq8)),
-                                reinterpret_cast<uint8_t*>(at(c.xs8)), stream, rnorm, L.norm_weight);
+                                reinterpret_cast<uint8_t*>(at(c.xs8)), sq, rnorm, L.norm_weight);
   else
-    err = launch_quant_act(x, T, H, MX_FMT_FP4, xq4, xs4, stream, rnorm, L.norm_weight);
+    err = launch_quant_act(x, T, H, MX_FMT_FP4, xq4, xs4, sq, rnorm, L.norm_weight);
   if (err != hipSuccess) return err;
   if ((err = mark(3)) != hipSuccess) return err;
 
@@ -937,6 +1005,40 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
   g.sorted_slots = sorted;
   g.block_expert = bexp;
   g.num_padded = npad;
+  uint8_t* xq8 = reinterpret_cast<uint8_t*>(at(c.xq8));
+  uint8_t* xs8 = reinterpret_cast<uint8_t*>(at(c.xs8));
+  uint8_t* a8 = reinterpret_cast<uint8_t*>(at(c.a8));
+  uint8_t* as8 = reinterpret_cast<uint8_t*>(at(c.as8));
+  constexpr int BM8 = Geo<FP8, 2>::BM;
+  // shared gate/up: A = MXFP8 x, B = Ws13.  With at least 512 tiles of
+  // 64 x 256 (two rounds of workgroups) and K on the scale-group loop,
+  // eight-wavefront 64 x 256 tiles: each K-tile's 40 KB of operands feed
+  // twice the products of a 64 x 128 tile's 24 KB (4% faster at 8192 rows);
+  // with fewer rows the 64 x 128 tiles keep more workgroups busy.
+  const bool wide_sgu = H % 512 == 0 && (size_t)((T + BM8 - 1) / BM8) * (Is / 128) >= 512;
+  auto shared_gate_up = [&](hipStream_t s) -> hipError_t {
+    GemmArgs r = g;
+    r.MB = (T + BM8 - 1) / BM8;
+    r.NT = Is / (wide_sgu ? 128 : 64);
+    r.KT = H / 128;
+    r.CT = pick_chunk(r.KT);
+    r.KG = (r.KT + 3) / 4;
+    r.a = xq8;
+    r.as = xs8;
+    r.a_stride = H;
+    r.as_stride = H / 32;
+    r.b = L.ws13;
+    r.bs = L.ws13_scale;
+    r.inter = Is;
+    r.oc = a8;
+    r.os = as8;
+    return wide_sgu ? launch_gemm<FP8, GU_SHARED, 4>(r, s) : launch_gemm<FP8, GU_SHARED, 2>(r, s);
+  };
+  if (side) {
+    if (Is > 0 && (err = shared_gate_up(sq)) != hipSuccess) return err;
+    if ((err = join()) != hipSuccess) return err;
+    lock.unlock();
+  }
   // routed gate/up: A = MXFP4 x gathered by slot, B = W13[e].  With at
   // least a full 128-row block per expert on average the products dominate:
   // 128 x 256 tiles (eight wavefronts, one workgroup per CU), whose K-tile of
@@ -999,36 +1101,7 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
     if ((err = mark(6)) != hipSuccess) return err;
     return mark(7);
   }
-  uint8_t* xq8 = reinterpret_cast<uint8_t*>(at(c.xq8));
-  uint8_t* xs8 = reinterpret_cast<uint8_t*>(at(c.xs8));
-  uint8_t* a8 = reinterpret_cast<uint8_t*>(at(c.a8));
-  uint8_t* as8 = reinterpret_cast<uint8_t*>(at(c.as8));
-  constexpr int BM8 = Geo<FP8, 2>::BM;
-  // shared gate/up: A = MXFP8 x, B = Ws13.  With at least 512 tiles of
-  // 64 x 256 (two rounds of workgroups) and K on the scale-group loop,
-  // eight-wavefront 64 x 256 tiles: each K-tile's 40 KB of operands feed
-  // twice the products of a 64 x 128 tile's 24 KB (4% faster at 8192 rows);
-  // with fewer rows the 64 x 128 tiles keep more workgroups busy.
-  const bool wide_sgu = H % 512 == 0 && (size_t)((T + BM8 - 1) / BM8) * (Is / 128) >= 512;
-  {
-    GemmArgs r = g;
-    r.MB = (T + BM8 - 1) / BM8;
-    r.NT = Is / (wide_sgu ? 128 : 64);
-    r.KT = H / 128;
-    r.CT = pick_chunk(r.KT);
-    r.KG = (r.KT + 3) / 4;
-    r.a = xq8;
-    r.as = xs8;
-    r.a_stride = H;
-    r.as_stride = H / 32;
-    r.b = L.ws13;
-    r.bs = L.ws13_scale;
-    r.inter = Is;
-    r.oc = a8;
-    r.os = as8;
-    err = wide_sgu ? launch_gemm<FP8, GU_SHARED, 4>(r, stream) : launch_gemm<FP8, GU_SHARED, 2>(r, stream);
-    if (err != hipSuccess) return err;
-  }
+  if (!side && (err = shared_gate_up(stream)) != hipSuccess) return err;
   if ((err = mark(6)) != hipSuccess) return err;
   // shared down + combine
   {

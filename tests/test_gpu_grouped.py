@@ -9,7 +9,9 @@
   kernel, and the rows at 128-row block boundaries and segment tails of
   twelve experts against the oracle;
 * at the TP4 per-GPU shape, with 256 experts top-8, and at a shape whose K
-  splits into 2 / 1 / 1 chunks (test_gpu_shapes.py).
+  splits into 2 / 1 / 1 chunks (test_gpu_shapes.py);
+* the two-stream schedule of the plain call against the one-stream timed
+  call, bit for bit, on a non-default stream and for back-to-back calls.
 """
 
 import numpy as np
@@ -146,3 +148,32 @@ def test_grouped_prefill_8192_every_row():
     xr = x[rows]
     helpers.prefetch(ol, np.unique(ids[rows]))
     _oracle_compare(cfg, gl, ol, xr, y[rows], label="block boundaries")
+
+
+def test_grouped_side_stream_matches_one_stream():
+    """The plain call runs the quantization and the shared gate/up on the
+    library's side stream; the timed call runs every step on the caller's
+    stream.  Both give the same bits, from a non-default caller stream too,
+    and back-to-back plain calls on one workspace (different inputs and row
+    counts, no synchronization between them) each give their own result."""
+    cfg, gl, _ = _layers("odd", oracle=False)
+    ws = binding.grouped_workspace(gl, 700)
+    xs = [_dev(synth.activations(cfg, T=T, index=j)) for j, T in enumerate((700, 37, 300))]
+    ref = []
+    for x in xs:
+        print(f"[grouped] timed T={x.shape[0]}", flush=True)
+        y, _ = binding.fused_moe_mxfp4_grouped_timed(gl, x, workspace=ws)
+        torch.cuda.synchronize()
+        ref.append(_host(y))
+    s = torch.cuda.Stream()
+    for rep in range(2):
+        print(f"[grouped] back-to-back plain calls, pass {rep}", flush=True)
+        with torch.cuda.stream(s):
+            ys = [binding.fused_moe_mxfp4_grouped(gl, x, workspace=ws) for x in xs]
+        s.synchronize()
+        for y, r in zip(ys, ref):
+            assert np.array_equal(_host(y), r)
+    ys = [binding.fused_moe_mxfp4_grouped(gl, x, workspace=ws) for x in xs]
+    torch.cuda.synchronize()
+    for y, r in zip(ys, ref):
+        assert np.array_equal(_host(y), r)
