@@ -328,9 +328,9 @@ moe_status fused_moe_mxfp4_decode_noalloc(const moe_layer_t* layer, const uint16
  * shared gate/up GEMM) run on a second stream that the library creates on
  * each device at its first call there (default priority, kept until the
  * process ends), forked from `stream` before the router and joined back
- * into it before the routed GEMMs: all of the call's work is ordered after
- * earlier work on `stream` and before later work on it, as for a single
- * stream.  Calls on one device from several host threads take turns on that
+ * into it before the steps that use their results: all of the call's work
+ * is ordered after earlier work on `stream` and before later work on it, as
+ * for a single stream.  Calls on one device from several host threads take turns on that
  * stream.  While `stream` is being captured into a graph every step runs on
  * `stream` itself.
  */

@@ -886,13 +886,14 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
 size_t grouped_ws_bytes(const moe_layer_t& L, int T) { return gcarve(L, T).total; }
 
 // The grouped path's second stream on each device (default priority, created
-// with the device current on its first untimed call) and its fork / join
-// events.  Callers hold g_side_mu from the fork's record to the join's wait,
-// so that concurrent host threads cannot interleave their records of the
-// shared events.
+// with the device current on its first untimed call) and its events: fork
+// (recorded on the caller's stream, waited for by the side stream), quant
+// (the side stream's quantization done) and join (all of its work done).
+// Callers hold g_side_mu from the fork's record to the join's wait, so that
+// concurrent host threads cannot interleave their records of these events.
 struct SideStream {
   hipStream_t s;
-  hipEvent_t fork, join;
+  hipEvent_t fork, join, quant;
 };
 std::mutex g_side_mu;
 SideStream g_side[kMaxDevices];
@@ -907,7 +908,8 @@ hipError_t side_stream(const SideStream** out) {  // g_side_mu held
     hipError_t err = hipStreamCreateWithFlags(&S.s, hipStreamNonBlocking);
     if (err != hipSuccess) return err;
     if ((err = hipEventCreateWithFlags(&S.fork, hipEventDisableTiming)) != hipSuccess ||
-        (err = hipEventCreateWithFlags(&S.join, hipEventDisableTiming)) != hipSuccess)
+        (err = hipEventCreateWithFlags(&S.join, hipEventDisableTiming)) != hipSuccess ||
+        (err = hipEventCreateWithFlags(&S.quant, hipEventDisableTiming)) != hipSuccess)
       return err;
     g_side_made[dev] = true;
   }
@@ -939,9 +941,10 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
   hipError_t err;
   // Untimed and not under stream capture, the steps that do not depend on the
   // routing (x's MX quantization, the shared gate/up GEMM) run on the
-  // device's side stream, forked from `stream` before the router and joined
-  // back before the routed gate/up: they fill the GPU while the router's tail,
-  // the top-k and the token sort leave it partly idle.
+  // device's side stream, forked from `stream` before the router: they fill
+  // the GPU while the router's tail, the top-k and the token sort leave it
+  // partly idle.  The routed gate/up waits for the quantization only, the
+  // shared down (or the combine) for all of the side stream's work.
   std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
   const SideStream* side = nullptr;
   if (!ev) {
@@ -1035,9 +1038,14 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
     return wide_sgu ? launch_gemm<FP8, GU_SHARED, 4>(r, s) : launch_gemm<FP8, GU_SHARED, 2>(r, s);
   };
   if (side) {
-    if (Is > 0 && (err = shared_gate_up(sq)) != hipSuccess) return err;
-    if ((err = join()) != hipSuccess) return err;
-    lock.unlock();
+    if (Is > 0) {
+      if ((err = hipEventRecord(side->quant, sq)) != hipSuccess) return err;
+      if ((err = shared_gate_up(sq)) != hipSuccess) return err;
+      if ((err = hipStreamWaitEvent(stream, side->quant, 0)) != hipSuccess) return err;
+    } else {
+      if ((err = join()) != hipSuccess) return err;
+      lock.unlock();
+    }
   }
   // routed gate/up: A = MXFP4 x gathered by slot, B = W13[e].  With at
   // least a full 128-row block per expert on average the products dominate:
@@ -1102,6 +1110,10 @@ hipError_t launch_grouped(const moe_layer_t& L, const uint16_t* x, int T, const 
     return mark(7);
   }
   if (!side && (err = shared_gate_up(stream)) != hipSuccess) return err;
+  if (side) {
+    if ((err = join()) != hipSuccess) return err;
+    lock.unlock();
+  }
   if ((err = mark(6)) != hipSuccess) return err;
   // shared down + combine
   {
