@@ -11,7 +11,8 @@
 * at the TP4 per-GPU shape, with 256 experts top-8, and at a shape whose K
   splits into 2 / 1 / 1 chunks (test_gpu_shapes.py);
 * the two-stream schedule of the plain call against the one-stream timed
-  call, bit for bit, on a non-default stream and for back-to-back calls.
+  call, bit for bit, on a non-default stream, for back-to-back calls and
+  from two host threads at once.
 """
 
 import numpy as np
@@ -177,3 +178,44 @@ def test_grouped_side_stream_matches_one_stream():
     torch.cuda.synchronize()
     for y, r in zip(ys, ref):
         assert np.array_equal(_host(y), r)
+
+
+def test_grouped_two_host_threads():
+    """Two host threads make plain grouped calls at the same time, each on its
+    own stream, workspace and inputs; they share the device's side stream, and
+    every result equals the one-stream timed call's."""
+    import threading
+
+    cfg, gl, _ = _layers("odd", oracle=False)
+    xs = [_dev(synth.activations(cfg, T=T, index=10 + j)) for j, T in enumerate((300, 211))]
+    wss = [binding.grouped_workspace(gl, x.shape[0]) for x in xs]
+    ref = []
+    for x, ws in zip(xs, wss):
+        y, _ = binding.fused_moe_mxfp4_grouped_timed(gl, x, workspace=ws)
+        torch.cuda.synchronize()
+        ref.append(_host(y))
+    outs = [[], []]
+    errors = []
+
+    def worker(j):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(4):
+                    outs[j].append(binding.fused_moe_mxfp4_grouped(gl, xs[j], workspace=wss[j]))
+            s.synchronize()
+        except Exception as e:  # reported by the main thread
+            errors.append(repr(e))
+
+    print("[grouped] two host threads, 4 calls each", flush=True)
+    threads = [threading.Thread(target=worker, args=(j,)) for j in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in threads)
+    assert not errors, errors
+    for j in range(2):
+        assert len(outs[j]) == 4
+        for y in outs[j]:
+            assert np.array_equal(_host(y), ref[j])
